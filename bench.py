@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Throughput of the gated-delta-rule hot path on one MI355X.
+
+One step = one ``gdn_chunk_fwd`` call (gate cumsum, intra-chunk solve, chunk
+scan fused with the output) over the GDN workload B=4 T=4096 H=16 K=V=128,
+bf16 q/k/v, fp32 gate/beta/state, zero h0, final state stored; inputs are
+seeded synthetic tensors already resident in HBM.  ``value`` is prefill
+tokens/s (B*T per call).  The same JSON line also carries the decode step
+(B=256, HV=32, K=V=128, bf16 state, T=1 and T=4: tokens/s and state GB/s),
+the KDA prefill (B=2 T=8192 H=32) when built, the per-kernel roofline of the
+dominant prefill kernel (live HIP-event timing inside the library, on the
+launch stream) and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+# Algorithmic FLOPs per token per v-head of each prefill kernel (dk = dv = d):
+#   intra: block-lower K K^T and Q K^T (2 x 80 d; 10 of 16 16x16 blocks of a
+#          64-token chunk) + the 16 block-merge products (16 * 2 * 16^3 / 64)
+#   scan:  K S^T, Q S^T, K^T Vn (3 x 2 d^2) + block-lower Ainv R and Aqk Vn (2 x 80 d)
+def intra_flops_per_token(d: int) -> int:
+    return 2 * 80 * d + 16 * 2 * 16 ** 3 // 64
+
+
+def scan_flops_per_token(d: int) -> int:
+    return 6 * d * d + 2 * 80 * d
+
+
+# The headline "% MFMA" uses the method's algorithmic count per token per
+# v-head, 6 dk dv + 80 (3 dk + 2 dv) + 2048 (block-lower K K^T, Q K^T, w, u,
+# Aqk Vn, w h, K^T Vn, Q h and the merge).
+def method_flops_per_token(dk: int, dv: int) -> int:
+    return 6 * dk * dv + 80 * (3 * dk + 2 * dv) + 2048
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    p.add_argument("--skip-extra", action="store_true", help="prefill workload only")
+    return p.parse_args()
+
+
+def timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        fn()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall
+
+
+def bench_prefill(args, binding, workloads, torch):
+    inp = workloads.gdn_bf16_b4_t4096()
+    dev = "cuda:0"
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    g, beta = inp.g.to(dev), inp.beta.to(dev)
+    B, T, Hk, HV, K, V = inp.dims
+    o = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.workspace_bytes(B, T, Hk, HV, K, V, B, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.gdn_chunk_fwd(q, k, v, g, beta, scale=inp.scale, out=o, workspace=ws)
+
+    ms, wall = timed(step, args.steps, args.warmup)
+    # live per-kernel timing: library events on the launch stream, same timed loop
+    binding.profile_read()
+    binding.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = binding.profile_read()
+    binding.profile_enable(False)
+    # cold-cache variant: 1 GiB scratch written between calls, only the call timed
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(min(args.steps, 10)):
+        scratch.fill_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del scratch
+    tokens = B * T
+    return dict(inp=inp, ms=ms, wall=wall, prof=prof, tokens=tokens, HV=HV, K=K, V=V,
+                cold_ms=sorted(cold)[len(cold) // 2])
+
+
+def bench_decode(args, binding, workloads, torch, T):
+    inp = workloads.decode_b256(T)
+    dev = "cuda:0"
+    t = {n: getattr(inp, n).to(dev) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
+    state = inp.state.to(dev)
+    B, _, H, K = inp.q.shape
+    HV, V = inp.v.shape[2], inp.v.shape[3]
+    o = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        binding.gdn_decode(t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"], t["dt_bias"], state,
+                           scale=inp.scale, out=o)
+
+    ms, _ = timed(step, args.steps, args.warmup)
+    binding.profile_read()
+    binding.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = binding.profile_read()
+    binding.profile_enable(False)
+    kms = prof["decode"][0] / max(prof["decode"][1], 1)
+    state_bytes = 2 * B * HV * V * K * 2
+    other = (2 * B * T * H * K + 2 * B * T * HV * V + 2 * B * T * HV) * 2 + 2 * HV * 4
+    return {
+        "workload": f"gdn_decode B={B} T={T} H={H} HV={HV} K=V={K} bf16 state",
+        "ms_per_call": round(ms, 5),
+        "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+        "state_GBps": round(state_bytes / (ms * 1e-3) / 1e9, 1),
+        "kernel_ms": round(kms, 5),
+        "kernel_state_GBps": round(state_bytes / (kms * 1e-3) / 1e9, 1),
+        "kernel_total_GBps": round((state_bytes + other) / (kms * 1e-3) / 1e9, 1),
+        "hbm_frac": round((state_bytes + other) / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
+def bench_kda(args, binding, workloads, torch):
+    inp = workloads.kda_bf16_b2_t8192()
+    dev = "cuda:0"
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    gk, beta = inp.gk.to(dev), inp.beta.to(dev)
+    B, T, Hk, HV, K, V = inp.dims
+
+    def step():
+        binding.kda_chunk_fwd(q, k, v, gk, beta, scale=inp.scale)
+
+    ms, _ = timed(step, max(args.steps // 2, 1), 1)
+    flops = method_flops_per_token(K, V) * B * T * HV
+    return {"workload": f"kda_chunk_fwd B={B} T={T} H={HV} K=V={K} bf16",
+            "ms_per_call": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "mfma_frac_method_flops": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def cpu_baseline(args, workloads):
+    """fp64 oracle on a bounded sample of the same prefill workload."""
+    import oracle
+    inp = workloads.gdn_bf16_b4_t4096()
+    B, T = inp.q.shape[:2]
+    S = min(args.cpu_sample_tokens, B * T)
+    rows = max(1, S // T)
+    toks = min(S, T) if rows == 1 else T
+    t0 = time.perf_counter()
+    oracle.gdn_recurrent(inp.q[:rows, :toks], inp.k[:rows, :toks], inp.v[:rows, :toks],
+                         inp.g[:rows, :toks], inp.beta[:rows, :toks], inp.scale)
+    dt = time.perf_counter() - t0
+    n = rows * toks
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch rows 0..{rows - 1}, tokens 0..{toks - 1} ({n} of {B * T} tokens, all 16 heads), "
+                      f"{dt:.1f} s; numpy fp64 token-by-token recurrence, single thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the method shards over "
+              "(sequence, head) with no communication, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from gated_delta_rule_61_amd import binding, workloads
+    binding.lib()
+    assert torch.cuda.is_available(), "needs a GPU"
+
+    pf = bench_prefill(args, binding, workloads, torch)
+    ms = pf["ms"]
+    tokens = pf["tokens"]
+    HV, K, V = pf["HV"], pf["K"], pf["V"]
+    prof = pf["prof"]
+    stage_ms = {s: (prof[s][0] / prof[s][1] if prof[s][1] else 0.0) for s in ("intra", "scan")}
+    flops = {"intra": intra_flops_per_token(K) * tokens * HV, "scan": scan_flops_per_token(K) * tokens * HV}
+    dom = max(stage_ms, key=stage_ms.get)
+    ach = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    method = method_flops_per_token(K, V) * tokens * HV
+    out = {
+        "metric": "prefill tokens/s + % MFMA peak; decode tokens/s + state HBM GB/s (1 GPU)",
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gdn_chunk_fwd B=4 T=4096 H=16 K=V=128 BT=64, bf16 q/k/v, fp32 g/beta/state, zero h0, ht stored",
+                   "global_batch": 4, "seq_len": 4096},
+        "mfma_frac_method_flops": round(method / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "cold_ms_per_step": round(pf["cold_ms"], 5),
+        "kernels_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if not args.skip_extra:
+        out["decode"] = {"T1": bench_decode(args, binding, workloads, torch, 1),
+                         "T4": bench_decode(args, binding, workloads, torch, 4)}
+        try:
+            out["kda"] = bench_kda(args, binding, workloads, torch)
+        except Exception as e:  # KDA path reports its own status
+            out["kda"] = {"error": f"{type(e).__name__}: {e}"}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, workloads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

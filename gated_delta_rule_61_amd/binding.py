@@ -1,0 +1,246 @@
+"""Thin Python binding of ``libgdn61.so`` (ctypes).
+
+Argument marshalling only: the functions below check tensor placement,
+dtypes and shapes, allocate outputs and workspace with PyTorch, and pass raw
+device pointers plus the current HIP stream to the C ABI declared in
+``include/gdn61.h``.  Every step of the computation runs in the library's
+gfx950 kernels; there is no fallback path -- if the library is missing or
+fails to load, every entry point raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn61.so")
+
+GDN_DTYPE_F32 = 0
+GDN_DTYPE_BF16 = 1
+
+_c_void_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_float = ctypes.c_float
+_c_size_t = ctypes.c_size_t
+
+_SIGNATURES = {
+    "gdn_status_string": (ctypes.c_char_p, [_c_int]),
+    "gdn_last_error": (ctypes.c_char_p, []),
+    "gdn_version": (ctypes.c_char_p, []),
+    "gdn_chunk_fwd_workspace_bytes": (_c_size_t, [_c_int] * 8),
+    "kda_chunk_fwd_workspace_bytes": (_c_size_t, [_c_int] * 8),
+    "gdn_chunk_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float,
+                               _c_void_p, _c_void_p, _c_void_p, _c_int,
+                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                               _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "kda_chunk_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float,
+                               _c_void_p, _c_void_p, _c_void_p, _c_int,
+                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "gdn_profile_enable": (_c_int, [_c_int]),
+    "gdn_profile_read": (_c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int)]),
+    "gdn_decode": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                            _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                            _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                            _c_float, _c_float, _c_float, _c_int, _c_float, _c_void_p]),
+}
+
+_lib = None
+
+
+class GDNError(RuntimeError):
+    """A call into the library returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load (once) and return the library; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m gated_delta_rule_61_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise GDNError(status, f"{L.gdn_status_string(status).decode()}: {L.gdn_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _io_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return GDN_DTYPE_BF16
+    if dtype == torch.float32:
+        return GDN_DTYPE_F32
+    raise TypeError(f"io dtype must be bfloat16 or float32, got {dtype}")
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype], shape, device) -> None:
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+STAGES = ("varlen_tables", "intra", "scan", "decode")
+
+
+def profile_enable(on: bool = True) -> None:
+    """Record HIP events around every kernel the library launches."""
+    _check(lib().gdn_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """Wait for the recorded events; return {stage: (total_ms, launches)}."""
+    ms = (ctypes.c_double * len(STAGES))()
+    cnt = (_c_int * len(STAGES))()
+    _check(lib().gdn_profile_read(ms, cnt))
+    return {name: (ms[i], cnt[i]) for i, name in enumerate(STAGES)}
+
+
+def workspace_bytes(B: int, T: int, Hk: int, HV: int, K: int, V: int, num_seqs: int,
+                    dtype: torch.dtype, kda: bool = False) -> int:
+    fn = lib().kda_chunk_fwd_workspace_bytes if kda else lib().gdn_chunk_fwd_workspace_bytes
+    return int(fn(B, T, Hk, HV, K, V, num_seqs, _io_code(dtype)))
+
+
+def _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, gate, gate_shape_tail, gate_name):
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
+        raise ValueError("q, k must be [B, T, Hk, K] and v [B, T, HV, V]")
+    B, T, Hk, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    dev = q.device
+    io = q.dtype
+    _io_code(io)
+    _need(q, "q", io, None, dev)
+    _need(k, "k", io, None, dev)
+    _need(v, "v", io, (B, T, HV, V), dev)
+    _need(beta, "beta", torch.float32, (B, T, HV), dev)
+    _need(gate, gate_name, torch.float32, (B, T, HV) + gate_shape_tail, dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int64, None, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    _need(h0, "h0", torch.float32, (N, HV, V, K), dev)
+    return B, T, Hk, HV, K, V, N, dev, io
+
+
+def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
+                  beta: torch.Tensor, scale: Optional[float] = None,
+                  h0: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """GDN chunked prefill.  Returns (o [B,T,HV,V], ht [N,HV,V,K] fp32 or None)."""
+    B, T, Hk, HV, K, V, N, dev, io = _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, g, (), "g")
+    if scale is None:
+        scale = K ** -0.5
+    o = torch.empty((B, T, HV, V), dtype=io, device=dev) if out is None else out
+    _need(o, "out", io, (B, T, HV, V), dev)
+    ht = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if output_final_state else None
+    nbytes = workspace_bytes(B, T, Hk, HV, K, V, N, io)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                               _ptr(h0), _ptr(ht), _ptr(cu_seqlens), N,
+                               B, T, Hk, HV, K, V, chunk_size, _io_code(io),
+                               _ptr(o), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return o, ht
+
+
+def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
+                  beta: torch.Tensor, scale: Optional[float] = None,
+                  h0: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                  return_intra: bool = True, workspace: Optional[torch.Tensor] = None):
+    """KDA chunked prefill.  Returns (o, ht, Aqk, Akk_inv); the last two are
+    [B,T,HV,64] in the io dtype (None when ``return_intra`` is False)."""
+    if gk is None:
+        raise ValueError("gk is required")
+    B, T, Hk, HV, K, V, N, dev, io = _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, gk,
+                                                   (q.shape[-1],), "gk")
+    if scale is None:
+        scale = K ** -0.5
+    o = torch.empty((B, T, HV, V), dtype=io, device=dev)
+    ht = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if output_final_state else None
+    Aqk = Akk = None
+    if return_intra:
+        Aqk = torch.zeros((B, T, HV, chunk_size), dtype=io, device=dev)
+        Akk = torch.zeros((B, T, HV, chunk_size), dtype=io, device=dev)
+    nbytes = workspace_bytes(B, T, Hk, HV, K, V, N, io, kda=True)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gk), _ptr(beta), float(scale),
+                               _ptr(h0), _ptr(ht), _ptr(cu_seqlens), N,
+                               B, T, Hk, HV, K, V, chunk_size, _io_code(io),
+                               _ptr(o), _ptr(Aqk), _ptr(Akk), _ptr(workspace), workspace.numel(),
+                               _stream(dev)))
+    return o, ht, Aqk, Akk
+
+
+def gdn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+               A_log: torch.Tensor, dt_bias: torch.Tensor, state: torch.Tensor,
+               state_indices: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+               softplus_beta: float = 1.0, softplus_threshold: float = 20.0,
+               use_qk_l2norm: bool = True, eps: float = 1e-6,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode T = 1..4 tokens; ``state`` [pool,HV,V,K] bf16 is updated in place.
+    Returns o [B,T,HV,V] bf16."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, K]")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    dev = q.device
+    bf = torch.bfloat16
+    _need(q, "q", bf, None, dev)
+    _need(k, "k", bf, (B, T, H, K), dev)
+    _need(v, "v", bf, (B, T, HV, V), dev)
+    _need(a, "a", bf, (B, T, HV), dev)
+    _need(b, "b", bf, (B, T, HV), dev)
+    _need(A_log, "A_log", torch.float32, (HV,), dev)
+    _need(dt_bias, "dt_bias", torch.float32, (HV,), dev)
+    if state.dim() != 4:
+        raise ValueError("state must be [pool, HV, V, K]")
+    _need(state, "state", bf, (state.shape[0], HV, V, K), dev)
+    if state_indices is not None:
+        if state_indices.dtype != torch.int32:
+            state_indices = state_indices.to(torch.int32)
+        _need(state_indices, "state_indices", torch.int32, (B,), dev)
+    if scale is None:
+        scale = K ** -0.5
+    o = torch.empty((B, T, HV, V), dtype=bf, device=dev) if out is None else out
+    _need(o, "out", bf, (B, T, HV, V), dev)
+    _check(lib().gdn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                            _ptr(state), _ptr(state_indices), _ptr(o),
+                            B, T, H, HV, K, V, state.shape[0],
+                            float(scale), float(softplus_beta), float(softplus_threshold),
+                            1 if use_qk_l2norm else 0, float(eps), _stream(dev)))
+    return o

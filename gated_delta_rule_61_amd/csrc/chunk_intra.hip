@@ -1,0 +1,314 @@
+// Chunk-parallel part of the chunked prefill, gfx950: per (chunk, v-head)
+//   Aqk  = scale * (Q K^T  o  Gamma)  on s <= t          (causal, gated)
+//   A    = beta_t (K K^T o Gamma)     on s <  t          (strictly lower)
+//   Ainv = (I + A)^-1
+// with Gamma_ts = exp(G_t - G_s) for GDN (G = chunk-local cumulative log-gate)
+// or the per-channel gated dot products for KDA.
+//
+// What is computed follows "sglang srt/layers/attention/fla/chunk_fwd.py"
+// (chunk_gated_delta_rule_fwd_kkt_solve_kernel, steps 1-5: the ten lower
+// 16 x 16 blocks of K K^T, gate and beta scaling with the strictly-lower mask
+// on the diagonal blocks, forward substitution on the four diagonal blocks,
+// the block merge Ai10 = -Ai11 A10 Ai00, ..., Ai30 = -Ai33 (A30 Ai00 + A31
+// Ai10 + A32 Ai20)) and, for the per-channel gate, "vLLM kimi_k3 amd ops
+// kda/chunk_intra" (chunk_kda_fwd_kernel_inter_solve_fused: off-diagonal
+// Aqk / Akk with a reference row, beta on Akk rows, scale on Aqk).
+//
+// gfx950 design: one wave64 per (chunk, v-head).
+//   * the ten lower 16 x 16 blocks of K K^T and Q K^T run as bf16
+//     v_mfma_f32_16x16x32 (fp32 io: v_mfma_f32_16x16x4_f32) straight from
+//     global memory -- the same k fragment serves as A and B operand;
+//   * gate / beta / mask are applied to the fp32 accumulators;
+//   * the substitution gives lane (b, j) column j of the inverse of diagonal
+//     block b: 16 lanes per block, 4 blocks in parallel, fp32 FMAs on
+//     registers with the A rows broadcast from LDS;
+//   * the merge runs as fp32 v_mfma_f32_16x16x4 chains inside the wave; an
+//     accumulator is reused as the next product's B operand without a trip
+//     through LDS (its lane layout equals the B layout up to a permutation of
+//     the reduction index, which the A operand mirrors);
+//   * results are staged in LDS and written as 16-byte rows.
+// Everything is kept in fp32 until the final store in the io dtype.
+
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int BT = 64;
+constexpr int AP = 68;  // padded fp32 row of the 64 x 64 LDS tile
+
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Locate the chunk of this work-group: sets [c0, c0 + nrow) and returns false
+// when the slot is past the last chunk.
+__device__ __forceinline__ bool locate_chunk(const int64_t* __restrict__ cu,
+                                             const int32_t* __restrict__ coff,
+                                             int N, int T, int NT, int& c0, int& nrow) {
+  const int c = blockIdx.x;
+  int bos, eos, it;
+  if (cu) {
+    if (c >= coff[N]) return false;
+    int lo = 0, hi = N;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (coff[mid] <= c) lo = mid; else hi = mid;
+    }
+    long long b0 = cu[lo], b1 = cu[lo + 1];
+    b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
+    b1 = b1 < b0 ? b0 : (b1 > T ? T : b1);
+    bos = (int)b0;
+    eos = (int)b1;
+    it = c - coff[lo];
+  } else {
+    const int b = c / NT;
+    it = c - b * NT;
+    bos = b * T;
+    eos = bos + T;
+  }
+  c0 = bos + BT * it;
+  nrow = eos - c0 < BT ? eos - c0 : BT;
+  return nrow > 0;
+}
+
+// Store the 64 x 64 fp32 LDS tile as rows of an [tokens, HV, 64] io-dtype
+// array (rows >= nrow skipped), 16 bytes per lane and access.
+template <typename T>
+__device__ __forceinline__ void store_tile(const float (*sA)[AP], T* __restrict__ out,
+                                          int c0, int nrow, int HV, int j, int lane) {
+  constexpr int PER = 16 / sizeof(T);        // elements per 16-byte vector
+  constexpr int SEGS = BT / PER;             // vectors per row
+#pragma unroll
+  for (int it = 0; it < BT * SEGS / 64; ++it) {
+    const int idx = it * 64 + lane;
+    const int r = idx / SEGS, sg = idx % SEGS;
+    if (r < nrow) {
+      T* p = out + ((size_t)(c0 + r) * HV + j) * BT + sg * PER;
+      if constexpr (sizeof(T) == 2) {
+        uint4 w;
+        const float* s = &sA[r][sg * 8];
+        w.x = pack2<T>(s[0], s[1]);
+        w.y = pack2<T>(s[2], s[3]);
+        w.z = pack2<T>(s[4], s[5]);
+        w.w = pack2<T>(s[6], s[7]);
+        *reinterpret_cast<uint4*>(p) = w;
+      } else {
+        const float* s = &sA[r][sg * 4];
+        *reinterpret_cast<float4*>(p) = make_float4(s[0], s[1], s[2], s[3]);
+      }
+    }
+  }
+}
+
+// tile index of lower block (rb, cb), cb <= rb
+__host__ __device__ constexpr int tix(int rb, int cb) { return rb * (rb + 1) / 2 + cb; }
+
+// -------------------------------------------------------------------------
+// Solve (I + A)^-1 for the strictly lower 64 x 64 fp32 matrix held in sA and
+// leave the inverse (unit lower, zero upper part) in sA.
+// -------------------------------------------------------------------------
+__device__ __forceinline__ void solve_unit_lower_64(float (*sA)[AP], int lane) {
+  const int b = lane >> 4, jj = lane & 15;
+  // forward substitution, column jj of diagonal block b
+  float X[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float* arow = &sA[16 * b + i][16 * b];
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int m = 0; m < i; m += 2) {
+      acc0 = fmaf(arow[m], X[m], acc0);
+      if (m + 1 < i) acc1 = fmaf(arow[m + 1], X[m + 1], acc1);
+    }
+    X[i] = (i == jj) ? 1.0f : ((i < jj) ? 0.0f : -(acc0 + acc1));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sA[16 * b + i][16 * b + jj] = X[i];
+  __syncthreads();
+
+  // block merge: X_rc = -X_rr * sum_{m=c}^{r-1} A_rm X_mc, fp32 MFMA 16x16x4.
+  const int row = lane & 15, grp = lane >> 4;
+  // A operand of block (br, bc): lane holds M[16br + row][16bc + 4grp + s]
+  auto mmA = [&](int br, int bc, const f32x4& Bv, f32x4 c) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * br + row][16 * bc + 4 * grp + s], Bv[s], c, 0, 0, 0);
+    return c;
+  };
+  // B operand of diagonal block d from LDS, in accumulator layout
+  auto diagB = [&](int d) {
+    f32x4 r;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r[s] = sA[16 * d + 4 * grp + s][16 * d + row];
+    return r;
+  };
+  const f32x4 X00 = diagB(0), X11 = diagB(1), X22 = diagB(2);
+  f32x4 P;
+  // column block 0
+  P = mmA(1, 0, X00, zero4());
+  f32x4 X10 = -mmA(1, 1, P, zero4());
+  P = mmA(2, 0, X00, zero4());
+  P = mmA(2, 1, X10, P);
+  f32x4 X20 = -mmA(2, 2, P, zero4());
+  P = mmA(3, 0, X00, zero4());
+  P = mmA(3, 1, X10, P);
+  P = mmA(3, 2, X20, P);
+  f32x4 X30 = -mmA(3, 3, P, zero4());
+  // column block 1
+  P = mmA(2, 1, X11, zero4());
+  f32x4 X21 = -mmA(2, 2, P, zero4());
+  P = mmA(3, 1, X11, zero4());
+  P = mmA(3, 2, X21, P);
+  f32x4 X31 = -mmA(3, 3, P, zero4());
+  // column block 2
+  P = mmA(3, 2, X22, zero4());
+  f32x4 X32 = -mmA(3, 3, P, zero4());
+  __syncthreads();
+  auto put = [&](int br, int bc, const f32x4& Xv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sA[16 * br + 4 * grp + i][16 * bc + row] = Xv[i];
+  };
+  put(1, 0, X10); put(2, 0, X20); put(3, 0, X30);
+  put(2, 1, X21); put(3, 1, X31); put(3, 2, X32);
+  __syncthreads();
+}
+
+// -------------------------------------------------------------------------
+// GDN intra kernel (scalar gate)
+// -------------------------------------------------------------------------
+template <typename T, int DK, typename C = typename ComputeOf<T>::type>
+__global__ __launch_bounds__(64) void gdn_intra_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, float scale, C* __restrict__ Ainv,
+    C* __restrict__ Aqk, const int64_t* __restrict__ cu, const int32_t* __restrict__ coff,
+    int Tlen, int N, int NT, int Hk, int HV) {
+  __shared__ __attribute__((aligned(16))) float sA[BT][AP];
+  const int lane = threadIdx.x;
+  const int j = blockIdx.y;
+  int c0, nrow;
+  if (!locate_chunk(cu, coff, N, Tlen, NT, c0, nrow)) return;
+  const int jk = j / (HV / Hk);
+  const int row = lane & 15, grp = lane >> 4;
+
+  // chunk-local cumulative gate and beta, lane = token
+  const float gl = (g && lane < nrow) ? g[(size_t)(c0 + lane) * HV + j] : 0.f;
+  const float G = wave_incl_scan(gl, lane);
+  const float bl = lane < nrow ? beta[(size_t)(c0 + lane) * HV + j] : 0.f;
+
+  // Step 1: ten lower blocks of K K^T and Q K^T
+  f32x4 KK[10], QK[10];
+#pragma unroll
+  for (int t = 0; t < 10; ++t) { KK[t] = zero4(); QK[t] = zero4(); }
+#pragma unroll
+  for (int s = 0; s < DK / 32; ++s) {
+    Frag<T> kf[4], qf[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = 16 * rb + row;
+      if (r < nrow) {
+        const size_t off = ((size_t)(c0 + r) * Hk + jk) * DK + 32 * s + 8 * grp;
+        load8(kf[rb], k + off);
+        load8(qf[rb], q + off);
+      } else {
+        kf[rb].zero();
+        qf[rb].zero();
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb <= rb; ++cb) {
+        KK[tix(rb, cb)] = mma(kf[rb], kf[cb], KK[tix(rb, cb)]);
+        QK[tix(rb, cb)] = mma(qf[rb], kf[cb], QK[tix(rb, cb)]);
+      }
+  }
+
+  // Step 2: gate / beta / mask.  Lane holds rows 16rb + 4grp + i, column 16cb + row.
+  float Gr[4][4], Br[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      Gr[rb][i] = __shfl(G, 16 * rb + 4 * grp + i, 64);
+      Br[rb][i] = __shfl(bl, 16 * rb + 4 * grp + i, 64);
+    }
+  float Gc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) Gc[cb] = __shfl(G, 16 * cb + row, 64);
+
+  // Aqk -> LDS (upper blocks zero) -> global
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + 4 * grp + i, s = 16 * cb + row;
+        float val = 0.f;
+        if (cb <= rb && s <= r) val = scale * QK[tix(rb, cb < rb ? cb : rb)][i] * __expf(Gr[rb][i] - Gc[cb]);
+        sA[r][s] = val;
+      }
+  __syncthreads();
+  store_tile<C>(sA, Aqk, c0, nrow, HV, j, lane);
+  __syncthreads();
+  // A = beta_r (k_r . k_s) exp(G_r - G_s), s < r
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + 4 * grp + i, s = 16 * cb + row;
+        float val = 0.f;
+        if (cb <= rb && s < r) val = Br[rb][i] * KK[tix(rb, cb < rb ? cb : rb)][i] * __expf(Gr[rb][i] - Gc[cb]);
+        sA[r][s] = val;
+      }
+  __syncthreads();
+
+  // Steps 3-4: substitution + merge
+  solve_unit_lower_64(sA, lane);
+
+  // Step 5: store
+  store_tile<C>(sA, Ainv, c0, nrow, HV, j, lane);
+}
+
+}  // namespace
+
+hipError_t launch_intra_gdn(const ChunkArgs& a, hipStream_t s, int NT, int nslots) {
+  const dim3 grid((unsigned)nslots, (unsigned)a.HV);
+  if (a.bf16) {
+    if (a.K == 128)
+      hipLaunchKernelGGL((gdn_intra_kernel<bf16_t, 128>), grid, dim3(64), 0, s,
+                         (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, a.scale,
+                         (f16_t*)a.Ainv, (f16_t*)a.Aqk, a.cu_seqlens, a.chunk_off,
+                         a.T, a.N, NT, a.Hk, a.HV);
+    else
+      hipLaunchKernelGGL((gdn_intra_kernel<bf16_t, 64>), grid, dim3(64), 0, s,
+                         (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, a.scale,
+                         (f16_t*)a.Ainv, (f16_t*)a.Aqk, a.cu_seqlens, a.chunk_off,
+                         a.T, a.N, NT, a.Hk, a.HV);
+  } else {
+    if (a.K == 128)
+      hipLaunchKernelGGL((gdn_intra_kernel<float, 128>), grid, dim3(64), 0, s,
+                         (const float*)a.q, (const float*)a.k, a.g, a.beta, a.scale,
+                         (float*)a.Ainv, (float*)a.Aqk, a.cu_seqlens, a.chunk_off,
+                         a.T, a.N, NT, a.Hk, a.HV);
+    else
+      hipLaunchKernelGGL((gdn_intra_kernel<float, 64>), grid, dim3(64), 0, s,
+                         (const float*)a.q, (const float*)a.k, a.g, a.beta, a.scale,
+                         (float*)a.Ainv, (float*)a.Aqk, a.cu_seqlens, a.chunk_off,
+                         a.T, a.N, NT, a.Hk, a.HV);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,355 @@
+// C ABI of the library: argument validation (host only, before any HIP call),
+// workspace layout, and the launch sequence of each entry point.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/gdn61.h"
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+hipError_t launch_intra_gdn(const ChunkArgs& a, hipStream_t s, int NT, int nslots);
+hipError_t launch_scan_gdn(const ChunkArgs& a, hipStream_t s);
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Chunk tables for packed variable-length batches: chunk offsets (exclusive
+// prefix of ceil(len / 64)) and the sequence order by decreasing length.
+// One work-group; N up to any size for the offsets, the order is sorted for
+// N <= 1024 and left as the identity beyond.
+__global__ __launch_bounds__(1024) void varlen_tables_kernel(const int64_t* __restrict__ cu, int N,
+                                                              int T, int32_t* __restrict__ coff,
+                                                              int32_t* __restrict__ order) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int per = (N + 1023) / 1024;
+  const int lo = t * per, hi = lo + per < N ? lo + per : N;
+  auto len = [&](int i) {
+    long long b0 = cu[i], b1 = cu[i + 1];
+    b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
+    b1 = b1 < b0 ? b0 : (b1 > T ? T : b1);
+    return (int)(b1 - b0);
+  };
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += (len(i) + 63) / 64;
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int x = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += x;
+    __syncthreads();
+  }
+  int run = t ? part[t - 1] : 0;
+  for (int i = lo; i < hi; ++i) {
+    coff[i] = run;
+    run += (len(i) + 63) / 64;
+  }
+  if (t == 1023) coff[N] = part[1023];
+  if (N <= 1024) {
+    if (t < N) {
+      const int li = len(t);
+      int rank = 0;
+      for (int m = 0; m < N; ++m) {
+        const int lm = len(m);
+        rank += (lm > li) || (lm == li && m < t);
+      }
+      order[rank] = t;
+    }
+  } else {
+    for (int i = t; i < N; i += 1024) order[i] = i;
+  }
+}
+
+struct Problem {
+  int B, T, Hk, HV, K, V, N;
+};
+
+int check_chunk(const void* q, const void* k, const void* v, const float* gate,
+                bool gate_required, const float* beta, const float* h0, float* ht,
+                const int64_t* cu, int num_seqs, int B, int T, int Hk, int HV, int K, int V,
+                int chunk_size, int dtype, const void* o, Problem& P) {
+  if (B < 0 || T < 0 || Hk <= 0 || HV <= 0 || K <= 0 || V <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "sizes must be positive (B, T >= 0): B=%d T=%d Hk=%d HV=%d K=%d V=%d",
+                B, T, Hk, HV, K, V);
+  if (HV % Hk != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "HV (%d) must be a multiple of Hk (%d)", HV, Hk);
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "unknown dtype code %d", dtype);
+  if (chunk_size != 64)
+    return fail(GDN_ERR_UNSUPPORTED, "chunk_size must be 64 (got %d)", chunk_size);
+  if (!((K == 64 && V == 64) || (K == 128 && V == 128)))
+    return fail(GDN_ERR_UNSUPPORTED, "supported head dims are K = V in {64, 128} (got K=%d V=%d)", K, V);
+  if ((long long)B * T >= (1LL << 31) / 64)
+    return fail(GDN_ERR_UNSUPPORTED, "B*T too large (got %lld tokens)", (long long)B * T);
+  if (cu) {
+    if (B != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens requires B == 1 (got B=%d)", B);
+    if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", num_seqs);
+    P.N = num_seqs;
+  } else {
+    P.N = B;
+  }
+  const bool work = (long long)B * T > 0;
+  if (work && (!q || !k || !v || !beta || !o))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, beta and o are required");
+  if (work && gate_required && !gate) return fail(GDN_ERR_INVALID_ARGUMENT, "gk is required");
+  const void* ptrs[] = {q, k, v, gate, beta, h0, ht, o};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(GDN_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  P.B = B; P.T = T; P.Hk = Hk; P.HV = HV; P.K = K; P.V = V;
+  return GDN_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- profiler
+namespace {
+struct ProfRec {
+  int stage;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;     // recorded, not yet read
+std::vector<hipEvent_t> g_prof_free;  // reusable events
+hipEvent_t prof_event() {
+  if (!g_prof_free.empty()) {
+    hipEvent_t e = g_prof_free.back();
+    g_prof_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+thread_local hipEvent_t t_open[GDN_STAGE_COUNT];
+}  // namespace
+
+void prof_begin(int stage, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  hipEvent_t e = prof_event();
+  if (e && hipEventRecord(e, s) == hipSuccess) t_open[stage] = e;
+}
+
+void prof_end(int stage, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || !t_open[stage]) return;
+  hipEvent_t e = prof_event();
+  if (e && hipEventRecord(e, s) == hipSuccess) g_prof_recs.push_back({stage, t_open[stage], e});
+  t_open[stage] = nullptr;
+}
+
+ChunkWorkspace chunk_workspace_layout(long long tokens, int HV, int N, int elem_bytes) {
+  ChunkWorkspace w;
+  const size_t mat = (size_t)tokens * HV * 64 * elem_bytes;
+  w.ainv_off = 0;
+  w.aqk_off = up(mat);
+  w.coff_off = w.aqk_off + up(mat);
+  w.order_off = w.coff_off + up((size_t)(N + 1) * 4);
+  w.total = w.order_off + up((size_t)(N > 0 ? N : 1) * 4);
+  return w;
+}
+
+hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t s) {
+  if (a.cu_seqlens) {
+    prof_begin(GDN_STAGE_VARLEN_TABLES, s);
+    hipLaunchKernelGGL(varlen_tables_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.N, a.T,
+                       a.chunk_off, a.seq_order);
+    hipError_t e = hipGetLastError();
+    prof_end(GDN_STAGE_VARLEN_TABLES, s);
+    if (e != hipSuccess) return e;
+  }
+  const int NT = (a.T + 63) / 64;
+  const int nslots = a.cu_seqlens ? NT + a.N : a.B * NT;
+  if (nslots > 0 && (long long)a.B * a.T > 0) {
+    prof_begin(GDN_STAGE_INTRA, s);
+    hipError_t e = launch_intra_gdn(a, s, NT, nslots);
+    prof_end(GDN_STAGE_INTRA, s);
+    if (e != hipSuccess) return e;
+  }
+  prof_begin(GDN_STAGE_SCAN, s);
+  const hipError_t e = launch_scan_gdn(a, s);
+  prof_end(GDN_STAGE_SCAN, s);
+  return e;
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "unsupported";
+    case GDN_ERR_WORKSPACE: return "workspace too small";
+    case GDN_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+const char* gdn_version(void) { return "gdn61 0.1 gfx950"; }
+
+size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V, int num_seqs,
+                                     int dtype) {
+  if (B < 0 || T < 0 || Hk <= 0 || HV <= 0 || K <= 0 || V <= 0 || num_seqs < 0) return 0;
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return 0;
+  const int N = num_seqs > B ? num_seqs : B;
+  return chunk_workspace_layout((long long)B * T, HV, N, dtype == GDN_DTYPE_BF16 ? 2 : 4).total;
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V, int num_seqs,
+                                     int dtype) {
+  return gdn_chunk_fwd_workspace_bytes(B, T, Hk, HV, K, V, num_seqs, dtype);
+}
+
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  float scale, const float* h0, float* ht, const int64_t* cu_seqlens,
+                  int num_seqs, int B, int T, int Hk, int HV, int K, int V, int chunk_size,
+                  int dtype, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  Problem P;
+  int st = check_chunk(q, k, v, g, false, beta, h0, ht, cu_seqlens, num_seqs, B, T, Hk, HV, K, V,
+                       chunk_size, dtype, o, P);
+  if (st != GDN_OK) return st;
+  const int eb = dtype == GDN_DTYPE_BF16 ? 2 : 4;
+  const ChunkWorkspace L = chunk_workspace_layout((long long)B * T, HV, P.N, eb);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (P.N == 0) return ok();
+  char* ws = (char*)workspace;
+  ChunkArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.gk = nullptr; a.beta = beta; a.scale = scale;
+  a.h0 = h0; a.ht = ht; a.cu_seqlens = cu_seqlens; a.N = P.N;
+  a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
+  a.bf16 = dtype == GDN_DTYPE_BF16;
+  a.o = o;
+  a.Ainv = ws + L.ainv_off;
+  a.Aqk = ws + L.aqk_off;
+  a.chunk_off = cu_seqlens ? (int32_t*)(ws + L.coff_off) : nullptr;
+  a.seq_order = cu_seqlens ? (int32_t*)(ws + L.order_off) : nullptr;
+  a.max_chunks = (T + 63) / 64 + (cu_seqlens ? P.N : 0);
+  const hipError_t e = launch_chunk_fwd(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* gk, const float* beta,
+                  float scale, const float* h0, float* ht, const int64_t* cu_seqlens,
+                  int num_seqs, int B, int T, int Hk, int HV, int K, int V, int chunk_size,
+                  int dtype, void* o, void* Aqk, void* Akk_inv, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  Problem P;
+  int st = check_chunk(q, k, v, gk, true, beta, h0, ht, cu_seqlens, num_seqs, B, T, Hk, HV, K, V,
+                       chunk_size, dtype, o, P);
+  if (st != GDN_OK) return st;
+  if ((Aqk && !aligned16(Aqk)) || (Akk_inv && !aligned16(Akk_inv)))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  (void)workspace; (void)workspace_bytes; (void)stream; (void)scale;
+  return fail(GDN_ERR_UNSUPPORTED, "kda_chunk_fwd: per-channel gate path not built yet");
+}
+
+int gdn_decode(const void* q, const void* k, const void* v, const void* a, const void* b,
+               const float* A_log, const float* dt_bias, void* state,
+               const int32_t* state_indices, void* o, int B, int T, int H, int HV, int K, int V,
+               int pool, float scale, float softplus_beta, float softplus_threshold,
+               int use_qk_l2norm, float eps, void* stream) {
+  if (B < 0 || H <= 0 || HV <= 0 || K <= 0 || V <= 0 || pool < 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "sizes must be positive: B=%d H=%d HV=%d K=%d V=%d pool=%d",
+                B, H, HV, K, V, pool);
+  if (T < 1 || T > 4) return fail(GDN_ERR_INVALID_ARGUMENT, "decode supports T = 1..4 (got T=%d)", T);
+  if (HV % H != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "HV (%d) must be a multiple of H (%d)", HV, H);
+  if (K != 128 || V != 128)
+    return fail(GDN_ERR_UNSUPPORTED, "decode supports K = V = 128 (got K=%d V=%d)", K, V);
+  if (!state_indices && pool < B)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "identity slots need pool >= B (pool=%d B=%d)", pool, B);
+  if (!(softplus_beta > 0.f)) return fail(GDN_ERR_INVALID_ARGUMENT, "softplus_beta must be > 0");
+  if (!(eps >= 0.f)) return fail(GDN_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  if (B == 0) return ok();
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !state || !o)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, a, b, A_log, dt_bias, state and o are required");
+  const void* ptrs[] = {q, k, v, state, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, state and o must be 16-byte aligned");
+  if ((long long)pool * HV * V * K >= (1LL << 40)) return fail(GDN_ERR_UNSUPPORTED, "state pool too large");
+  DecodeArgs d;
+  d.q = q; d.k = k; d.v = v; d.a = a; d.b = b; d.A_log = A_log; d.dt_bias = dt_bias;
+  d.state = state; d.idx = state_indices; d.o = o;
+  d.B = B; d.T = T; d.H = H; d.HV = HV; d.K = K; d.V = V; d.pool = pool;
+  d.scale = scale; d.sp_beta = softplus_beta; d.sp_thr = softplus_threshold; d.eps = eps;
+  d.use_norm = use_qk_l2norm != 0;
+  prof_begin(GDN_STAGE_DECODE, (hipStream_t)stream);
+  const hipError_t e = launch_decode(d, (hipStream_t)stream);
+  prof_end(GDN_STAGE_DECODE, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int gdn_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return GDN_OK;
+}
+
+int gdn_profile_read(double* ms, int* counts) {
+  std::vector<ProfRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    recs.swap(g_prof_recs);
+  }
+  int status = GDN_OK;
+  for (const ProfRec& r : recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+      status = fail(GDN_ERR_LAUNCH, "event timing failed");
+      continue;
+    }
+    if (ms) ms[r.stage] += t;
+    if (counts) counts[r.stage] += 1;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (const ProfRec& r : recs) {
+    g_prof_free.push_back(r.a);
+    g_prof_free.push_back(r.b);
+  }
+  return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Device-side building blocks shared by the gfx950 kernels of this library:
+// MFMA fragment types and wrappers, bf16 conversion, 16-lane DPP reductions.
+//
+// MFMA conventions (CDNA3/CDNA4, wave64), used by every contraction here:
+//   * A 16 x 32 "slab" operand: lane l holds 8 values of row (l % 16) at
+//     reduction positions 8 * (l / 16) + e, e = 0..7.  The B operand (32 x 16)
+//     is the mirror image: lane l holds column (l % 16) at the same reduction
+//     positions.  A and B pair their slots identically, so any placement of
+//     the reduction index that both operands share gives the full sum.
+//   * A 16 x 16 fp32 accumulator: lane l holds rows 4 * (l / 16) + i,
+//     i = 0..3, of column (l % 16).
+// bf16 slabs run as one v_mfma_f32_16x16x32_bf16; fp32 slabs as eight
+// v_mfma_f32_16x16x4_f32 (slot e of every lane in step e), which keeps the
+// exact fp32 products for fp32 inputs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16_t;   // compute type of the bf16-io contractions
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t bf16_t;  // raw bf16 bits in memory
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf2f(bf16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+// Round-to-nearest-even float -> bf16 (the hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16_t f2bf(float x) {
+  return __builtin_bit_cast(bf16_t, (__bf16)x);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// ------------------------------------------------------- 16-lane reductions
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
+// quad_perm [1,0,3,2] and [2,3,0,1] sum each quad, row_half_mirror adds the
+// neighbouring quad, row_mirror the other half row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  return x;
+}
+
+// ---------------------------------------------------------- MFMA fragments
+// Fragment of one 16 x 32 slab for element type T (bf16 or fp32).
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+  bf16x8 v;
+  __device__ __forceinline__ void zero() {
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+  }
+  __device__ __forceinline__ void set(int e, float x) { v[e] = (__bf16)x; }
+  __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
+};
+template <> struct Frag<f16_t> {
+  f16x8 v;
+  __device__ __forceinline__ void zero() {
+    for (int e = 0; e < 8; ++e) v[e] = (_Float16)0.0f;
+  }
+  __device__ __forceinline__ void set(int e, float x) {
+    v[e] = (_Float16)__builtin_amdgcn_fmed3f(x, -65504.0f, 65504.0f);
+  }
+  __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
+};
+template <> struct Frag<float> {
+  f32x8 v;
+  __device__ __forceinline__ void zero() {
+    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+  }
+  __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
+  __device__ __forceinline__ float get(int e) const { return v[e]; }
+};
+
+__device__ __forceinline__ f32x4 mma(const Frag<bf16_t>& a, const Frag<bf16_t>& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<f16_t>& a, const Frag<f16_t>& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<float>& a, const Frag<float>& b, f32x4 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+  return c;
+}
+
+// Load 8 consecutive elements (one slab row segment) from memory of type T
+// into a fragment; the pointer must be 16-byte (bf16) / 32-byte (fp32)
+// aligned.
+__device__ __forceinline__ void load8(Frag<bf16_t>& f, const bf16_t* p) {
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void load8(Frag<f16_t>& f, const f16_t* p) {
+  f.v = *reinterpret_cast<const f16x8*>(p);
+}
+__device__ __forceinline__ void load8(Frag<float>& f, const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// Element conversions between the io / compute types and fp32.  Conversions
+// to fp16 saturate at +-65504, so no finite input becomes inf.
+__device__ __forceinline__ float to_f(bf16_t x) { return bf2f(x); }
+__device__ __forceinline__ float to_f(f16_t x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float x) { return f2bf(x); }
+template <> __device__ __forceinline__ f16_t from_f<f16_t>(float x) {
+  return (_Float16)__builtin_amdgcn_fmed3f(x, -65504.0f, 65504.0f);
+}
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+
+// Convert a fragment between element types (identity when equal).
+template <typename C, typename T>
+__device__ __forceinline__ Frag<C> conv(const Frag<T>& a) {
+  if constexpr (__is_same(C, T)) {
+    return a;
+  } else {
+    Frag<C> r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.set(e, a.get(e));
+    return r;
+  }
+}
+
+// Compute type of the MFMA operands for an io type: fp16 for bf16 io (one
+// rounding of 2^-11 instead of 2^-8 on every intermediate operand; the
+// bf16 inputs themselves convert exactly in fp16's normal range), fp32 for
+// fp32 io.
+template <typename T> struct ComputeOf;
+template <> struct ComputeOf<bf16_t> { typedef f16_t type; };
+template <> struct ComputeOf<float> { typedef float type; };
+
+// Two floats -> two 16-bit values of type T packed in a word (lo first).
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, from_f<T>(lo)) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, from_f<T>(hi)) << 16);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace gdn

@@ -1,0 +1,53 @@
+// Host-side launch helpers of the gfx950 kernels (internal to the library).
+// Arguments have been validated by the C-ABI layer before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Per-stage event timing (enabled through gdn_profile_enable).
+void prof_begin(int stage, hipStream_t s);
+void prof_end(int stage, hipStream_t s);
+
+struct DecodeArgs {
+  const void *q, *k, *v, *a, *b;
+  const float *A_log, *dt_bias;
+  void* state;
+  const int32_t* idx;
+  void* o;
+  int B, T, H, HV, K, V, pool;
+  float scale, sp_beta, sp_thr, eps;
+  int use_norm;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// One chunked prefill problem (GDN: gk == nullptr; KDA: g == nullptr).
+struct ChunkArgs {
+  const void *q, *k, *v;
+  const float *g, *gk, *beta;
+  float scale;
+  const float* h0;
+  float* ht;
+  const int64_t* cu_seqlens;
+  int N;                 // sequences (B without cu_seqlens)
+  int B, T, Hk, HV, K, V;
+  int bf16;              // 1 = bf16 io, 0 = fp32 io
+  void* o;
+  void* Ainv;            // [B*T, HV, 64] io dtype: (I + A)^-1 rows
+  void* Aqk;             // [B*T, HV, 64] io dtype: scale * gated causal Q K^T rows
+  int32_t* chunk_off;    // [N + 1] varlen chunk offsets (workspace) or nullptr
+  int32_t* seq_order;    // [N] sequences, longest first (workspace) or nullptr
+  int max_chunks;        // upper bound of the total chunk count
+};
+hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t s);
+
+// Workspace layout shared by the size query and the launcher.
+struct ChunkWorkspace {
+  size_t ainv_off, aqk_off, coff_off, order_off, total;
+};
+ChunkWorkspace chunk_workspace_layout(long long BT_tokens, int HV, int N, int elem_bytes);
+
+}  // namespace gdn

@@ -1,0 +1,209 @@
+/*
+ * gdn61.h -- C ABI of the MI355X (gfx950) gated-delta-rule library.
+ *
+ * The library computes, for each (sequence, value head), the gated delta rule
+ *
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = scale * S_t q_t,
+ *
+ * with the state S held "V-first" as a V x K matrix (row = value channel,
+ * column = key channel, K contiguous).  GDN uses one log-gate g_t per token
+ * and v-head; KDA uses one per token, v-head and key channel, replacing
+ * exp(g_t) S by S diag(exp(gk_t)).  Sources, by page and section:
+ *   - "sglang srt/layers/attention/fla/chunk_fwd.py":
+ *     chunk_gated_delta_rule_fwd_intra (arguments k, v, g, beta, cu_seqlens,
+ *     chunk_size; A of shape [B, T, H, BT]) and the fused beta*K K^T +
+ *     solve_tril kernel;
+ *   - "fla ops/common/chunk_h.py": chunk_fwd_h (h0, output_final_state,
+ *     state_v_first, cu_seqlens; final state fp32);
+ *   - "vLLM kimi_k3 amd ops kda/chunk_intra": the KDA Aqk / Akk_inv outputs
+ *     (row-per-token layout [B, T, HV, BT], Aqk scaled by `scale`);
+ *   - "flashinfer gdn_kernels/gdn_decode_bf16_state.py": the public
+ *     gated_delta_rule entry (A_log, a, dt_bias, softplus_beta,
+ *     softplus_threshold, q, k, v, b, state pool [pool, HV, V, K] bf16
+ *     updated in place, per-batch slot indices int32, use_qk_l2norm,
+ *     scale; T = 1..4).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller, contiguous
+ *     and row-major in the stated shape, aligned to 16 bytes (the library
+ *     reads and writes 16-byte vectors).  The library allocates nothing,
+ *     keeps no state between calls and never synchronises the host.
+ *   - `stream` is a hipStream_t (NULL = the null stream); all work is queued
+ *     on it asynchronously, in stream order.
+ *   - Outputs must not alias inputs (the decode state, updated in place, is
+ *     the one exception).
+ *   - Every argument check runs on the host before any HIP call; a failed
+ *     check returns GDN_ERR_INVALID_ARGUMENT or GDN_ERR_UNSUPPORTED and
+ *     queues nothing.  gdn_last_error() then describes the failure.
+ *   - A launch failure reported by the HIP runtime returns GDN_ERR_LAUNCH.
+ *   - io dtype codes: GDN_DTYPE_F32 (0) or GDN_DTYPE_BF16 (1).
+ */
+#ifndef GDN61_H
+#define GDN61_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad size, bad layout */
+  GDN_ERR_UNSUPPORTED = 2,      /* valid request outside the compiled set     */
+  GDN_ERR_WORKSPACE = 3,        /* workspace missing or smaller than needed   */
+  GDN_ERR_LAUNCH = 4            /* the HIP runtime rejected a kernel launch   */
+} gdn_status_t;
+
+enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 };
+
+/* Static text for a status code. */
+const char* gdn_status_string(int status);
+
+/* Detail message of the last failing call made by this host thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char* gdn_last_error(void);
+
+/* Library version, e.g. "gdn61 0.1 gfx950". */
+const char* gdn_version(void);
+
+/*
+ * Workspace needed by gdn_chunk_fwd / kda_chunk_fwd, in bytes, for the
+ * given problem (num_seqs = N of cu_seqlens, or B without it).  Returns 0
+ * when the arguments are invalid.  The workspace holds the per-chunk
+ * (I + A)^-1 and masked, gated Q K^T blocks ([B*T, HV, 64] each, io dtype)
+ * and the varlen chunk tables.
+ */
+size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
+                                     int num_seqs, int dtype);
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
+                                     int num_seqs, int dtype);
+
+/*
+ * GDN chunked prefill forward (scalar gate).
+ *
+ *   q, k        [B, T, Hk, K]   io dtype
+ *   v           [B, T, HV, V]   io dtype
+ *   g           [B, T, HV]      fp32 per-token natural-log gate (the chunk-
+ *                               local cumulative sum is taken inside), or
+ *                               NULL for no decay
+ *   beta        [B, T, HV]      fp32
+ *   scale       output scale (callers usually pass K^-0.5)
+ *   h0          [N, HV, V, K]   fp32 initial state, or NULL for zeros
+ *   ht          [N, HV, V, K]   fp32 final state out, or NULL to skip
+ *   cu_seqlens  [N + 1]         int64 device array of packed sequence
+ *                               boundaries, or NULL.  With it B must be 1 and
+ *                               num_seqs = N; the values must satisfy
+ *                               0 = cu[0] <= cu[1] <= ... <= cu[N] = T
+ *                               (values outside [0, T] are clamped so no
+ *                               access leaves the buffers; results are then
+ *                               unspecified).  Without it num_seqs is ignored
+ *                               and N = B.
+ *   o           [B, T, HV, V]   io dtype output
+ *   workspace   device buffer of at least gdn_chunk_fwd_workspace_bytes()
+ *
+ * q/k head of v-head j is j / (HV / Hk) (HV must be a multiple of Hk).
+ * Supported: K = V in {64, 128}, chunk_size = 64, T >= 0.
+ * T = 0 (or all sequences empty) is valid: ht = h0 (or zeros) is written.
+ */
+int gdn_chunk_fwd(const void* q, const void* k, const void* v,
+                  const float* g, const float* beta, float scale,
+                  const float* h0, float* ht,
+                  const int64_t* cu_seqlens, int num_seqs,
+                  int B, int T, int Hk, int HV, int K, int V,
+                  int chunk_size, int dtype,
+                  void* o, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * KDA chunked prefill forward (one log-gate per key channel).
+ *
+ * As gdn_chunk_fwd, with
+ *   gk          [B, T, HV, K]   fp32 per-token, per-channel natural-log gate
+ *                               (required)
+ *   Aqk         [B, T, HV, 64]  io dtype out, or NULL: row t holds
+ *                               scale * sum_c q_t,c k_s,c exp(G_t,c - G_s,c)
+ *                               for the tokens s <= t of t's chunk, at column
+ *                               s - chunk_start; 0 elsewhere
+ *   Akk_inv     [B, T, HV, 64]  io dtype out, or NULL: row t holds row
+ *                               (t - chunk_start) of (I + A)^-1, where
+ *                               A_ts = beta_t sum_c k_t,c k_s,c
+ *                               exp(G_t,c - G_s,c) for s < t in the chunk;
+ *                               0 above the diagonal and past the chunk end
+ * (G = cumulative log-gate from the chunk start).
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v,
+                  const float* gk, const float* beta, float scale,
+                  const float* h0, float* ht,
+                  const int64_t* cu_seqlens, int num_seqs,
+                  int B, int T, int Hk, int HV, int K, int V,
+                  int chunk_size, int dtype,
+                  void* o, void* Aqk, void* Akk_inv,
+                  void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * GDN decode step over a bf16 state pool, T = 1..4 tokens per call.
+ *
+ *   q, k           [B, T, H, K]    bf16 (normalised in-kernel when
+ *                                  use_qk_l2norm != 0:
+ *                                  q * scale / sqrt(sum q^2 + eps),
+ *                                  k / sqrt(sum k^2 + eps))
+ *   v              [B, T, HV, V]   bf16
+ *   a, b           [B, T, HV]      bf16 gate inputs
+ *   A_log, dt_bias [HV]            fp32
+ *   state          [pool, HV, V, K] bf16, read and written IN PLACE: slot
+ *                                  indices[b] (or b when indices is NULL)
+ *                                  holds the state of batch row b
+ *   state_indices  [B] int32 device array, or NULL for the identity
+ *                  (then pool >= B is required).  A slot outside [0, pool)
+ *                  leaves the pool untouched and writes o = 0 for that row.
+ *                  Two rows naming the same slot race (undefined result).
+ *   o              [B, T, HV, V]   bf16 output
+ *
+ * Per token: x = a + dt_bias; softplus(x) = log(1 + exp(sb*x))/sb if
+ * sb*x <= threshold else x (sb = softplus_beta); alpha = exp(-exp(A_log)
+ * * softplus(x)); beta = sigmoid(b); S <- alpha S; delta = beta (v - S k);
+ * S <- S + delta k^T; o = S q.  The state is carried in fp32 across the T
+ * tokens and rounded to bf16 (nearest-even) once, after the last token.
+ * q/k head of v-head j is j / (HV / H).
+ * Supported: K = V = 128, T in 1..4.
+ */
+int gdn_decode(const void* q, const void* k, const void* v,
+               const void* a, const void* b,
+               const float* A_log, const float* dt_bias,
+               void* state, const int32_t* state_indices,
+               void* o,
+               int B, int T, int H, int HV, int K, int V, int pool,
+               float scale, float softplus_beta, float softplus_threshold,
+               int use_qk_l2norm, float eps,
+               void* stream);
+
+/*
+ * Per-stage timing for measurement tools.  While enabled, every call of the
+ * entry points above records a pair of HIP events on the caller's stream
+ * around each kernel it launches (stage ids below); this adds two event
+ * records per kernel and nothing else.  gdn_profile_read() waits for the
+ * recorded events, adds their elapsed times per stage into ms[stage] and
+ * counts[stage] (arrays of at least GDN_STAGE_COUNT entries, caller-owned
+ * host memory), then forgets them.  Returns GDN_OK, or GDN_ERR_LAUNCH if the
+ * HIP runtime fails.  Not meant to be toggled while calls are in flight on
+ * other host threads.
+ */
+enum {
+  GDN_STAGE_VARLEN_TABLES = 0, /* varlen chunk tables                         */
+  GDN_STAGE_INTRA = 1,         /* per-chunk (I + A)^-1 and Aqk                 */
+  GDN_STAGE_SCAN = 2,          /* chunk-state scan fused with the output       */
+  GDN_STAGE_DECODE = 3,        /* decode step                                  */
+  GDN_STAGE_COUNT = 4
+};
+int gdn_profile_enable(int on);
+int gdn_profile_read(double* ms, int* counts);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN61_H */

@@ -47,11 +47,13 @@ def decode_normalize(x, eps: float = 1e-6, scale: float = 1.0):
 
 def gdn_decode(q, k, v, a, b, A_log, dt_bias, state, indices=None, scale=None,
                softplus_beta: float = 1.0, softplus_threshold: float = 20.0,
-               use_qk_l2norm: bool = True, eps: float = 1e-6, batches=None):
+               use_qk_l2norm: bool = True, eps: float = 1e-6, batches=None,
+               round_state: bool = True):
     """Return (o [B, T, HV, V] fp64, new_state [pool, HV, V, K] bf16 values as fp64).
 
     ``batches`` restricts the run to some batch rows (others: o = 0, slots
-    unchanged) -- used to sample large problems.
+    unchanged) -- used to sample large problems.  ``round_state=False``
+    returns the updated slots before their bf16 rounding (exact fp64 state).
     """
     q, k, v, state = _f64(q), _f64(k), _f64(v), _f64(state)
     B, T, H, K = q.shape
@@ -82,5 +84,5 @@ def gdn_decode(q, k, v, a, b, A_log, dt_bias, state, indices=None, scale=None,
             delta = beta[bi, t][:, None] * (v[bi, t] - pred)
             S += delta[:, :, None] * kt[:, None, :]
             o[bi, t] = np.einsum("hvk,hk->hv", S, qt)
-        new_state[p] = round_to_bf16(S)
+        new_state[p] = round_to_bf16(S) if round_state else S
     return o, new_state

@@ -1,0 +1,118 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call
+(no GPU is touched by these tests)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_61_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        from gated_delta_rule_61_amd import build
+        build.build()
+    return binding.lib()
+
+
+def declared_functions():
+    names = []
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"gdn_chunk_fwd", "kda_chunk_fwd", "gdn_decode"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared but not exported"
+
+
+def test_version_and_status_strings(L):
+    assert L.gdn_version().startswith(b"gdn61")
+    assert L.gdn_status_string(0) == b"ok"
+    assert L.gdn_status_string(1) == b"invalid argument"
+    assert L.gdn_status_string(99) == b"unknown status"
+
+
+def _chunk(L, **kw):
+    a = dict(q=None, k=None, v=None, g=None, beta=None, scale=1.0, h0=None, ht=None, cu=None, ns=0,
+             B=1, T=64, Hk=2, HV=2, K=64, V=64, cs=64, dt=1, o=None, ws=None, wsb=0, st=None)
+    a.update(kw)
+    return L.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["h0"], a["ht"],
+                           a["cu"], a["ns"], a["B"], a["T"], a["Hk"], a["HV"], a["K"], a["V"], a["cs"],
+                           a["dt"], a["o"], a["ws"], a["wsb"], a["st"])
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced (checks fail first)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(cs=32), 2, b"chunk_size"),
+    (dict(K=96, V=96), 2, b"head dims"),
+    (dict(Hk=3, HV=4), 1, b"multiple"),
+    (dict(dt=7), 1, b"dtype"),
+    (dict(B=-1), 1, b"sizes"),
+    (dict(B=2, cu=FAKE, ns=3), 1, b"B == 1"),
+    (dict(), 1, b"required"),
+    (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE), 3, b"workspace"),
+    (dict(q=FAKE + 4, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, ws=FAKE, wsb=1 << 40), 1, b"aligned"),
+])
+def test_chunk_fwd_rejects(L, kw, status, msg):
+    assert _chunk(L, **kw) == status
+    assert msg in L.gdn_last_error()
+
+
+def test_kda_requires_gate(L):
+    r = L.kda_chunk_fwd(FAKE, FAKE, FAKE, None, FAKE, 1.0, None, None, None, 0, 1, 64, 1, 1, 64, 64, 64, 1,
+                        FAKE, None, None, FAKE, 1 << 40, None)
+    assert r == 1 and b"gk" in L.gdn_last_error()
+
+
+def _dec(L, **kw):
+    a = dict(ptr=FAKE, idx=None, B=2, T=1, H=1, HV=2, K=128, V=128, pool=2, sb=1.0, thr=20.0, eps=1e-6)
+    a.update(kw)
+    p = a["ptr"]
+    return L.gdn_decode(p, p, p, p, p, p, p, p, a["idx"], p, a["B"], a["T"], a["H"], a["HV"], a["K"],
+                        a["V"], a["pool"], 1.0, a["sb"], a["thr"], 1, a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(T=0), 1, b"T = 1..4"),
+    (dict(T=5), 1, b"T = 1..4"),
+    (dict(K=64, V=64), 2, b"K = V = 128"),
+    (dict(H=3, HV=4), 1, b"multiple"),
+    (dict(pool=1), 1, b"pool >= B"),
+    (dict(sb=0.0), 1, b"softplus_beta"),
+    (dict(ptr=None), 1, b"required"),
+    (dict(ptr=FAKE + 2), 1, b"aligned"),
+])
+def test_decode_rejects(L, kw, status, msg):
+    assert _dec(L, **kw) == status
+    assert msg in L.gdn_last_error()
+
+
+def test_workspace_query(L):
+    n = L.gdn_chunk_fwd_workspace_bytes(4, 4096, 16, 16, 128, 128, 4, 1)
+    assert n >= 2 * 4 * 4096 * 16 * 64 * 2
+    assert n % 256 == 0
+    assert L.gdn_chunk_fwd_workspace_bytes(1, 64, 1, 1, 64, 64, 1, 9) == 0
+    assert L.kda_chunk_fwd_workspace_bytes(1, 64, 1, 1, 64, 64, 1, 1) > 0
+
+
+def test_binding_raises_without_cuda_tensors():
+    import torch
+    q = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        binding.gdn_chunk_fwd(q, q, q, None, torch.zeros(1, 4, 1))

@@ -1,0 +1,101 @@
+"""GPU parity of the decode kernel against the fp64 oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_61_amd import binding, workloads
+from tests.tolerance import check, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _run(inp, batches=None, use_norm=True):
+    d = {n: getattr(inp, n) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
+    g = {n: t.to(DEV) for n, t in d.items()}
+    state = inp.state.to(DEV).clone()
+    idx = None if inp.indices is None else inp.indices.to(DEV)
+    o = binding.gdn_decode(g["q"], g["k"], g["v"], g["a"], g["b"], g["A_log"], g["dt_bias"], state,
+                           idx, scale=inp.scale, use_qk_l2norm=use_norm)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.gdn_decode(inp.q, inp.k, inp.v, inp.a, inp.b, inp.A_log, inp.dt_bias,
+                                     inp.state, indices=inp.indices, scale=inp.scale,
+                                     use_qk_l2norm=use_norm, batches=batches, round_state=False)
+    return o.cpu(), state.cpu(), o_ref, s_ref
+
+
+def _ulp_consistent(s_gpu, s_exact):
+    """The GPU's bf16 state is within one bf16 ulp of the oracle's state
+    rounded to bf16 (the two roundings may straddle a rounding boundary),
+    up to a floor of 1e-4 RMS for entries near zero, where the fp32
+    arithmetic error exceeds their tiny ulp."""
+    r = oracle.round_to_bf16(s_exact)
+    g = to64(s_gpu)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - 7)
+    floor = 1e-4 * np.sqrt(np.mean(r * r))
+    assert np.all(np.abs(g - r) <= ulp + floor), "state differs from the rounded oracle state by more than one ulp"
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_decode_small(T):
+    print(f"decode small T={T}", flush=True)
+    inp = workloads.make_decode(3, T, 2, 4, 128, 128, seed=50 + T)
+    o, s, o_ref, s_ref = _run(inp)
+    check("o", o, o_ref, torch.bfloat16)
+    check("state", s, s_ref, torch.bfloat16)
+    _ulp_consistent(s, s_ref)
+
+
+def test_decode_no_norm():
+    inp = workloads.make_decode(2, 2, 1, 2, 128, 128, seed=61)
+    inp.q = (inp.q.float() * 0.1).to(torch.bfloat16)
+    inp.k = (inp.k.float() * 0.1).to(torch.bfloat16)
+    o, s, o_ref, s_ref = _run(inp, use_norm=False)
+    check("o", o, o_ref, torch.bfloat16)
+    check("state", s, s_ref, torch.bfloat16)
+
+
+def test_decode_pool_indices_and_invalid_slot():
+    print("decode pool", flush=True)
+    inp = workloads.make_decode(4, 2, 2, 4, 128, 128, seed=62, pool=9, indices=[7, 0, 4, 2])
+    o, s, o_ref, s_ref = _run(inp)
+    check("o", o, o_ref, torch.bfloat16)
+    check("state", s, s_ref, torch.bfloat16)
+    untouched = [1, 3, 5, 6, 8]
+    assert torch.equal(s[untouched], inp.state[untouched])
+    # an out-of-range slot: o = 0, pool untouched
+    bad = workloads.make_decode(2, 1, 2, 4, 128, 128, seed=63, pool=3, indices=[1, 3])
+    state = bad.state.to(DEV).clone()
+    o = binding.gdn_decode(bad.q.to(DEV), bad.k.to(DEV), bad.v.to(DEV), bad.a.to(DEV), bad.b.to(DEV),
+                           bad.A_log.to(DEV), bad.dt_bias.to(DEV), state, bad.indices.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.all(o[1].float() == 0)
+    st = state.cpu()
+    assert torch.equal(st[0], bad.state[0]) and torch.equal(st[2], bad.state[2])
+    assert not torch.equal(st[1], bad.state[1])
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_b256_sampled(T):
+    """The full B=256, HV=32 workload; the oracle checks 12 sampled rows."""
+    print(f"decode B256 T={T}", flush=True)
+    inp = workloads.decode_b256(T)
+    rows = sorted(np.random.default_rng(T).choice(256, 12, replace=False).tolist())
+    o, s, o_ref, s_ref = _run(inp, batches=rows)
+    check("o", o[rows], o_ref[rows], torch.bfloat16)
+    check("state", s[rows], s_ref[rows], torch.bfloat16)
+    _ulp_consistent(s[rows], s_ref[rows])
+    # every row's state was rewritten (alpha < 1 almost surely changes the bits)
+    assert not torch.equal(s[200], inp.state[200])
+
+
+def test_decode_empty_batch():
+    inp = workloads.make_decode(1, 1, 2, 4, 128, 128, seed=64)
+    state = inp.state.to(DEV)
+    z = lambda t: t[:0].to(DEV)
+    o = binding.gdn_decode(z(inp.q), z(inp.k), z(inp.v), z(inp.a), z(inp.b), inp.A_log.to(DEV),
+                           inp.dt_bias.to(DEV), state)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0
