@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=8192)
     p.add_argument("--skip-extra", action="store_true", help="prefill workload only")
+    p.add_argument("--only", choices=["prefill", "decode", "kda"], default=None,
+                   help="run one workload (for profiling) and print its figures")
+    p.add_argument("--no-cold", action="store_true", help="skip the cold-cache prefill timing")
     return p.parse_args()
 
 
@@ -98,9 +101,9 @@ def bench_prefill(args, binding, workloads, torch):
     prof = binding.profile_read()
     binding.profile_enable(False)
     # cold-cache variant: 1 GiB scratch written between calls, only the call timed
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cold = []
-    for _ in range(min(args.steps, 10)):
+    scratch = None if args.no_cold else torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for _ in range(0 if args.no_cold else min(args.steps, 10)):
         scratch.fill_(1.0)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -112,7 +115,7 @@ def bench_prefill(args, binding, workloads, torch):
     del scratch
     tokens = B * T
     return dict(inp=inp, ms=ms, wall=wall, prof=prof, tokens=tokens, HV=HV, K=K, V=V,
-                cold_ms=sorted(cold)[len(cold) // 2])
+                cold_ms=sorted(cold)[len(cold) // 2] if cold else None)
 
 
 def bench_decode(args, binding, workloads, torch, T):
@@ -197,6 +200,13 @@ def main():
     binding.lib()
     assert torch.cuda.is_available(), "needs a GPU"
 
+    if args.only == "decode":
+        print(json.dumps({"decode": {"T1": bench_decode(args, binding, workloads, torch, 1),
+                                     "T4": bench_decode(args, binding, workloads, torch, 4)}}), flush=True)
+        return
+    if args.only == "kda":
+        print(json.dumps({"kda": bench_kda(args, binding, workloads, torch)}), flush=True)
+        return
     pf = bench_prefill(args, binding, workloads, torch)
     ms = pf["ms"]
     tokens = pf["tokens"]
@@ -223,20 +233,20 @@ def main():
         "config": {"workload": "gdn_chunk_fwd B=4 T=4096 H=16 K=V=128 BT=64, bf16 q/k/v, fp32 g/beta/state, zero h0, ht stored",
                    "global_batch": 4, "seq_len": 4096},
         "mfma_frac_method_flops": round(method / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "cold_ms_per_step": round(pf["cold_ms"], 5),
+        "cold_ms_per_step": None if pf["cold_ms"] is None else round(pf["cold_ms"], 5),
         "kernels_ms": {s: round(v, 5) for s, v in stage_ms.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
     }
-    if not args.skip_extra:
+    if not args.skip_extra and args.only is None:
         out["decode"] = {"T1": bench_decode(args, binding, workloads, torch, 1),
                          "T4": bench_decode(args, binding, workloads, torch, 4)}
         try:
             out["kda"] = bench_kda(args, binding, workloads, torch)
         except Exception as e:  # KDA path reports its own status
             out["kda"] = {"error": f"{type(e).__name__}: {e}"}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.only is None:
         out["cpu_baseline"] = cpu_baseline(args, workloads)
     print(json.dumps(out), flush=True)
 

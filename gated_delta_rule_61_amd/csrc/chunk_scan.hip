@@ -15,21 +15,28 @@
 // u never reach memory ("fla ops/common/chunk_h.py", chunk_fwd_kernel_h:
 // sequential chunk loop with an fp32 state, h *= exp(g_last), v scaled by
 // exp(g_last - g); "sglang srt/layers/attention/fla/chunk_fwd.py", the
-// intra-chunk A consumed by recompute_w_u).  For KDA every scalar e^G becomes
-// a per-channel factor inside the contractions (see the KDA variant).
+// intra-chunk A consumed by recompute_w_u).
 //
-// gfx950 design: 4 waves (256 threads) per work-group.
-//   * S^T stays in MFMA accumulators: wave w owns key rows
-//     [w*DK/4, (w+1)*DK/4) x BV columns; a bf16 copy lives in LDS as the B
-//     operand of the next chunk's K S^T and Q S^T;
+// gfx950 design: 4 waves (256 threads) per work-group, BV = 16 columns.
+//   * S^T stays in fp32 MFMA accumulators: wave w owns key rows
+//     [w*DK/4, (w+1)*DK/4); LDS holds S as the B operand of the next chunk's
+//     K S^T and Q S^T;
+//   * the products with the inputs (K S^T, Q S^T, K^T Vn) run in bf16 on the
+//     raw q / k, which are exact in bf16; their computed operands S and
+//     diag(e^{G_last-G}) Vn are split into bf16 hi + lo (two MFMAs, ~16
+//     significant bits) instead of converting every input element;
+//   * the small 64 x 64 products (Ainv R, Aqk Vn) run in fp16 (Ainv and Aqk
+//     are bounded by construction);
 //   * wave w owns tokens 16w..16w+15 of X, O, R, Vn; its q / k / Ainv / Aqk
-//     fragments are prefetched from HBM one chunk ahead into registers;
+//     fragments, v, and gate factors are prefetched one chunk ahead into one
+//     of two register sets used in turn (no copies);
 //   * the key chunk is written to LDS transposed (token-contiguous per key
 //     channel) by all 256 threads, as the A operand of K^T Vn;
 //   * three block barriers per chunk, no global round trip of any
 //     intermediate;
 //   * work-groups of one (sequence, head) share an XCD (its L2), and
 //     sequences are issued longest first.
+// fp32 io runs the same schedule with fp32 operands everywhere.
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -51,13 +58,21 @@ __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d) {
   }
 }
 
-__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
+// Store 4 consecutive values as bf16 hi and lo parts (x ~= hi + lo, about 16
+// significant bits); for fp32 the value goes to `ph` unchanged.
+template <typename T>
+__device__ __forceinline__ void st4_split(T* ph, T* pl, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t h0 = pack_bf2(a, b), h1 = pack_bf2(c, d);
+    *reinterpret_cast<uint2*>(ph) = make_uint2(h0, h1);
+    const float la = a - __builtin_bit_cast(float, h0 << 16);
+    const float lb = b - __builtin_bit_cast(float, h0 & 0xFFFF0000u);
+    const float lc = c - __builtin_bit_cast(float, h1 << 16);
+    const float ld = d - __builtin_bit_cast(float, h1 & 0xFFFF0000u);
+    *reinterpret_cast<uint2*>(pl) = make_uint2(pack_bf2(la, lb), pack_bf2(lc, ld));
+  } else {
+    *reinterpret_cast<float4*>(ph) = make_float4(a, b, c, d);
   }
-  return x;
 }
 
 // raw 8-element row segment of the io type
@@ -66,9 +81,8 @@ template <> struct Seg8<bf16_t> {
   uint4 v;
   __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
   __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
-  __device__ __forceinline__ bf16_t get(int e) const {
-    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
-    return (bf16_t)((e & 1) ? (w >> 16) : (w & 0xFFFF));
+  __device__ __forceinline__ uint32_t word(int e) const {
+    return e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
   }
 };
 template <> struct Seg8<float> {
@@ -84,62 +98,98 @@ template <> struct Seg8<float> {
   }
 };
 
-// Write TPT consecutive tokens of one key channel into the transposed tile
-// (element type C).
-template <typename C, int TPT>
-__device__ __forceinline__ void put_tokens(C* dst, const float (&vals)[TPT]) {
+// Channel e of TPT consecutive tokens -> TPT consecutive elements of the
+// transposed tile row (pure bit moves for bf16).
+template <int TPT>
+__device__ __forceinline__ void put_channel(bf16_t* dst, const Seg8<bf16_t> (&src)[TPT], int e) {
+  auto pair = [&](int a, int b) -> uint32_t {
+    const uint32_t x = src[a].word(e), y = src[b].word(e);
+    return (e & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+  };
   if constexpr (TPT == 4) {
-    st4<C>(dst, vals[0], vals[1], vals[2], vals[3]);
-  } else if constexpr (sizeof(C) == 2 && TPT == 2) {
-    *reinterpret_cast<uint32_t*>(dst) = pack2<C>(vals[0], vals[1]);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pair(0, 1), pair(2, 3));
   } else {
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) dst[u] = from_f<C>(vals[u]);
+    *reinterpret_cast<uint32_t*>(dst) = pair(0, 1);
+  }
+}
+template <int TPT>
+__device__ __forceinline__ void put_channel(float* dst, const Seg8<float> (&src)[TPT], int e) {
+  if constexpr (TPT == 4) {
+    *reinterpret_cast<float4*>(dst) = make_float4(src[0].get(e), src[1].get(e), src[2].get(e), src[3].get(e));
+  } else {
+    *reinterpret_cast<float2*>(dst) = make_float2(src[0].get(e), src[1].get(e));
   }
 }
 
-template <typename T, int DK, int BV, typename C = typename ComputeOf<T>::type>
+template <typename T, int DK, int BV, typename P = typename ComputeOf<T>::type>
 struct ScanRegs {
   static constexpr int KS = DK / 32;        // channel slabs
   static constexpr int CB = BV / 16;        // 16-column blocks of the tile
   static constexpr int CG = DK / 8;         // 8-channel groups (loader)
   static constexpr int TG = 256 / CG;       // token groups (loader)
   static constexpr int TPT = BT / TG;       // tokens per loader thread
-  Frag<T> kA[KS], qA[KS];                   // rows 16w + row of k, q
-  Frag<C> ai[2], aq[2];                     // rows 16w + row of Ainv, Aqk (compute type)
+  Frag<T> kA[KS], qA[KS];                   // rows 16w + row of k, q (raw)
+  Frag<P> ai[2], aq[2];                     // rows 16w + row of Ainv, Aqk
   T vv[CB][4];                              // v[16w + 4grp + i][v0 + 16cb + row], raw
-                                            // (converted at use so the prefetch never waits)
   Seg8<T> kt[TPT];                          // loader: tokens TPT*tg + u, channels 8cg..
-  float gl, bl;                             // g, beta of token `lane`
+                                            // (tg = tid % TG, cg = tid / TG)
+  float4 gf[4];                             // gate factors of rows 16w + 4grp + i
+  float eGl;                                // e^{G_last} of the chunk (uniform)
 };
 
-template <typename T, int DK, int BV, typename C>
-__device__ __forceinline__ void load_chunk(ScanRegs<T, DK, BV>& R, const T* __restrict__ q,
-                                           const T* __restrict__ k, const T* __restrict__ v,
-                                           const float* __restrict__ g,
-                                           const float* __restrict__ beta,
-                                           const C* __restrict__ Ainv, const C* __restrict__ Aqk,
-                                           int c0, int nrow, int Hk, int HV, int V, int jk,
-                                           int j, int v0, int w, int lane, int tid) {
-  typedef ScanRegs<T, DK, BV> RT;
-  const int row = lane & 15, grp = lane >> 4;
-  const int r = 16 * w + row;
-  if (r < nrow) {
-    const size_t qk = ((size_t)(c0 + r) * Hk + jk) * DK + 8 * grp;
+// Streams the scan reads: work-group-uniform base pointers at the current
+// chunk (advanced by scalar adds) plus constant per-lane 32-bit offsets, so
+// every load is a saddr + voffset access with no per-chunk address VALU.
+template <typename T, typename P>
+struct ScanStreams {
+  const T *q, *k, *v;
+  const P *ai, *aq;
+  const float4* gf;
+  uint32_t oA, oAi, oV[4], oG[4], oK[4];  // element offsets within the chunk
+};
+
+// Issue the loads of one chunk.  Full chunks take the unpredicated path; the
+// tail chunk of a sequence (nrow < 64) zero-fills rows past its end.  Raw
+// values only: nothing here waits on a load.
+template <typename T, int DK, int BV, typename P>
+__device__ __forceinline__ void load_chunk(ScanRegs<T, DK, BV, P>& R, const ScanStreams<T, P>& S,
+                                           int nrow, int w, int lane, int tid) {
+  typedef ScanRegs<T, DK, BV, P> RT;
+  R.eGl = S.gf[0].w;  // row 0 of the chunk is always valid
+  if (nrow == BT) {
 #pragma unroll
     for (int s = 0; s < RT::KS; ++s) {
-      load8(R.kA[s], k + qk + 32 * s);
-      load8(R.qA[s], q + qk + 32 * s);
+      load8(R.kA[s], S.k + S.oA + 32 * s);
+      load8(R.qA[s], S.q + S.oA + 32 * s);
     }
-    const size_t ao = ((size_t)(c0 + r) * HV + j) * BT + 8 * grp;
-    load8(R.ai[0], Ainv + ao);
-    load8(R.aq[0], Aqk + ao);
+    load8(R.ai[0], S.ai + S.oAi);
+    load8(R.aq[0], S.aq + S.oAi);
     if (w >= 2) {
-      load8(R.ai[1], Ainv + ao + 32);
-      load8(R.aq[1], Aqk + ao + 32);
-    } else {
-      R.ai[1].zero();
-      R.aq[1].zero();
+      load8(R.ai[1], S.ai + S.oAi + 32);
+      load8(R.aq[1], S.aq + S.oAi + 32);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int cb = 0; cb < RT::CB; ++cb) R.vv[cb][i] = S.v[S.oV[i] + 16 * cb];
+      R.gf[i] = S.gf[S.oG[i]];
+    }
+#pragma unroll
+    for (int u = 0; u < RT::TPT; ++u) R.kt[u].load(S.k + S.oK[u]);
+    return;
+  }
+  const int row = lane & 15, grp = lane >> 4;
+  if (16 * w + row < nrow) {
+#pragma unroll
+    for (int s = 0; s < RT::KS; ++s) {
+      load8(R.kA[s], S.k + S.oA + 32 * s);
+      load8(R.qA[s], S.q + S.oA + 32 * s);
+    }
+    load8(R.ai[0], S.ai + S.oAi);
+    load8(R.aq[0], S.aq + S.oAi);
+    if (w >= 2) {
+      load8(R.ai[1], S.ai + S.oAi + 32);
+      load8(R.aq[1], S.aq + S.oAi + 32);
     }
   } else {
 #pragma unroll
@@ -147,42 +197,44 @@ __device__ __forceinline__ void load_chunk(ScanRegs<T, DK, BV>& R, const T* __re
     R.ai[0].zero(); R.aq[0].zero(); R.ai[1].zero(); R.aq[1].zero();
   }
 #pragma unroll
-  for (int cb = 0; cb < RT::CB; ++cb)
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = 16 * w + 4 * grp + i < nrow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * w + 4 * grp + i;
-      R.vv[cb][i] = rr < nrow ? v[((size_t)(c0 + rr) * HV + j) * V + v0 + 16 * cb + row] : T(0);
-    }
-  const int tg = tid / RT::CG, cg = tid % RT::CG;
+    for (int cb = 0; cb < RT::CB; ++cb) R.vv[cb][i] = ok ? S.v[S.oV[i] + 16 * cb] : T(0);
+    R.gf[i] = ok ? S.gf[S.oG[i]] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int tg = tid % RT::TG;
 #pragma unroll
   for (int u = 0; u < RT::TPT; ++u) {
-    const int tok = RT::TPT * tg + u;
-    if (tok < nrow) R.kt[u].load(k + ((size_t)(c0 + tok) * Hk + jk) * DK + 8 * cg);
+    if (RT::TPT * tg + u < nrow) R.kt[u].load(S.k + S.oK[u]);
     else R.kt[u].zero();
   }
-  R.gl = (g && lane < nrow) ? g[(size_t)(c0 + lane) * HV + j] : 0.f;
-  R.bl = lane < nrow ? beta[(size_t)(c0 + lane) * HV + j] : 0.f;
 }
 
-template <typename T, int DK, int BV, typename C = typename ComputeOf<T>::type>
+template <typename T, int DK, int BV, typename P = typename ComputeOf<T>::type>
 __global__ __launch_bounds__(256) void gdn_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, float scale,
-    const float* __restrict__ h0, float* __restrict__ ht, const C* __restrict__ Ainv,
-    const C* __restrict__ Aqk, T* __restrict__ o, const int64_t* __restrict__ cu,
+    const float4* __restrict__ GF, float scale,
+    const float* __restrict__ h0, float* __restrict__ ht, const P* __restrict__ Ainv,
+    const P* __restrict__ Aqk, T* __restrict__ o, const int64_t* __restrict__ cu,
     const int32_t* __restrict__ order, int Tlen, int N, int Hk, int HV, int V) {
-  typedef ScanRegs<T, DK, BV> RT;
+  typedef ScanRegs<T, DK, BV, P> RT;
+  constexpr bool SPLIT = sizeof(T) == 2;  // bf16 io: hi + lo parts of computed operands
   constexpr int KS = RT::KS, CB = RT::CB;
-  constexpr int WR = DK / 4;        // state rows (key channels) per wave
-  constexpr int RB = WR / 16;       // 16-row blocks per wave
-  constexpr int KP = DK + 8;        // padded key row of the state copy
-  __shared__ __attribute__((aligned(16))) C sKt[DK][TP];         // K^T of the chunk (token-contiguous)
-  __shared__ __attribute__((aligned(16))) C sS[BV][KP];          // S (value rows, key-contiguous), io type
-  __shared__ __attribute__((aligned(16))) C sR[BV][TP];          // R^T
-  __shared__ __attribute__((aligned(16))) C sVn[BV][TP];         // Vn^T
-  __shared__ __attribute__((aligned(16))) C sVt[BV][TP];         // (diag(e^{G_last - G}) Vn)^T
+  constexpr int WR = DK / 4;              // state rows (key channels) per wave
+  constexpr int RB = WR / 16;             // 16-row blocks per wave
+  constexpr int KP = DK + 8;              // padded key row of the state copy
+  constexpr int NL = SPLIT ? BV : 1;      // rows of the lo-part tiles
+  __shared__ __attribute__((aligned(16))) T sKt[DK][TP];   // K^T of the chunk (raw, token-contiguous)
+  __shared__ __attribute__((aligned(16))) T sSh[BV][KP];   // S (value rows, key-contiguous), hi part
+  __shared__ __attribute__((aligned(16))) T sSl[NL][KP];   //   lo part
+  __shared__ __attribute__((aligned(16))) P sR[BV][TP];    // R^T
+  __shared__ __attribute__((aligned(16))) P sVn[BV][TP];   // Vn^T
+  __shared__ __attribute__((aligned(16))) T sVth[BV][TP];  // (diag(e^{G_last - G}) Vn)^T, hi part
+  __shared__ __attribute__((aligned(16))) T sVtl[NL][TP];  //   lo part
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int row = lane & 15, grp = lane >> 4;
   const int NVT = V / BV;
 
@@ -224,49 +276,51 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
       } else {
         St[rb][cb] = zero4();
       }
-      st4<C>(&sS[16 * cb + row][WR * w + 16 * rb + 4 * grp], St[rb][cb][0], St[rb][cb][1],
-             St[rb][cb][2], St[rb][cb][3]);
+      const int c = WR * w + 16 * rb + 4 * grp;
+      st4_split<T>(&sSh[16 * cb + row][c], &sSl[SPLIT ? 16 * cb + row : 0][c], St[rb][cb][0],
+                   St[rb][cb][1], St[rb][cb][2], St[rb][cb][3]);
     }
+
+  // ---- streams: uniform bases at chunk 0, per-lane offsets, per-chunk strides
+  const uint32_t sQK = (uint32_t)Hk * DK, sA = (uint32_t)HV * BT, sV = (uint32_t)HV * V, sG = (uint32_t)HV;
+  // loader: token group varies fastest across lanes, so the transposed
+  // K^T writes of a half-wave cover one contiguous 128-byte row segment
+  const int tg = tid % RT::TG, cg = tid / RT::TG;
+  ScanStreams<T, P> St_;
+  St_.q = q + (size_t)bos * sQK + (size_t)jk * DK;
+  St_.k = k + (size_t)bos * sQK + (size_t)jk * DK;
+  St_.ai = Ainv + (size_t)bos * sA + (size_t)j * BT;
+  St_.aq = Aqk + (size_t)bos * sA + (size_t)j * BT;
+  St_.v = v + (size_t)bos * sV + (size_t)j * V + v0;
+  St_.gf = GF + (size_t)bos * sG + j;
+  St_.oA = (uint32_t)(16 * w + row) * sQK + 8 * grp;
+  St_.oAi = (uint32_t)(16 * w + row) * sA + 8 * grp;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    St_.oV[i] = (uint32_t)(16 * w + 4 * grp + i) * sV + row;
+    St_.oG[i] = (uint32_t)(16 * w + 4 * grp + i) * sG;
+    St_.oK[i] = (uint32_t)(RT::TPT * tg + (i < RT::TPT ? i : 0)) * sQK + 8 * cg;
+  }
+  const size_t cQK = (size_t)BT * sQK, cA = (size_t)BT * sA, cV = (size_t)BT * sV, cG = (size_t)BT * sG;
 
   const int NC = (eos - bos + BT - 1) / BT;
-  RT nx;
-  if (NC > 0)
-    load_chunk<T, DK, BV>(nx, q, k, v, g, beta, Ainv, Aqk, bos, eos - bos < BT ? eos - bos : BT,
-                          Hk, HV, V, jk, j, v0, w, lane, tid);
 
-  for (int ic = 0; ic < NC; ++ic) {
+  // One chunk: compute from `cur`, prefetch the next chunk into `nxt`.
+  auto step = [&](RT& cur, RT& nxt, int ic) {
     const int c0 = bos + ic * BT;
     const int nrow = eos - c0 < BT ? eos - c0 : BT;
-    RT cur = nx;
+    // K^T into LDS from the loader registers
+#pragma unroll
+    for (int e = 0; e < 8; ++e) put_channel<RT::TPT>(&sKt[8 * cg + e][RT::TPT * tg], cur.kt, e);
     if (ic + 1 < NC) {
+      St_.q += cQK; St_.k += cQK; St_.ai += cA; St_.aq += cA; St_.v += cV; St_.gf += cG;
       const int c1 = c0 + BT;
-      load_chunk<T, DK, BV>(nx, q, k, v, g, beta, Ainv, Aqk, c1, eos - c1 < BT ? eos - c1 : BT,
-                            Hk, HV, V, jk, j, v0, w, lane, tid);
+      load_chunk<T, DK, BV, P>(nxt, St_, eos - c1 < BT ? eos - c1 : BT, w, lane, tid);
     }
-    // K^T into LDS (token-contiguous per channel)
-    {
-      const int tg = tid / RT::CG, cg = tid % RT::CG;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float vals[RT::TPT];
-#pragma unroll
-        for (int u = 0; u < RT::TPT; ++u) vals[u] = to_f(cur.kt[u].get(e));
-        put_tokens<C, RT::TPT>(&sKt[8 * cg + e][RT::TPT * tg], vals);
-      }
-    }
-    // gates: lane = token
-    const float G = wave_incl_scan(cur.gl, lane);
-    const float Gl = __shfl(G, nrow - 1, 64);
     float eG[4], eGt[4], br[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * w + 4 * grp + i;
-      const float Gr = __shfl(G, rr, 64);
-      eG[i] = __expf(Gr);
-      eGt[i] = __expf(Gl - Gr);
-      br[i] = __shfl(cur.bl, rr, 64);
-    }
-    const float eGl = __expf(Gl);
+    for (int i = 0; i < 4; ++i) { eG[i] = cur.gf[i].x; eGt[i] = cur.gf[i].y; br[i] = cur.gf[i].z; }
+    const float eGl = cur.eGl;
 
     // ---- steps 1-2: X = K S^T, Oi = Q S^T (rows 16w.., all BV columns)
     f32x4 X[CB], Oi[CB];
@@ -274,13 +328,17 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
     for (int cb = 0; cb < CB; ++cb) { X[cb] = zero4(); Oi[cb] = zero4(); }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const Frag<C> kc = conv<C>(cur.kA[s]), qc = conv<C>(cur.qA[s]);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        Frag<C> sf;
-        load8(sf, &sS[16 * cb + row][32 * s + 8 * grp]);
-        X[cb] = mma(kc, sf, X[cb]);
-        Oi[cb] = mma(qc, sf, Oi[cb]);
+        Frag<T> sf;
+        load8(sf, &sSh[16 * cb + row][32 * s + 8 * grp]);
+        X[cb] = mma(cur.kA[s], sf, X[cb]);
+        Oi[cb] = mma(cur.qA[s], sf, Oi[cb]);
+        if constexpr (SPLIT) {
+          load8(sf, &sSl[16 * cb + row][32 * s + 8 * grp]);
+          X[cb] = mma(cur.kA[s], sf, X[cb]);
+          Oi[cb] = mma(cur.qA[s], sf, Oi[cb]);
+        }
       }
     }
     // ---- step 3: R = beta (v - e^G X) -> LDS (transposed)
@@ -289,7 +347,7 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
       float rv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) rv[i] = br[i] * (to_f(cur.vv[cb][i]) - eG[i] * X[cb][i]);
-      st4<C>(&sR[16 * cb + row][16 * w + 4 * grp], rv[0], rv[1], rv[2], rv[3]);
+      st4<P>(&sR[16 * cb + row][16 * w + 4 * grp], rv[0], rv[1], rv[2], rv[3]);
     }
     __syncthreads();
 
@@ -297,16 +355,16 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
     f32x4 Vn[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      Frag<C> rf;
+      Frag<P> rf;
       load8(rf, &sR[16 * cb + row][8 * grp]);
       Vn[cb] = mma(cur.ai[0], rf, zero4());
       if (w >= 2) {
         load8(rf, &sR[16 * cb + row][32 + 8 * grp]);
         Vn[cb] = mma(cur.ai[1], rf, Vn[cb]);
       }
-      st4<C>(&sVn[16 * cb + row][16 * w + 4 * grp], Vn[cb][0], Vn[cb][1], Vn[cb][2], Vn[cb][3]);
-      st4<C>(&sVt[16 * cb + row][16 * w + 4 * grp], Vn[cb][0] * eGt[0], Vn[cb][1] * eGt[1],
-             Vn[cb][2] * eGt[2], Vn[cb][3] * eGt[3]);
+      st4<P>(&sVn[16 * cb + row][16 * w + 4 * grp], Vn[cb][0], Vn[cb][1], Vn[cb][2], Vn[cb][3]);
+      st4_split<T>(&sVth[16 * cb + row][16 * w + 4 * grp], &sVtl[SPLIT ? 16 * cb + row : 0][16 * w + 4 * grp],
+                   Vn[cb][0] * eGt[0], Vn[cb][1] * eGt[1], Vn[cb][2] * eGt[2], Vn[cb][3] * eGt[3]);
     }
     __syncthreads();
 
@@ -316,7 +374,7 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
       f32x4 acc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = Oi[cb][i] * (scale * eG[i]);
-      Frag<C> vf;
+      Frag<P> vf;
       load8(vf, &sVn[16 * cb + row][8 * grp]);
       acc = mma(cur.aq[0], vf, acc);
       if (w >= 2) {
@@ -337,38 +395,51 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
         f32x4 acc = St[rb][cb] * eGl;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          Frag<C> af, bfr;
+          Frag<T> af, bfr;
           load8(af, &sKt[WR * w + 16 * rb + row][32 * s + 8 * grp]);
-          load8(bfr, &sVt[16 * cb + row][32 * s + 8 * grp]);
+          load8(bfr, &sVth[16 * cb + row][32 * s + 8 * grp]);
           acc = mma(af, bfr, acc);
+          if constexpr (SPLIT) {
+            load8(bfr, &sVtl[16 * cb + row][32 * s + 8 * grp]);
+            acc = mma(af, bfr, acc);
+          }
         }
         St[rb][cb] = acc;
-        st4<C>(&sS[16 * cb + row][WR * w + 16 * rb + 4 * grp], acc[0], acc[1], acc[2], acc[3]);
+        const int c = WR * w + 16 * rb + 4 * grp;
+        st4_split<T>(&sSh[16 * cb + row][c], &sSl[SPLIT ? 16 * cb + row : 0][c], acc[0], acc[1],
+                     acc[2], acc[3]);
       }
     __syncthreads();
+  };
+
+  RT ra, rb;
+  if (NC > 0) load_chunk<T, DK, BV, P>(ra, St_, eos - bos < BT ? eos - bos : BT, w, lane, tid);
+  for (int ic = 0; ic < NC; ic += 2) {
+    step(ra, rb, ic);
+    if (ic + 1 < NC) step(rb, ra, ic + 1);
   }
 
   if (ht) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int rb2 = 0; rb2 < RB; ++rb2)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
-        *reinterpret_cast<float4*>(ht + hbase + (size_t)(v0 + 16 * cb + row) * DK + WR * w + 16 * rb +
+        *reinterpret_cast<float4*>(ht + hbase + (size_t)(v0 + 16 * cb + row) * DK + WR * w + 16 * rb2 +
                                    4 * grp) =
-            make_float4(St[rb][cb][0], St[rb][cb][1], St[rb][cb][2], St[rb][cb][3]);
+            make_float4(St[rb2][cb][0], St[rb2][cb][1], St[rb2][cb][2], St[rb2][cb][3]);
   }
 }
 
 template <typename T, int DK, int BV>
 hipError_t launch_scan_t(const ChunkArgs& a, hipStream_t s) {
-  typedef typename ComputeOf<T>::type C;
+  typedef typename ComputeOf<T>::type P;
   const int nvt = a.V / BV;
   const int groups = a.N * a.HV;
   const int nblk = ((groups + 7) / 8) * 8 * nvt;
   hipLaunchKernelGGL((gdn_scan_kernel<T, DK, BV>), dim3((unsigned)nblk), dim3(256), 0, s,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta, a.scale, a.h0, a.ht,
-                     (const C*)a.Ainv, (const C*)a.Aqk, (T*)a.o, a.cu_seqlens, a.seq_order, a.T,
-                     a.N, a.Hk, a.HV, a.V);
+                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float4*)a.GF, a.scale,
+                     a.h0, a.ht, (const P*)a.Ainv, (const P*)a.Aqk, (T*)a.o, a.cu_seqlens,
+                     a.seq_order, a.T, a.N, a.Hk, a.HV, a.V);
   return hipGetLastError();
 }
 
@@ -376,11 +447,11 @@ hipError_t launch_scan_t(const ChunkArgs& a, hipStream_t s) {
 
 hipError_t launch_scan_gdn(const ChunkArgs& a, hipStream_t s) {
   if (a.bf16) {
-    if (a.K == 128) return launch_scan_t<bf16_t, 128, 32>(a, s);
-    return launch_scan_t<bf16_t, 64, 32>(a, s);
+    if (a.K == 128) return launch_scan_t<bf16_t, 128, 16>(a, s);
+    return launch_scan_t<bf16_t, 64, 16>(a, s);
   }
-  if (a.K == 128) return launch_scan_t<float, 128, 32>(a, s);
-  return launch_scan_t<float, 64, 32>(a, s);
+  if (a.K == 128) return launch_scan_t<float, 128, 16>(a, s);
+  return launch_scan_t<float, 64, 16>(a, s);
 }
 
 }  // namespace gdn

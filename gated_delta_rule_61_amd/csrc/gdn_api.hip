@@ -175,7 +175,8 @@ ChunkWorkspace chunk_workspace_layout(long long tokens, int HV, int N, int elem_
   const size_t mat = (size_t)tokens * HV * 64 * elem_bytes;
   w.ainv_off = 0;
   w.aqk_off = up(mat);
-  w.coff_off = w.aqk_off + up(mat);
+  w.gf_off = w.aqk_off + up(mat);
+  w.coff_off = w.gf_off + up((size_t)tokens * HV * 16);
   w.order_off = w.coff_off + up((size_t)(N + 1) * 4);
   w.total = w.order_off + up((size_t)(N > 0 ? N : 1) * 4);
   return w;
@@ -263,6 +264,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   a.o = o;
   a.Ainv = ws + L.ainv_off;
   a.Aqk = ws + L.aqk_off;
+  a.GF = ws + L.gf_off;
   a.chunk_off = cu_seqlens ? (int32_t*)(ws + L.coff_off) : nullptr;
   a.seq_order = cu_seqlens ? (int32_t*)(ws + L.order_off) : nullptr;
   a.max_chunks = (T + 63) / 64 + (cu_seqlens ? P.N : 0);

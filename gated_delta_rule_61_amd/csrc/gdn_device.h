@@ -125,17 +125,19 @@ template <> __device__ __forceinline__ f16_t from_f<f16_t>(float x) {
 }
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 
-// Convert a fragment between element types (identity when equal).
+// Convert a fragment of raw inputs between element types (identity when
+// equal).  bf16 -> fp16 is exact for |x| in fp16's normal range; inputs are
+// not clamped here (q and k are expected far below 65504 in magnitude).
 template <typename C, typename T>
-__device__ __forceinline__ Frag<C> conv(const Frag<T>& a) {
-  if constexpr (__is_same(C, T)) {
-    return a;
-  } else {
-    Frag<C> r;
+__device__ __forceinline__ Frag<C> conv(const Frag<T>& a);
+template <>
+__device__ __forceinline__ Frag<float> conv<float, float>(const Frag<float>& a) { return a; }
+template <>
+__device__ __forceinline__ Frag<f16_t> conv<f16_t, bf16_t>(const Frag<bf16_t>& a) {
+  Frag<f16_t> r;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r.set(e, a.get(e));
-    return r;
-  }
+  for (int e = 0; e < 8; ++e) r.v[e] = (_Float16)(float)a.v[e];
+  return r;
 }
 
 // Compute type of the MFMA operands for an io type: fp16 for bf16 io (one

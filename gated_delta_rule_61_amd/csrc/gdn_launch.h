@@ -36,8 +36,9 @@ struct ChunkArgs {
   int B, T, Hk, HV, K, V;
   int bf16;              // 1 = bf16 io, 0 = fp32 io
   void* o;
-  void* Ainv;            // [B*T, HV, 64] io dtype: (I + A)^-1 rows
-  void* Aqk;             // [B*T, HV, 64] io dtype: scale * gated causal Q K^T rows
+  void* Ainv;            // [B*T, HV, 64] compute dtype: (I + A)^-1 rows
+  void* Aqk;             // [B*T, HV, 64] compute dtype: scale * gated causal Q K^T rows
+  void* GF;              // [B*T, HV] float4: e^G, e^{G_last - G}, beta, e^{G_last}
   int32_t* chunk_off;    // [N + 1] varlen chunk offsets (workspace) or nullptr
   int32_t* seq_order;    // [N] sequences, longest first (workspace) or nullptr
   int max_chunks;        // upper bound of the total chunk count
@@ -46,7 +47,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t s);
 
 // Workspace layout shared by the size query and the launcher.
 struct ChunkWorkspace {
-  size_t ainv_off, aqk_off, coff_off, order_off, total;
+  size_t ainv_off, aqk_off, gf_off, coff_off, order_off, total;
 };
 ChunkWorkspace chunk_workspace_layout(long long BT_tokens, int HV, int N, int elem_bytes);
 
