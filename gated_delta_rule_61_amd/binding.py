@@ -193,8 +193,8 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.T
     ht = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if output_final_state else None
     Aqk = Akk = None
     if return_intra:
-        Aqk = torch.zeros((B, T, HV, chunk_size), dtype=io, device=dev)
-        Akk = torch.zeros((B, T, HV, chunk_size), dtype=io, device=dev)
+        Aqk = torch.empty((B, T, HV, chunk_size), dtype=io, device=dev)
+        Akk = torch.empty((B, T, HV, chunk_size), dtype=io, device=dev)
     nbytes = workspace_bytes(B, T, Hk, HV, K, V, N, io, kda=True)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)

@@ -37,6 +37,14 @@
 //   * work-groups of one (sequence, head) share an XCD (its L2), and
 //     sequences are issued longest first.
 // fp32 io runs the same schedule with fp32 operands everywhere.
+//
+// KDA (one log-gate per key channel) runs the same kernel: every scalar e^G
+// becomes a per-channel factor inside the contractions, so the intra kernel
+// writes the gated operands K o e^G, Q o e^G and K o e^{G_last - G} (fp16,
+// bounded by |k|, |q|) and a per-channel decay e^{G_last}; the scan reads
+// those in place of q / k, skips the per-row gate scaling and decays S^T
+// row by row ("fla ops/common/chunk_h.py", USE_GK: h *= exp(gk_last)[:, None],
+// k *= exp(gk_last - gk)).
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -59,10 +67,10 @@ __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d) {
 }
 
 // Store 4 consecutive values as bf16 hi and lo parts (x ~= hi + lo, about 16
-// significant bits); for fp32 the value goes to `ph` unchanged.
+// significant bits); for fp16 / fp32 operands the value goes to `ph` alone.
 template <typename T>
 __device__ __forceinline__ void st4_split(T* ph, T* pl, float a, float b, float c, float d) {
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (__is_same(T, bf16_t)) {
     const uint32_t h0 = pack_bf2(a, b), h1 = pack_bf2(c, d);
     *reinterpret_cast<uint2*>(ph) = make_uint2(h0, h1);
     const float la = a - __builtin_bit_cast(float, h0 << 16);
@@ -71,7 +79,7 @@ __device__ __forceinline__ void st4_split(T* ph, T* pl, float a, float b, float 
     const float ld = d - __builtin_bit_cast(float, h1 & 0xFFFF0000u);
     *reinterpret_cast<uint2*>(pl) = make_uint2(pack_bf2(la, lb), pack_bf2(lc, ld));
   } else {
-    *reinterpret_cast<float4*>(ph) = make_float4(a, b, c, d);
+    st4<T>(ph, a, b, c, d);
   }
 }
 
@@ -84,6 +92,9 @@ template <> struct Seg8<bf16_t> {
   __device__ __forceinline__ uint32_t word(int e) const {
     return e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
   }
+};
+template <> struct Seg8<f16_t> : Seg8<bf16_t> {
+  __device__ __forceinline__ void load(const f16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
 };
 template <> struct Seg8<float> {
   float4 a, b;
@@ -113,6 +124,18 @@ __device__ __forceinline__ void put_channel(bf16_t* dst, const Seg8<bf16_t> (&sr
   }
 }
 template <int TPT>
+__device__ __forceinline__ void put_channel(f16_t* dst, const Seg8<f16_t> (&src)[TPT], int e) {
+  auto pair = [&](int a, int b) -> uint32_t {
+    const uint32_t x = src[a].word(e), y = src[b].word(e);
+    return (e & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+  };
+  if constexpr (TPT == 4) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pair(0, 1), pair(2, 3));
+  } else {
+    *reinterpret_cast<uint32_t*>(dst) = pair(0, 1);
+  }
+}
+template <int TPT>
 __device__ __forceinline__ void put_channel(float* dst, const Seg8<float> (&src)[TPT], int e) {
   if constexpr (TPT == 4) {
     *reinterpret_cast<float4*>(dst) = make_float4(src[0].get(e), src[1].get(e), src[2].get(e), src[3].get(e));
@@ -121,46 +144,75 @@ __device__ __forceinline__ void put_channel(float* dst, const Seg8<float> (&src)
   }
 }
 
-template <typename T, int DK, int BV, typename P = typename ComputeOf<T>::type>
-struct ScanRegs {
+// Types of one scan instantiation.
+//   IOT: io type of v and o;  OPT: type of the operand tensors the scan reads
+//   (q / k for GDN, the gated operands for KDA);  P: type of the small 64 x 64
+//   products.  SPLIT: computed operands (S, diag(.) Vn) go to LDS as bf16
+//   hi + lo; otherwise in OPT.
+template <typename IOT_, typename OPT_, int DK_, int BV_, bool KDA_>
+struct ScanCfg {
+  typedef IOT_ IOT;
+  typedef OPT_ OPT;
+  typedef typename ComputeOf<IOT_>::type P;
+  static constexpr int DK = DK_, BV = BV_;
+  static constexpr bool KDA = KDA_;
+  static constexpr bool SPLIT = __is_same(OPT_, bf16_t);
   static constexpr int KS = DK / 32;        // channel slabs
   static constexpr int CB = BV / 16;        // 16-column blocks of the tile
+  static constexpr int WR = DK / 4;         // state rows (key channels) per wave
+  static constexpr int RB = WR / 16;        // 16-row blocks per wave
   static constexpr int CG = DK / 8;         // 8-channel groups (loader)
   static constexpr int TG = 256 / CG;       // token groups (loader)
   static constexpr int TPT = BT / TG;       // tokens per loader thread
-  Frag<T> kA[KS], qA[KS];                   // rows 16w + row of k, q (raw)
+};
+
+template <typename C>
+struct ScanRegs {
+  typedef typename C::OPT OPT;
+  typedef typename C::P P;
+  Frag<OPT> xA[C::KS], oA[C::KS];           // rows 16w + row of the X / O operands (k, q)
   Frag<P> ai[2], aq[2];                     // rows 16w + row of Ainv, Aqk
-  T vv[CB][4];                              // v[16w + 4grp + i][v0 + 16cb + row], raw
-  Seg8<T> kt[TPT];                          // loader: tokens TPT*tg + u, channels 8cg..
+  typename C::IOT vv[C::CB][4];             // v[16w + 4grp + i][v0 + 16cb + row], raw
+  Seg8<OPT> kt[C::TPT];                     // loader: tokens TPT*tg + u, channels 8cg..
                                             // (tg = tid % TG, cg = tid / TG)
   float4 gf[4];                             // gate factors of rows 16w + 4grp + i
-  float eGl;                                // e^{G_last} of the chunk (uniform)
+  float eGl;                                // GDN: e^{G_last} of the chunk (uniform)
+  float4 dg[C::RB];                         // KDA: e^{G_last} of key rows WR*w + 16rb + 4grp + i
 };
 
 // Streams the scan reads: work-group-uniform base pointers at the current
 // chunk (advanced by scalar adds) plus constant per-lane 32-bit offsets, so
-// every load is a saddr + voffset access with no per-chunk address VALU.
-template <typename T, typename P>
+// no per-chunk address arithmetic runs per lane.
+template <typename C>
 struct ScanStreams {
-  const T *q, *k, *v;
+  typedef typename C::OPT OPT;
+  typedef typename C::P P;
+  const OPT *x, *op, *t;                    // X operand, O operand, update operand (row-major)
+  const typename C::IOT* v;
   const P *ai, *aq;
   const float4* gf;
-  uint32_t oA, oAi, oV[4], oG[4], oK[4];  // element offsets within the chunk
+  const float* dg;                          // KDA decay rows of the chunk
+  uint32_t oA, oAi, oV[4], oG[4], oK[4], oD;  // element offsets within the chunk
 };
 
 // Issue the loads of one chunk.  Full chunks take the unpredicated path; the
 // tail chunk of a sequence (nrow < 64) zero-fills rows past its end.  Raw
 // values only: nothing here waits on a load.
-template <typename T, int DK, int BV, typename P>
-__device__ __forceinline__ void load_chunk(ScanRegs<T, DK, BV, P>& R, const ScanStreams<T, P>& S,
-                                           int nrow, int w, int lane, int tid) {
-  typedef ScanRegs<T, DK, BV, P> RT;
-  R.eGl = S.gf[0].w;  // row 0 of the chunk is always valid
+template <typename C>
+__device__ __forceinline__ void load_chunk(ScanRegs<C>& R, const ScanStreams<C>& S, int nrow,
+                                           int w, int lane, int tid) {
+  typedef typename C::IOT IOT;
+  if constexpr (C::KDA) {
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) R.dg[rb] = *reinterpret_cast<const float4*>(S.dg + S.oD + 16 * rb);
+  } else {
+    R.eGl = S.gf[0].w;  // row 0 of the chunk is always valid
+  }
   if (nrow == BT) {
 #pragma unroll
-    for (int s = 0; s < RT::KS; ++s) {
-      load8(R.kA[s], S.k + S.oA + 32 * s);
-      load8(R.qA[s], S.q + S.oA + 32 * s);
+    for (int s = 0; s < C::KS; ++s) {
+      load8(R.xA[s], S.x + S.oA + 32 * s);
+      load8(R.oA[s], S.op + S.oA + 32 * s);
     }
     load8(R.ai[0], S.ai + S.oAi);
     load8(R.aq[0], S.aq + S.oAi);
@@ -171,19 +223,19 @@ __device__ __forceinline__ void load_chunk(ScanRegs<T, DK, BV, P>& R, const Scan
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int cb = 0; cb < RT::CB; ++cb) R.vv[cb][i] = S.v[S.oV[i] + 16 * cb];
+      for (int cb = 0; cb < C::CB; ++cb) R.vv[cb][i] = S.v[S.oV[i] + 16 * cb];
       R.gf[i] = S.gf[S.oG[i]];
     }
 #pragma unroll
-    for (int u = 0; u < RT::TPT; ++u) R.kt[u].load(S.k + S.oK[u]);
+    for (int u = 0; u < C::TPT; ++u) R.kt[u].load(S.t + S.oK[u]);
     return;
   }
   const int row = lane & 15, grp = lane >> 4;
   if (16 * w + row < nrow) {
 #pragma unroll
-    for (int s = 0; s < RT::KS; ++s) {
-      load8(R.kA[s], S.k + S.oA + 32 * s);
-      load8(R.qA[s], S.q + S.oA + 32 * s);
+    for (int s = 0; s < C::KS; ++s) {
+      load8(R.xA[s], S.x + S.oA + 32 * s);
+      load8(R.oA[s], S.op + S.oA + 32 * s);
     }
     load8(R.ai[0], S.ai + S.oAi);
     load8(R.aq[0], S.aq + S.oAi);
@@ -193,45 +245,60 @@ __device__ __forceinline__ void load_chunk(ScanRegs<T, DK, BV, P>& R, const Scan
     }
   } else {
 #pragma unroll
-    for (int s = 0; s < RT::KS; ++s) { R.kA[s].zero(); R.qA[s].zero(); }
+    for (int s = 0; s < C::KS; ++s) { R.xA[s].zero(); R.oA[s].zero(); }
     R.ai[0].zero(); R.aq[0].zero(); R.ai[1].zero(); R.aq[1].zero();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const bool ok = 16 * w + 4 * grp + i < nrow;
 #pragma unroll
-    for (int cb = 0; cb < RT::CB; ++cb) R.vv[cb][i] = ok ? S.v[S.oV[i] + 16 * cb] : T(0);
+    for (int cb = 0; cb < C::CB; ++cb) R.vv[cb][i] = ok ? S.v[S.oV[i] + 16 * cb] : IOT(0);
     R.gf[i] = ok ? S.gf[S.oG[i]] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const int tg = tid % RT::TG;
+  const int tg = tid % C::TG;
 #pragma unroll
-  for (int u = 0; u < RT::TPT; ++u) {
-    if (RT::TPT * tg + u < nrow) R.kt[u].load(S.k + S.oK[u]);
+  for (int u = 0; u < C::TPT; ++u) {
+    if (C::TPT * tg + u < nrow) R.kt[u].load(S.t + S.oK[u]);
     else R.kt[u].zero();
   }
 }
 
-template <typename T, int DK, int BV, typename P = typename ComputeOf<T>::type>
-__global__ __launch_bounds__(256) void gdn_scan_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float4* __restrict__ GF, float scale,
-    const float* __restrict__ h0, float* __restrict__ ht, const P* __restrict__ Ainv,
-    const P* __restrict__ Aqk, T* __restrict__ o, const int64_t* __restrict__ cu,
-    const int32_t* __restrict__ order, int Tlen, int N, int Hk, int HV, int V) {
-  typedef ScanRegs<T, DK, BV, P> RT;
-  constexpr bool SPLIT = sizeof(T) == 2;  // bf16 io: hi + lo parts of computed operands
-  constexpr int KS = RT::KS, CB = RT::CB;
-  constexpr int WR = DK / 4;              // state rows (key channels) per wave
-  constexpr int RB = WR / 16;             // 16-row blocks per wave
+// Operand tensors and chunk tables of one scan launch.
+struct ScanArgs {
+  const void *x, *op, *t;   // X operand, O operand, update operand
+  int op_rows;              // heads per token row of the operand tensors
+  int op_head_div;          // operand head of v-head j: j / op_head_div
+  const float* dg;          // KDA decay [chunks, HV, K] or nullptr
+  const int32_t* coff;      // varlen chunk offsets or nullptr
+  int NT;                   // chunks per sequence without varlen
+};
+
+template <typename C>
+__global__ __launch_bounds__(256) void chunk_scan_kernel(
+    const typename C::OPT* __restrict__ xop, const typename C::OPT* __restrict__ oop,
+    const typename C::OPT* __restrict__ top, int op_rows, int op_head_div,
+    const typename C::IOT* __restrict__ v, const float4* __restrict__ GF,
+    const float* __restrict__ DG, float scale, const float* __restrict__ h0,
+    float* __restrict__ ht, const typename C::P* __restrict__ Ainv,
+    const typename C::P* __restrict__ Aqk, typename C::IOT* __restrict__ o,
+    const int64_t* __restrict__ cu, const int32_t* __restrict__ coff,
+    const int32_t* __restrict__ order, int Tlen, int NT, int N, int HV, int V) {
+  typedef ScanRegs<C> RT;
+  typedef typename C::OPT OPT;
+  typedef typename C::P P;
+  typedef typename C::IOT IOT;
+  constexpr bool SPLIT = C::SPLIT;
+  constexpr int DK = C::DK, BV = C::BV;
+  constexpr int KS = C::KS, CB = C::CB, WR = C::WR, RB = C::RB;
   constexpr int KP = DK + 8;              // padded key row of the state copy
   constexpr int NL = SPLIT ? BV : 1;      // rows of the lo-part tiles
-  __shared__ __attribute__((aligned(16))) T sKt[DK][TP];   // K^T of the chunk (raw, token-contiguous)
-  __shared__ __attribute__((aligned(16))) T sSh[BV][KP];   // S (value rows, key-contiguous), hi part
-  __shared__ __attribute__((aligned(16))) T sSl[NL][KP];   //   lo part
-  __shared__ __attribute__((aligned(16))) P sR[BV][TP];    // R^T
-  __shared__ __attribute__((aligned(16))) P sVn[BV][TP];   // Vn^T
-  __shared__ __attribute__((aligned(16))) T sVth[BV][TP];  // (diag(e^{G_last - G}) Vn)^T, hi part
-  __shared__ __attribute__((aligned(16))) T sVtl[NL][TP];  //   lo part
+  __shared__ __attribute__((aligned(16))) OPT sKt[DK][TP];   // update operand^T (token-contiguous)
+  __shared__ __attribute__((aligned(16))) OPT sSh[BV][KP];   // S (value rows, key-contiguous), hi part
+  __shared__ __attribute__((aligned(16))) OPT sSl[NL][KP];   //   lo part
+  __shared__ __attribute__((aligned(16))) P sR[BV][TP];      // R^T
+  __shared__ __attribute__((aligned(16))) P sVn[BV][TP];     // Vn^T
+  __shared__ __attribute__((aligned(16))) OPT sVth[BV][TP];  // (diag(e^{G_last - G}) Vn)^T, hi part
+  __shared__ __attribute__((aligned(16))) OPT sVtl[NL][TP];  //   lo part
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
@@ -247,18 +314,20 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
   if (grpi >= N * HV) return;
   const int rank = grpi / HV, j = grpi - rank * HV;
   const int n = order ? order[rank] : rank;
-  int bos, eos;
+  int bos, eos, chunk0;
   if (cu) {
     long long b0 = cu[n], b1 = cu[n + 1];
     b0 = b0 < 0 ? 0 : (b0 > Tlen ? Tlen : b0);
     b1 = b1 < b0 ? b0 : (b1 > Tlen ? Tlen : b1);
     bos = (int)b0;
     eos = (int)b1;
+    chunk0 = coff ? coff[n] : 0;
   } else {
     bos = n * Tlen;
     eos = bos + Tlen;
+    chunk0 = n * NT;
   }
-  const int jk = j / (HV / Hk);
+  const int jo = j / op_head_div;  // operand head
   const int v0 = vt * BV;
 
   // ---- initial state: St[rb][cb] lane holds S^T[c][v] for
@@ -277,31 +346,36 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
         St[rb][cb] = zero4();
       }
       const int c = WR * w + 16 * rb + 4 * grp;
-      st4_split<T>(&sSh[16 * cb + row][c], &sSl[SPLIT ? 16 * cb + row : 0][c], St[rb][cb][0],
-                   St[rb][cb][1], St[rb][cb][2], St[rb][cb][3]);
+      st4_split<OPT>(&sSh[16 * cb + row][c], &sSl[SPLIT ? 16 * cb + row : 0][c], St[rb][cb][0],
+                     St[rb][cb][1], St[rb][cb][2], St[rb][cb][3]);
     }
 
   // ---- streams: uniform bases at chunk 0, per-lane offsets, per-chunk strides
-  const uint32_t sQK = (uint32_t)Hk * DK, sA = (uint32_t)HV * BT, sV = (uint32_t)HV * V, sG = (uint32_t)HV;
+  const uint32_t sQK = (uint32_t)op_rows * DK, sA = (uint32_t)HV * BT, sV = (uint32_t)HV * V,
+                 sG = (uint32_t)HV;
   // loader: token group varies fastest across lanes, so the transposed
-  // K^T writes of a half-wave cover one contiguous 128-byte row segment
-  const int tg = tid % RT::TG, cg = tid / RT::TG;
-  ScanStreams<T, P> St_;
-  St_.q = q + (size_t)bos * sQK + (size_t)jk * DK;
-  St_.k = k + (size_t)bos * sQK + (size_t)jk * DK;
+  // writes of a half-wave cover one contiguous 128-byte row segment
+  const int tg = tid % C::TG, cg = tid / C::TG;
+  ScanStreams<C> St_;
+  St_.x = xop + (size_t)bos * sQK + (size_t)jo * DK;
+  St_.op = oop + (size_t)bos * sQK + (size_t)jo * DK;
+  St_.t = top + (size_t)bos * sQK + (size_t)jo * DK;
   St_.ai = Ainv + (size_t)bos * sA + (size_t)j * BT;
   St_.aq = Aqk + (size_t)bos * sA + (size_t)j * BT;
   St_.v = v + (size_t)bos * sV + (size_t)j * V + v0;
   St_.gf = GF + (size_t)bos * sG + j;
+  St_.dg = DG ? DG + ((size_t)chunk0 * HV + j) * DK : nullptr;
   St_.oA = (uint32_t)(16 * w + row) * sQK + 8 * grp;
   St_.oAi = (uint32_t)(16 * w + row) * sA + 8 * grp;
+  St_.oD = (uint32_t)(WR * w + 4 * grp);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     St_.oV[i] = (uint32_t)(16 * w + 4 * grp + i) * sV + row;
     St_.oG[i] = (uint32_t)(16 * w + 4 * grp + i) * sG;
-    St_.oK[i] = (uint32_t)(RT::TPT * tg + (i < RT::TPT ? i : 0)) * sQK + 8 * cg;
+    St_.oK[i] = (uint32_t)(C::TPT * tg + (i < C::TPT ? i : 0)) * sQK + 8 * cg;
   }
-  const size_t cQK = (size_t)BT * sQK, cA = (size_t)BT * sA, cV = (size_t)BT * sV, cG = (size_t)BT * sG;
+  const size_t cQK = (size_t)BT * sQK, cA = (size_t)BT * sA, cV = (size_t)BT * sV,
+               cG = (size_t)BT * sG, cD = (size_t)HV * DK;
 
   const int NC = (eos - bos + BT - 1) / BT;
 
@@ -309,18 +383,19 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
   auto step = [&](RT& cur, RT& nxt, int ic) {
     const int c0 = bos + ic * BT;
     const int nrow = eos - c0 < BT ? eos - c0 : BT;
-    // K^T into LDS from the loader registers
+    // update operand^T into LDS from the loader registers
 #pragma unroll
-    for (int e = 0; e < 8; ++e) put_channel<RT::TPT>(&sKt[8 * cg + e][RT::TPT * tg], cur.kt, e);
+    for (int e = 0; e < 8; ++e) put_channel<C::TPT>(&sKt[8 * cg + e][C::TPT * tg], cur.kt, e);
     if (ic + 1 < NC) {
-      St_.q += cQK; St_.k += cQK; St_.ai += cA; St_.aq += cA; St_.v += cV; St_.gf += cG;
+      St_.x += cQK; St_.op += cQK; St_.t += cQK; St_.ai += cA; St_.aq += cA; St_.v += cV;
+      St_.gf += cG;
+      if constexpr (C::KDA) St_.dg += cD;
       const int c1 = c0 + BT;
-      load_chunk<T, DK, BV, P>(nxt, St_, eos - c1 < BT ? eos - c1 : BT, w, lane, tid);
+      load_chunk<C>(nxt, St_, eos - c1 < BT ? eos - c1 : BT, w, lane, tid);
     }
     float eG[4], eGt[4], br[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) { eG[i] = cur.gf[i].x; eGt[i] = cur.gf[i].y; br[i] = cur.gf[i].z; }
-    const float eGl = cur.eGl;
 
     // ---- steps 1-2: X = K S^T, Oi = Q S^T (rows 16w.., all BV columns)
     f32x4 X[CB], Oi[CB];
@@ -330,23 +405,24 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        Frag<T> sf;
+        Frag<OPT> sf;
         load8(sf, &sSh[16 * cb + row][32 * s + 8 * grp]);
-        X[cb] = mma(cur.kA[s], sf, X[cb]);
-        Oi[cb] = mma(cur.qA[s], sf, Oi[cb]);
+        X[cb] = mma(cur.xA[s], sf, X[cb]);
+        Oi[cb] = mma(cur.oA[s], sf, Oi[cb]);
         if constexpr (SPLIT) {
           load8(sf, &sSl[16 * cb + row][32 * s + 8 * grp]);
-          X[cb] = mma(cur.kA[s], sf, X[cb]);
-          Oi[cb] = mma(cur.qA[s], sf, Oi[cb]);
+          X[cb] = mma(cur.xA[s], sf, X[cb]);
+          Oi[cb] = mma(cur.oA[s], sf, Oi[cb]);
         }
       }
     }
-    // ---- step 3: R = beta (v - e^G X) -> LDS (transposed)
+    // ---- step 3: R = beta (v - e^G X) -> LDS (transposed); KDA: e^G is in the operand
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       float rv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rv[i] = br[i] * (to_f(cur.vv[cb][i]) - eG[i] * X[cb][i]);
+      for (int i = 0; i < 4; ++i)
+        rv[i] = br[i] * (to_f(cur.vv[cb][i]) - (C::KDA ? X[cb][i] : eG[i] * X[cb][i]));
       st4<P>(&sR[16 * cb + row][16 * w + 4 * grp], rv[0], rv[1], rv[2], rv[3]);
     }
     __syncthreads();
@@ -363,8 +439,13 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
         Vn[cb] = mma(cur.ai[1], rf, Vn[cb]);
       }
       st4<P>(&sVn[16 * cb + row][16 * w + 4 * grp], Vn[cb][0], Vn[cb][1], Vn[cb][2], Vn[cb][3]);
-      st4_split<T>(&sVth[16 * cb + row][16 * w + 4 * grp], &sVtl[SPLIT ? 16 * cb + row : 0][16 * w + 4 * grp],
-                   Vn[cb][0] * eGt[0], Vn[cb][1] * eGt[1], Vn[cb][2] * eGt[2], Vn[cb][3] * eGt[3]);
+      if constexpr (C::KDA) {
+        st4_split<OPT>(&sVth[16 * cb + row][16 * w + 4 * grp], &sVtl[SPLIT ? 16 * cb + row : 0][16 * w + 4 * grp],
+                       Vn[cb][0], Vn[cb][1], Vn[cb][2], Vn[cb][3]);
+      } else {
+        st4_split<OPT>(&sVth[16 * cb + row][16 * w + 4 * grp], &sVtl[SPLIT ? 16 * cb + row : 0][16 * w + 4 * grp],
+                       Vn[cb][0] * eGt[0], Vn[cb][1] * eGt[1], Vn[cb][2] * eGt[2], Vn[cb][3] * eGt[3]);
+      }
     }
     __syncthreads();
 
@@ -373,7 +454,7 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
     for (int cb = 0; cb < CB; ++cb) {
       f32x4 acc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = Oi[cb][i] * (scale * eG[i]);
+      for (int i = 0; i < 4; ++i) acc[i] = Oi[cb][i] * (C::KDA ? scale : scale * eG[i]);
       Frag<P> vf;
       load8(vf, &sVn[16 * cb + row][8 * grp]);
       acc = mma(cur.aq[0], vf, acc);
@@ -384,7 +465,7 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * w + 4 * grp + i;
-        if (rr < nrow) o[((size_t)(c0 + rr) * HV + j) * V + v0 + 16 * cb + row] = from_f<T>(acc[i]);
+        if (rr < nrow) o[((size_t)(c0 + rr) * HV + j) * V + v0 + 16 * cb + row] = from_f<IOT>(acc[i]);
       }
     }
     // ---- step 6: S^T = e^{G_last} S^T + K^T diag(e^{G_last - G}) Vn
@@ -392,10 +473,15 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        f32x4 acc = St[rb][cb] * eGl;
+        f32x4 acc;
+        if constexpr (C::KDA) {
+          acc = St[rb][cb] * f32x4{cur.dg[rb].x, cur.dg[rb].y, cur.dg[rb].z, cur.dg[rb].w};
+        } else {
+          acc = St[rb][cb] * cur.eGl;
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          Frag<T> af, bfr;
+          Frag<OPT> af, bfr;
           load8(af, &sKt[WR * w + 16 * rb + row][32 * s + 8 * grp]);
           load8(bfr, &sVth[16 * cb + row][32 * s + 8 * grp]);
           acc = mma(af, bfr, acc);
@@ -406,14 +492,14 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
         }
         St[rb][cb] = acc;
         const int c = WR * w + 16 * rb + 4 * grp;
-        st4_split<T>(&sSh[16 * cb + row][c], &sSl[SPLIT ? 16 * cb + row : 0][c], acc[0], acc[1],
-                     acc[2], acc[3]);
+        st4_split<OPT>(&sSh[16 * cb + row][c], &sSl[SPLIT ? 16 * cb + row : 0][c], acc[0], acc[1],
+                       acc[2], acc[3]);
       }
     __syncthreads();
   };
 
   RT ra, rb;
-  if (NC > 0) load_chunk<T, DK, BV, P>(ra, St_, eos - bos < BT ? eos - bos : BT, w, lane, tid);
+  if (NC > 0) load_chunk<C>(ra, St_, eos - bos < BT ? eos - bos : BT, w, lane, tid);
   for (int ic = 0; ic < NC; ic += 2) {
     step(ra, rb, ic);
     if (ic + 1 < NC) step(rb, ra, ic + 1);
@@ -430,28 +516,57 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
   }
 }
 
-template <typename T, int DK, int BV>
-hipError_t launch_scan_t(const ChunkArgs& a, hipStream_t s) {
-  typedef typename ComputeOf<T>::type P;
-  const int nvt = a.V / BV;
+template <typename C>
+hipError_t launch_scan_c(const ChunkArgs& a, const ScanArgs& sa, hipStream_t s) {
+  typedef typename C::OPT OPT;
+  typedef typename C::P P;
+  typedef typename C::IOT IOT;
+  const int nvt = a.V / C::BV;
   const int groups = a.N * a.HV;
   const int nblk = ((groups + 7) / 8) * 8 * nvt;
-  hipLaunchKernelGGL((gdn_scan_kernel<T, DK, BV>), dim3((unsigned)nblk), dim3(256), 0, s,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float4*)a.GF, a.scale,
-                     a.h0, a.ht, (const P*)a.Ainv, (const P*)a.Aqk, (T*)a.o, a.cu_seqlens,
-                     a.seq_order, a.T, a.N, a.Hk, a.HV, a.V);
+  hipLaunchKernelGGL((chunk_scan_kernel<C>), dim3((unsigned)nblk), dim3(256), 0, s,
+                     (const OPT*)sa.x, (const OPT*)sa.op, (const OPT*)sa.t, sa.op_rows,
+                     sa.op_head_div, (const IOT*)a.v, (const float4*)a.GF, sa.dg, a.scale, a.h0,
+                     a.ht, (const P*)a.Ainv, (const P*)a.Aqk, (IOT*)a.o, a.cu_seqlens, sa.coff,
+                     a.seq_order, a.T, sa.NT, a.N, a.HV, a.V);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_scan_gdn(const ChunkArgs& a, hipStream_t s) {
+  ScanArgs sa;
+  sa.x = a.k; sa.op = a.q; sa.t = a.k;
+  sa.op_rows = a.Hk;
+  sa.op_head_div = a.HV / a.Hk;
+  sa.dg = nullptr;
+  sa.coff = nullptr;
+  sa.NT = (a.T + BT - 1) / BT;
   if (a.bf16) {
-    if (a.K == 128) return launch_scan_t<bf16_t, 128, 16>(a, s);
-    return launch_scan_t<bf16_t, 64, 16>(a, s);
+    if (a.K == 128) return launch_scan_c<ScanCfg<bf16_t, bf16_t, 128, 16, false>>(a, sa, s);
+    return launch_scan_c<ScanCfg<bf16_t, bf16_t, 64, 16, false>>(a, sa, s);
   }
-  if (a.K == 128) return launch_scan_t<float, 128, 16>(a, s);
-  return launch_scan_t<float, 64, 16>(a, s);
+  if (a.K == 128) return launch_scan_c<ScanCfg<float, float, 128, 16, false>>(a, sa, s);
+  return launch_scan_c<ScanCfg<float, float, 64, 16, false>>(a, sa, s);
+}
+
+// KDA: operands are the gated tensors written by the KDA intra kernel, one
+// per v-head ([tokens, HV, K]), plus the per-chunk decay rows DG.
+hipError_t launch_scan_kda(const ChunkArgs& a, const void* qg, const void* kg, const void* kt,
+                           const float* dg, hipStream_t s) {
+  ScanArgs sa;
+  sa.x = kg; sa.op = qg; sa.t = kt;
+  sa.op_rows = a.HV;
+  sa.op_head_div = 1;
+  sa.dg = dg;
+  sa.coff = a.chunk_off;
+  sa.NT = (a.T + BT - 1) / BT;
+  if (a.bf16) {
+    if (a.K == 128) return launch_scan_c<ScanCfg<bf16_t, f16_t, 128, 16, true>>(a, sa, s);
+    return launch_scan_c<ScanCfg<bf16_t, f16_t, 64, 16, true>>(a, sa, s);
+  }
+  if (a.K == 128) return launch_scan_c<ScanCfg<float, float, 128, 16, true>>(a, sa, s);
+  return launch_scan_c<ScanCfg<float, float, 64, 16, true>>(a, sa, s);
 }
 
 }  // namespace gdn

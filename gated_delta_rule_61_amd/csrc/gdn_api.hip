@@ -17,6 +17,10 @@ namespace gdn {
 
 hipError_t launch_intra_gdn(const ChunkArgs& a, hipStream_t s, int NT, int nslots);
 hipError_t launch_scan_gdn(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_intra_kda(const ChunkArgs& a, const KdaBuffers& kb, hipStream_t s, int NT,
+                            int nslots);
+hipError_t launch_scan_kda(const ChunkArgs& a, const void* qg, const void* kg, const void* kt,
+                           const float* dg, hipStream_t s);
 
 namespace {
 
@@ -170,7 +174,8 @@ void prof_end(int stage, hipStream_t s) {
   t_open[stage] = nullptr;
 }
 
-ChunkWorkspace chunk_workspace_layout(long long tokens, int HV, int N, int elem_bytes) {
+ChunkWorkspace chunk_workspace_layout(long long tokens, int HV, int K, int N, int max_chunks,
+                                      int elem_bytes, bool kda) {
   ChunkWorkspace w;
   const size_t mat = (size_t)tokens * HV * 64 * elem_bytes;
   w.ainv_off = 0;
@@ -178,8 +183,41 @@ ChunkWorkspace chunk_workspace_layout(long long tokens, int HV, int N, int elem_
   w.gf_off = w.aqk_off + up(mat);
   w.coff_off = w.gf_off + up((size_t)tokens * HV * 16);
   w.order_off = w.coff_off + up((size_t)(N + 1) * 4);
-  w.total = w.order_off + up((size_t)(N > 0 ? N : 1) * 4);
+  size_t end = w.order_off + up((size_t)(N > 0 ? N : 1) * 4);
+  w.qg_off = w.kg_off = w.kt_off = w.dg_off = 0;
+  if (kda) {
+    const size_t op = (size_t)tokens * HV * K * elem_bytes;
+    w.qg_off = end;
+    w.kg_off = w.qg_off + up(op);
+    w.kt_off = w.kg_off + up(op);
+    w.dg_off = w.kt_off + up(op);
+    end = w.dg_off + up((size_t)(max_chunks > 0 ? max_chunks : 1) * HV * K * 4);
+  }
+  w.total = end;
   return w;
+}
+
+hipError_t launch_kda_fwd(const ChunkArgs& a, const KdaBuffers& kb, hipStream_t s) {
+  if (a.cu_seqlens) {
+    prof_begin(GDN_STAGE_VARLEN_TABLES, s);
+    hipLaunchKernelGGL(varlen_tables_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.N, a.T,
+                       a.chunk_off, a.seq_order);
+    hipError_t e = hipGetLastError();
+    prof_end(GDN_STAGE_VARLEN_TABLES, s);
+    if (e != hipSuccess) return e;
+  }
+  const int NT = (a.T + 63) / 64;
+  const int nslots = a.cu_seqlens ? NT + a.N : a.B * NT;
+  if (nslots > 0 && (long long)a.B * a.T > 0) {
+    prof_begin(GDN_STAGE_INTRA, s);
+    hipError_t e = launch_intra_kda(a, kb, s, NT, nslots);
+    prof_end(GDN_STAGE_INTRA, s);
+    if (e != hipSuccess) return e;
+  }
+  prof_begin(GDN_STAGE_SCAN, s);
+  const hipError_t e = launch_scan_kda(a, kb.qg, kb.kg, kb.kt, kb.dg, s);
+  prof_end(GDN_STAGE_SCAN, s);
+  return e;
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t s) {
@@ -231,12 +269,19 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
   if (B < 0 || T < 0 || Hk <= 0 || HV <= 0 || K <= 0 || V <= 0 || num_seqs < 0) return 0;
   if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return 0;
   const int N = num_seqs > B ? num_seqs : B;
-  return chunk_workspace_layout((long long)B * T, HV, N, dtype == GDN_DTYPE_BF16 ? 2 : 4).total;
+  const int maxc = (T + 63) / 64 * B + N;
+  return chunk_workspace_layout((long long)B * T, HV, K, N, maxc, dtype == GDN_DTYPE_BF16 ? 2 : 4,
+                                false).total;
 }
 
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V, int num_seqs,
                                      int dtype) {
-  return gdn_chunk_fwd_workspace_bytes(B, T, Hk, HV, K, V, num_seqs, dtype);
+  if (B < 0 || T < 0 || Hk <= 0 || HV <= 0 || K <= 0 || V <= 0 || num_seqs < 0) return 0;
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return 0;
+  const int N = num_seqs > B ? num_seqs : B;
+  const int maxc = (T + 63) / 64 * B + N;
+  return chunk_workspace_layout((long long)B * T, HV, K, N, maxc, dtype == GDN_DTYPE_BF16 ? 2 : 4,
+                                true).total;
 }
 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -248,7 +293,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                        chunk_size, dtype, o, P);
   if (st != GDN_OK) return st;
   const int eb = dtype == GDN_DTYPE_BF16 ? 2 : 4;
-  const ChunkWorkspace L = chunk_workspace_layout((long long)B * T, HV, P.N, eb);
+  const ChunkWorkspace L = chunk_workspace_layout((long long)B * T, HV, K, P.N,
+                                                  (T + 63) / 64 * B + P.N, eb, false);
   if (!workspace || workspace_bytes < L.total)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", L.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -284,8 +330,38 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* gk, 
   if (st != GDN_OK) return st;
   if ((Aqk && !aligned16(Aqk)) || (Akk_inv && !aligned16(Akk_inv)))
     return fail(GDN_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
-  (void)workspace; (void)workspace_bytes; (void)stream; (void)scale;
-  return fail(GDN_ERR_UNSUPPORTED, "kda_chunk_fwd: per-channel gate path not built yet");
+  const int eb = dtype == GDN_DTYPE_BF16 ? 2 : 4;
+  const ChunkWorkspace L = chunk_workspace_layout((long long)B * T, HV, K, P.N,
+                                                  (T + 63) / 64 * B + P.N, eb, true);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (P.N == 0) return ok();
+  char* ws = (char*)workspace;
+  ChunkArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = nullptr; a.gk = gk; a.beta = beta; a.scale = scale;
+  a.h0 = h0; a.ht = ht; a.cu_seqlens = cu_seqlens; a.N = P.N;
+  a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
+  a.bf16 = dtype == GDN_DTYPE_BF16;
+  a.o = o;
+  a.Ainv = ws + L.ainv_off;
+  a.Aqk = ws + L.aqk_off;
+  a.GF = ws + L.gf_off;
+  a.chunk_off = cu_seqlens ? (int32_t*)(ws + L.coff_off) : nullptr;
+  a.seq_order = cu_seqlens ? (int32_t*)(ws + L.order_off) : nullptr;
+  a.max_chunks = (T + 63) / 64 * B + P.N;
+  KdaBuffers kb;
+  kb.Aqk_out = Aqk;
+  kb.Akk_out = Akk_inv;
+  kb.qg = ws + L.qg_off;
+  kb.kg = ws + L.kg_off;
+  kb.kt = ws + L.kt_off;
+  kb.dg = (float*)(ws + L.dg_off);
+  const hipError_t e = launch_kda_fwd(a, kb, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int gdn_decode(const void* q, const void* k, const void* v, const void* a, const void* b,

@@ -45,10 +45,22 @@ struct ChunkArgs {
 };
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t s);
 
+// Extra buffers of the KDA path.
+struct KdaBuffers {
+  void* Aqk_out;         // [B*T, HV, 64] io dtype output or nullptr
+  void* Akk_out;         // [B*T, HV, 64] io dtype output or nullptr
+  void *qg, *kg, *kt;    // [B*T, HV, K] compute dtype: Q o e^G, K o e^G, K o e^{G_last - G}
+  float* dg;             // [chunks, HV, K] e^{G_last}
+};
+hipError_t launch_kda_fwd(const ChunkArgs& a, const KdaBuffers& kb, hipStream_t s);
+
 // Workspace layout shared by the size query and the launcher.
 struct ChunkWorkspace {
-  size_t ainv_off, aqk_off, gf_off, coff_off, order_off, total;
+  size_t ainv_off, aqk_off, gf_off, coff_off, order_off;
+  size_t qg_off, kg_off, kt_off, dg_off;  // KDA only
+  size_t total;
 };
-ChunkWorkspace chunk_workspace_layout(long long BT_tokens, int HV, int N, int elem_bytes);
+ChunkWorkspace chunk_workspace_layout(long long tokens, int HV, int K, int N, int max_chunks,
+                                      int elem_bytes, bool kda);
 
 }  // namespace gdn
