@@ -53,9 +53,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    p.add_argument("--cpu-sample-tokens", type=int, default=16384)
     p.add_argument("--skip-extra", action="store_true", help="prefill workload only")
-    p.add_argument("--only", choices=["prefill", "decode", "kda"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "kda", "copy"], default=None,
                    help="run one workload (for profiling) and print its figures")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache prefill timing")
     return p.parse_args()
@@ -151,6 +151,7 @@ def bench_decode(args, binding, workloads, torch, T):
         "kernel_state_GBps": round(state_bytes / (kms * 1e-3) / 1e9, 1),
         "kernel_total_GBps": round((state_bytes + other) / (kms * 1e-3) / 1e9, 1),
         "hbm_frac": round((state_bytes + other) / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(f"decode:T{T}"),
     }
 
 
@@ -169,6 +170,32 @@ def bench_kda(args, binding, workloads, torch):
     return {"workload": f"kda_chunk_fwd B={B} T={T} H={HV} K=V={K} bf16",
             "ms_per_call": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "mfma_frac_method_flops": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources (the same hash the profile summaries record)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_61_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch of one kernel from the committed rocprofv3 byte
+    counters, or None when the kernels changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except OSError:
+        return None
+    if d.get("source_sha") != source_hash() or key not in d.get("per_launch", {}):
+        return None
+    t = d["per_launch"][key]
+    return int(t["fetch_bytes"] + t["write_bytes"])
 
 
 def cpu_baseline(args, workloads):
@@ -204,6 +231,15 @@ def main():
         print(json.dumps({"decode": {"T1": bench_decode(args, binding, workloads, torch, 1),
                                      "T4": bench_decode(args, binding, workloads, torch, 4)}}), flush=True)
         return
+    if args.only == "copy":
+        # calibration for the HBM byte counters: a plain 512 MiB device copy
+        src = torch.ones(1 << 27, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "calls": args.steps}), flush=True)
+        return
     if args.only == "kda":
         print(json.dumps({"kda": bench_kda(args, binding, workloads, torch)}), flush=True)
         return
@@ -237,7 +273,8 @@ def main():
         "kernels_ms": {s: round(v, 5) for s, v in stage_ms.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(f"prefill:{dom}")},
     }
     if not args.skip_extra and args.only is None:
         out["decode"] = {"T1": bench_decode(args, binding, workloads, torch, 1),

@@ -9,7 +9,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/gdn61.h"
+#include "gdn61.h"
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
