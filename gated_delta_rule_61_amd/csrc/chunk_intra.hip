@@ -47,7 +47,7 @@ __global__ __launch_bounds__(64) void gdn_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, C* __restrict__ Ainv,
     C* __restrict__ Aqk, float4* __restrict__ GF, const int64_t* __restrict__ cu,
-    const int32_t* __restrict__ coff, int Tlen, int N, int NT, int Hk, int HV) {
+    const int32_t* __restrict__ coff, int Tlen, int ttot, int N, int NT, int Hk, int HV) {
   __shared__ __attribute__((aligned(16))) float sA[BT][AP];
   const int lane = threadIdx.x;
   const int j = blockIdx.y;
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(64) void gdn_intra_kernel(
   {
     const float Gl = __shfl(G, nrow - 1, 64);
     if (lane < nrow)
-      GF[(size_t)(c0 + lane) * HV + j] = make_float4(__expf(G), __expf(Gl - G), bl, __expf(Gl));
+      GF[(size_t)j * ttot + c0 + lane] = make_float4(__expf(G), __expf(Gl - G), bl, __expf(Gl));
   }
 
   // Step 1: ten lower blocks of K K^T and Q K^T
@@ -153,23 +153,23 @@ hipError_t launch_intra_gdn(const ChunkArgs& a, hipStream_t s, int NT, int nslot
       hipLaunchKernelGGL((gdn_intra_kernel<bf16_t, 128>), grid, dim3(64), 0, s,
                          (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, a.scale,
                          (f16_t*)a.Ainv, (f16_t*)a.Aqk, (float4*)a.GF, a.cu_seqlens, a.chunk_off,
-                         a.T, a.N, NT, a.Hk, a.HV);
+                         a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
     else
       hipLaunchKernelGGL((gdn_intra_kernel<bf16_t, 64>), grid, dim3(64), 0, s,
                          (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, a.scale,
                          (f16_t*)a.Ainv, (f16_t*)a.Aqk, (float4*)a.GF, a.cu_seqlens, a.chunk_off,
-                         a.T, a.N, NT, a.Hk, a.HV);
+                         a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
   } else {
     if (a.K == 128)
       hipLaunchKernelGGL((gdn_intra_kernel<float, 128>), grid, dim3(64), 0, s,
                          (const float*)a.q, (const float*)a.k, a.g, a.beta, a.scale,
                          (float*)a.Ainv, (float*)a.Aqk, (float4*)a.GF, a.cu_seqlens, a.chunk_off,
-                         a.T, a.N, NT, a.Hk, a.HV);
+                         a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
     else
       hipLaunchKernelGGL((gdn_intra_kernel<float, 64>), grid, dim3(64), 0, s,
                          (const float*)a.q, (const float*)a.k, a.g, a.beta, a.scale,
                          (float*)a.Ainv, (float*)a.Aqk, (float4*)a.GF, a.cu_seqlens, a.chunk_off,
-                         a.T, a.N, NT, a.Hk, a.HV);
+                         a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
   }
   return hipGetLastError();
 }

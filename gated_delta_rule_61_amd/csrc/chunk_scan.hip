@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     float* __restrict__ ht, const typename C::P* __restrict__ Ainv,
     const typename C::P* __restrict__ Aqk, typename C::IOT* __restrict__ o,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ coff,
-    const int32_t* __restrict__ order, int Tlen, int NT, int N, int HV, int V) {
+    const int32_t* __restrict__ order, int Tlen, int ttot, int NT, int N, int HV, int V) {
   typedef ScanRegs<C> RT;
   typedef typename C::OPT OPT;
   typedef typename C::P P;
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
 
   // ---- streams: uniform bases at chunk 0, per-lane offsets, per-chunk strides
   const uint32_t sQK = (uint32_t)op_rows * DK, sA = (uint32_t)HV * BT, sV = (uint32_t)HV * V,
-                 sG = (uint32_t)HV;
+                 sG = 1;
   // loader: token group varies fastest across lanes, so the transposed
   // writes of a half-wave cover one contiguous 128-byte row segment
   const int tg = tid % C::TG, cg = tid / C::TG;
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
   St_.ai = Ainv + (size_t)bos * sA + (size_t)j * BT;
   St_.aq = Aqk + (size_t)bos * sA + (size_t)j * BT;
   St_.v = v + (size_t)bos * sV + (size_t)j * V + v0;
-  St_.gf = GF + (size_t)bos * sG + j;
+  St_.gf = GF + (size_t)j * ttot + bos;
   St_.dg = DG ? DG + ((size_t)chunk0 * HV + j) * DK : nullptr;
   St_.oA = (uint32_t)(16 * w + row) * sQK + 8 * grp;
   St_.oAi = (uint32_t)(16 * w + row) * sA + 8 * grp;
@@ -528,7 +528,7 @@ hipError_t launch_scan_c(const ChunkArgs& a, const ScanArgs& sa, hipStream_t s) 
                      (const OPT*)sa.x, (const OPT*)sa.op, (const OPT*)sa.t, sa.op_rows,
                      sa.op_head_div, (const IOT*)a.v, (const float4*)a.GF, sa.dg, a.scale, a.h0,
                      a.ht, (const P*)a.Ainv, (const P*)a.Aqk, (IOT*)a.o, a.cu_seqlens, sa.coff,
-                     a.seq_order, a.T, sa.NT, a.N, a.HV, a.V);
+                     a.seq_order, a.T, a.B * a.T, sa.NT, a.N, a.HV, a.V);
   return hipGetLastError();
 }
 
@@ -542,10 +542,7 @@ hipError_t launch_scan_gdn(const ChunkArgs& a, hipStream_t s) {
   sa.dg = nullptr;
   sa.coff = nullptr;
   sa.NT = (a.T + BT - 1) / BT;
-  if (a.bf16) {
-    if (a.K == 128) return launch_scan_c<ScanCfg<bf16_t, bf16_t, 128, 16, false>>(a, sa, s);
-    return launch_scan_c<ScanCfg<bf16_t, bf16_t, 64, 16, false>>(a, sa, s);
-  }
+  if (a.bf16) return launch_scan_gdn_bf16(a, s);
   if (a.K == 128) return launch_scan_c<ScanCfg<float, float, 128, 16, false>>(a, sa, s);
   return launch_scan_c<ScanCfg<float, float, 64, 16, false>>(a, sa, s);
 }

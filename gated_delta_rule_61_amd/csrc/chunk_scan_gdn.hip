@@ -1,0 +1,608 @@
+// Sequential part of the chunked prefill for bf16 io with the scalar gate,
+// gfx950.  The mathematics is the one of the generic scan: per (sequence,
+// v-head, V-tile), over the chunks in order, with S^T (K x BV, fp32) the state
+// at the chunk start and Ainv, Aqk, G from the intra kernel,
+//
+//   X     = diag(e^G) K S^T
+//   R     = beta * (V - X)
+//   Vn    = Ainv R                               (u - w h)
+//   O     = scale diag(e^G) Q S^T + Aqk Vn
+//   S^T  <- e^{G_last} S^T + K^T diag(e^{G_last - G}) Vn
+//
+// ("fla ops/common/chunk_h.py", chunk_fwd_kernel_h: sequential chunk loop,
+// fp32 state, h *= exp(g_last), v scaled by exp(g_last - g); "sglang
+// srt/layers/attention/fla/chunk_fwd.py": the intra-chunk matrices consumed by
+// recompute_w_u and the output step.)
+//
+// gfx950 design.  Work-group = one (sequence, v-head, 32-column V tile), eight
+// waves, two per SIMD:
+//   * two state waves, one per 16-column block, keep their S^T (K x 16) in
+//     fp32 MFMA accumulators and run the chain of a chunk,
+//       X = K S^T  ->  R  ->  Vn = Ainv R  ->  S^T update,
+//     without an LDS round trip of their own.  An accumulator lane holds
+//     column l % 16 at rows 4 (l / 16) + i; two accumulators give a lane the
+//     8 reduction slots of a 32-deep B operand.  The rows of the A operands
+//     (tokens of K / Ainv, channels of K^T) are placed so that accumulator
+//     pair (2s, 2s + 1) covers exactly reduction slots 32s + 8 (l / 16) + e in
+//     natural order: block 2s + h, row 4a + b  <->  index 32s + 8a + 4h + b.
+//     S, R and Vn so become B operands in registers, and every A fragment is
+//     one 16-byte LDS read;
+//   * the K^T operand of the state update comes from the same k tile through
+//     gfx950's transposing LDS read (ds_read_b64_tr_b16);
+//   * two helper waves compute O (no later step of the chunk needs it) from
+//     the S and Vn fragments the state waves publish in LDS;
+//   * four mover waves (the second wave on each SIMD) move the data: the next
+//     chunk's q / k / Ainv / Aqk / v / gate rows go from global memory to LDS
+//     with direct-to-LDS loads (global_load_lds_dwordx4, whole rows, no
+//     registers), double buffered; a wave keeps only a few such loads in
+//     flight, so four issuing waves move about twice what two do.  The lines
+//     of the chunk after next are pulled into L2 ahead of them; O leaves
+//     through LDS as 16-byte row stores;
+//   * q / k and Ainv / Aqk tiles are stored with a 16-byte-unit XOR swizzle so
+//     that the fragment reads and the transposing reads hit distinct banks;
+//   * the raw bf16 q / k enter the products exactly; S enters Q S^T and
+//     diag(e^{G_last - G}) Vn the state update as hi + lo bf16 pairs (about 16
+//     significant bits); K S^T takes S rounded to bf16 (its error enters R
+//     below R's own fp16 rounding); the 64 x 64 products (Ainv R, Aqk Vn) run
+//     in fp16;
+//   * two barriers per chunk; the work-groups of one (sequence, head) share an
+//     XCD (its L2), sequences are issued longest first.
+
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int BT = 64;     // chunk length
+constexpr int BV = 32;     // V columns per work-group
+constexpr int NSW = 2;     // state waves (= helper waves)
+constexpr int NMV = 4;     // mover waves
+constexpr int NTHR = 64 * (2 * NSW + NMV);
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lchar;  // LDS byte pointer
+
+// compile-time stage selectors of the double-buffered chunk inputs
+struct Stage0 { static constexpr bool value = false; };
+struct Stage1 { static constexpr bool value = true; };
+
+// compile-time loop: f(Int<I>{}) for I = 0 .. N - 1
+template <int I> struct Int { static constexpr int value = I; };
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Row (token or channel) of block `blk`, row r of a 16-row MFMA tile.
+__device__ __forceinline__ int perm_row(int blk, int r) {
+  return 32 * (blk >> 1) + 8 * (r >> 2) + 4 * (blk & 1) + (r & 3);
+}
+// perm_row(blk, r) - perm_row(0, r)
+__device__ __forceinline__ constexpr int blk_rows(int blk) { return 32 * (blk >> 1) + 4 * (blk & 1); }
+
+// 16-byte-unit XOR swizzles of the q / k tiles (rows of 2 DK bytes) and the
+// Ainv / Aqk tiles (rows of 128 bytes).  Bank-conflict free for (a) the row
+// fragment reads, 16 rows perm_row(blk, 0..15) at one unit, and (b) the
+// transposing reads of K^T, rows t0 + {0..3} at units u0 + {0..3}.
+template <int DK>
+__device__ __forceinline__ int qk_swz(int t) {
+  if constexpr (DK == 128) return ((t & 3) << 2) | ((t >> 3) & 3);
+  else return (((t >> 1) & 1) << 2) | ((t >> 3) & 3);
+}
+__device__ __forceinline__ int a_swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 3) & 3); }
+
+// byte offset of 16-byte unit u of row t
+template <int DK>
+__device__ __forceinline__ int qk_off(int t, int u) {
+  return t * (2 * DK) + ((u ^ qk_swz<DK>(t)) << 4);
+}
+__device__ __forceinline__ int a_off(int t, int u) { return t * 128 + ((u ^ a_swz(t)) << 4); }
+
+// select by value (a conditional over two captured lvalues would select their
+// addresses and keep the lambda's captures in memory)
+template <typename T>
+__device__ __forceinline__ T pick(bool c, T a, T b) { return c ? a : b; }
+
+__device__ __forceinline__ u32x4 ld16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// LDS transpose read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
+// receives element i % 4 of the 4-element (8-byte) rows addressed by lanes
+// i / 4 + 4k, k = 0..3.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ld_tr(const char* p) {
+  typedef __attribute__((address_space(3))) v4i16 lv4i16;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4i16*)p));
+}
+
+// Work-group barrier ordering LDS only: this wave's LDS writes have completed
+// (lgkmcnt) before the barrier.  Unlike __syncthreads() it does not wait for
+// the direct-to-LDS loads in flight, which the wave that issued them waits for
+// before the barrier that publishes their data.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ f32x4 mma_bf(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_h(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two accumulators -> one B fragment (slots 0..3 from `a`, 4..7 from `b`),
+// as a bf16 hi + lo pair (x ~= hi + lo).
+__device__ __forceinline__ void split_bf(f32x4 a, f32x4 b, u32x4& hi, u32x4& lo) {
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t h = pack_bf2(x[2 * p], x[2 * p + 1]);
+    hi[p] = h;
+    lo[p] = pack_bf2(x[2 * p] - __builtin_bit_cast(float, h << 16),
+                     x[2 * p + 1] - __builtin_bit_cast(float, h & 0xFFFF0000u));
+  }
+}
+// ... as fp16 (saturating)
+__device__ __forceinline__ u32x4 pack_h(f32x4 a, f32x4 b) {
+  return u32x4{pack2<f16_t>(a[0], a[1]), pack2<f16_t>(a[2], a[3]), pack2<f16_t>(b[0], b[1]),
+               pack2<f16_t>(b[2], b[3])};
+}
+
+// 16 bytes per lane, global -> LDS; lane l's bytes land at lds + 16 l
+__device__ __forceinline__ void dma16(const void* src, lchar* lds) {
+  typedef __attribute__((address_space(1))) const void gvoid;
+  __builtin_amdgcn_global_load_lds((gvoid*)src, lds, 16, 0, 0);
+}
+// one dword per lane into a landing area nobody reads: pulls the line into L2
+__device__ __forceinline__ void touch4(const void* src, lchar* sink) {
+  typedef __attribute__((address_space(1))) const void gvoid;
+  __builtin_amdgcn_global_load_lds((gvoid*)src, sink, 4, 0, 0);
+}
+
+// vector-memory operations a helper leaves in flight across the chunk's last
+// barrier: the L2 prefetch loads issued after the chunk's data loads
+constexpr int kTouches = 2;
+
+template <int DK>
+struct Lds {
+  static constexpr int QK = BT * DK * 2;        // one q or k tile (bytes)
+  static constexpr int AT = BT * BT * 2;        // one Ainv or Aqk tile (fp16)
+  static constexpr int VT = BT * BV * 2;        // v tile
+  static constexpr int OROW = BV * 2 + 16;      // padded o row (bytes)
+  static constexpr int KS = DK / 32, KB = DK / 16;
+  static constexpr int NQK = DK / 8;            // 1 KB loads per q / k tile
+  static constexpr int QROWS = 512 / DK;        // q / k rows per 1 KB load
+};
+
+template <int DK>
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_scan_bf16_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float4* __restrict__ GF, const f16_t* __restrict__ Ainv, const f16_t* __restrict__ Aqk,
+    float scale, const float* __restrict__ h0, float* __restrict__ ht, bf16_t* __restrict__ o,
+    const int64_t* __restrict__ cu, const int32_t* __restrict__ order, int Tlen, int ttot, int N,
+    int Hk, int HV, int V) {
+  typedef Lds<DK> L;
+  constexpr int KS = L::KS, KB = L::KB, NQK = L::NQK;
+  // two stages of the chunk inputs, separate arrays so that the compiler can
+  // tell the stage being filled from the one being read
+  __shared__ __attribute__((aligned(16))) char sK0[L::QK], sK1[L::QK], sQ0[L::QK], sQ1[L::QK];
+  __shared__ __attribute__((aligned(16))) char sAi0[L::AT], sAi1[L::AT], sAq0[L::AT], sAq1[L::AT];
+  __shared__ __attribute__((aligned(16))) char sV0[L::VT], sV1[L::VT];
+  __shared__ __attribute__((aligned(16))) float4 sG0[BT], sG1[BT];
+  __shared__ __attribute__((aligned(16))) u32x4 sSF[NSW][KS][2][64];  // S fragments (fp32)
+  __shared__ __attribute__((aligned(16))) u32x4 sVnF[NSW][2][64];     // Vn fragments (fp16)
+  __shared__ __attribute__((aligned(16))) char sO[BT * L::OROW];       // o tile
+  __shared__ __attribute__((aligned(16))) uint32_t sSink[64];          // L2-prefetch landing words
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool is_state = w < NSW;
+  const int cb = w % NSW;                 // 16-column block (state, helper)
+  const int n = lane & 15, g = lane >> 4;
+  const int NVT = V / BV;
+
+  // ---- work-group -> (sequence, head, V-tile): the NVT tiles of a (sequence,
+  // head) stay on one XCD, groups in order of decreasing sequence length
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, pos = bid >> 3;
+  const int vt = pos % NVT;
+  const int grpi = (pos / NVT) * 8 + xcd;
+  if (grpi >= N * HV) return;
+  const int rank = grpi / HV, j = grpi - rank * HV;
+  const int ns = order ? order[rank] : rank;
+  int bos, eos;
+  if (cu) {
+    long long b0 = cu[ns], b1 = cu[ns + 1];
+    b0 = b0 < 0 ? 0 : (b0 > Tlen ? Tlen : b0);
+    b1 = b1 < b0 ? b0 : (b1 > Tlen ? Tlen : b1);
+    bos = (int)b0;
+    eos = (int)b1;
+  } else {
+    bos = ns * Tlen;
+    eos = bos + Tlen;
+  }
+  const int jo = j / (HV / Hk);
+  const int v0 = vt * BV;
+  const int NC = (eos - bos + BT - 1) / BT;
+  const size_t hbase = ((size_t)ns * HV + j) * (size_t)V * DK;
+  const uint32_t qk_row = (uint32_t)Hk * DK * 2, a_row = (uint32_t)HV * BT * 2,
+                 v_row = (uint32_t)HV * V * 2;
+
+  if (is_state) {
+    // =================== state wave: the recurrence of 16 columns
+    // S^T blocks: block kb, lane: channels perm_row(kb, 4g + i), column 16cb + n
+    f32x4 St[KB];
+    u32x4 Sh[KS];   // S rounded to bf16, B operand of X = K S^T
+    // publish S (fp32, fragment order) for the output; keep its bf16 rounding
+    auto publish_s = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        sSF[cb][s][0][lane] = __builtin_bit_cast(u32x4, St[2 * s]);
+        sSF[cb][s][1][lane] = __builtin_bit_cast(u32x4, St[2 * s + 1]);
+        const f32x4 a = St[2 * s], b = St[2 * s + 1];
+        Sh[s] = u32x4{pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(b[0], b[1]),
+                      pack_bf2(b[2], b[3])};
+      }
+    };
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (h0) {
+        const float4 x = *reinterpret_cast<const float4*>(
+            h0 + hbase + (size_t)(v0 + 16 * cb + n) * DK + perm_row(kb, 4 * g));
+        St[kb] = f32x4{x.x, x.y, x.z, x.w};
+      } else {
+        St[kb] = zero4();
+      }
+    }
+    publish_s();
+    __syncthreads();
+
+    // per-lane LDS byte offsets, the same in every chunk.  The swizzle of row
+    // perm_row(blk, n) does not depend on blk, so a tile block adds
+    // blk_rows(blk) whole rows to the offsets of block 0.
+    int o_kf[KS];                 // K row fragments, slab s
+#pragma unroll
+    for (int s = 0; s < KS; ++s) o_kf[s] = qk_off<DK>(perm_row(0, n), 4 * s + g);
+    const int o_ai0 = a_off(perm_row(0, n), g), o_ai1 = a_off(perm_row(0, n), 4 + g);
+    int o_tr[KB / 2][2][2];       // K^T transposing reads [kb / 2][slab][token half]
+#pragma unroll
+    for (int kh = 0; kh < KB / 2; ++kh)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          o_tr[kh][s][h] = qk_off<DK>(32 * s + 8 * g + (n >> 2) + 4 * h, 4 * kh + (n & 3));
+
+    auto chunk = [&](auto stg, int c) __attribute__((always_inline)) {
+      constexpr bool S1 = decltype(stg)::value;
+      const char* sK = S1 ? sK1 : sK0;
+      const char* sAi = S1 ? sAi1 : sAi0;
+      const bf16_t* sV = reinterpret_cast<const bf16_t*>(S1 ? sV1 : sV0);
+      const float4* sG = S1 ? sG1 : sG0;
+      const int nrow = eos - (bos + c * BT) < BT ? eos - (bos + c * BT) : BT;
+
+      // ---- K^T fragments of the state update, read first (they depend on the
+      // k tile only): lane (n, g) of block kb holds channel perm_row(kb, n)
+      // of tokens 32s + 8g + e, e = 0..7, the slot order of Vt.  Two
+      // transposing reads each: this lane addresses channels
+      // perm_row(kb, 4 (n % 4)) .. + 3 of token 32s + 8g + n / 4 (+ 4).
+      u32x4 Kt[KB][2];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const uint2 lo = ld_tr(sK + o_tr[kb >> 1][s][0] + 8 * (kb & 1));
+          const uint2 hi = ld_tr(sK + o_tr[kb >> 1][s][1] + 8 * (kb & 1));
+          Kt[kb][s] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+      // ---- X = K S^T with S rounded to bf16 (its rounding error enters R
+      // below the fp16 rounding of R itself); block tb, lane: tokens
+      // perm_row(tb, 4g + i)
+      u32x4 A[KS][4];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) A[s][tb] = ld16(sK + o_kf[s] + blk_rows(tb) * (2 * DK));
+      f32x4 X[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) X[tb] = zero4();
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) X[tb] = mma_bf(A[s][tb], Sh[s], X[tb]);
+      // ---- R = beta (v - e^G X); rows past the end are zero
+      f32x4 R[4], eGt[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = perm_row(tb, 4 * g + i);
+          const float4 gf = sG[t];
+          const float vv = bf2f(sV[t * BV + 16 * cb + n]);
+          R[tb][i] = gf.z * (vv - gf.x * X[tb][i]);
+          eGt[tb][i] = gf.y;
+        }
+      if (nrow < BT) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = perm_row(tb, 4 * g + i) < nrow;
+            R[tb][i] = ok ? R[tb][i] : 0.f;
+            eGt[tb][i] = ok ? eGt[tb][i] : 0.f;
+          }
+      }
+      const u32x4 Rf0 = pack_h(R[0], R[1]), Rf1 = pack_h(R[2], R[3]);
+      // ---- Vn = Ainv R (block lower triangular in 32-token slabs)
+      u32x4 Ai[6];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) Ai[tb] = ld16(sAi + o_ai0 + blk_rows(tb) * 128);
+      Ai[4] = ld16(sAi + o_ai1 + blk_rows(2) * 128);
+      Ai[5] = ld16(sAi + o_ai1 + blk_rows(3) * 128);
+      f32x4 Vn[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) Vn[tb] = mma_h(Ai[tb], Rf0, zero4());
+      Vn[2] = mma_h(Ai[4], Rf1, Vn[2]);
+      Vn[3] = mma_h(Ai[5], Rf1, Vn[3]);
+      // publish Vn for the output; Vt = diag(e^{G_last - G}) Vn (zero past the end)
+      sVnF[cb][0][lane] = pack_h(Vn[0], Vn[1]);
+      sVnF[cb][1][lane] = pack_h(Vn[2], Vn[3]);
+      u32x4 Vh[2], Vl[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        split_bf(Vn[2 * s] * eGt[2 * s], Vn[2 * s + 1] * eGt[2 * s + 1], Vh[s], Vl[s]);
+      const float eGl = sG[0].w;
+      lds_barrier();
+
+      // ---- S^T <- e^{G_last} S^T + K^T Vt
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) St[kb] = St[kb] * eGl;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) St[kb] = mma_bf(Kt[kb][s], Vh[s], St[kb]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) St[kb] = mma_bf(Kt[kb][s], Vl[s], St[kb]);
+      }
+      publish_s();
+      lds_barrier();
+    };
+    for (int c = 0; c < NC; c += 2) {
+      chunk(Stage0{}, c);
+      if (c + 1 < NC) chunk(Stage1{}, c + 1);
+    }
+    if (ht) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        *reinterpret_cast<float4*>(ht + hbase + (size_t)(v0 + 16 * cb + n) * DK + perm_row(kb, 4 * g)) =
+            make_float4(St[kb][0], St[kb][1], St[kb][2], St[kb][3]);
+    }
+  } else if (w < 2 * NSW) {
+    // =================== helper wave: the output of 16 columns
+    __syncthreads();
+    auto chunk = [&](auto stg, int c) __attribute__((always_inline)) {
+      constexpr bool S1 = decltype(stg)::value;
+      const char* sQ = S1 ? sQ1 : sQ0;
+      const char* sAq = S1 ? sAq1 : sAq0;
+      const float4* sG = S1 ? sG1 : sG0;
+      // ---- Oi = Q S^T from the published fp32 S (split into bf16 hi + lo)
+      f32x4 Oi[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) Oi[tb] = zero4();
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        u32x4 bh, bl;
+        split_bf(__builtin_bit_cast(f32x4, sSF[cb][s][0][lane]),
+                 __builtin_bit_cast(f32x4, sSF[cb][s][1][lane]), bh, bl);
+        u32x4 A[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) A[tb] = ld16(sQ + qk_off<DK>(perm_row(tb, n), 4 * s + g));
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) Oi[tb] = mma_bf(A[tb], bh, Oi[tb]);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) Oi[tb] = mma_bf(A[tb], bl, Oi[tb]);
+      }
+      lds_barrier();
+
+      // ---- O = scale e^G Oi + Aqk Vn -> LDS tile
+      const u32x4 vf0 = sVnF[cb][0][lane], vf1 = sVnF[cb][1][lane];
+      u32x4 Aq[6];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) Aq[tb] = ld16(sAq + a_off(perm_row(tb, n), g));
+      Aq[4] = ld16(sAq + a_off(perm_row(2, n), 4 + g));
+      Aq[5] = ld16(sAq + a_off(perm_row(3, n), 4 + g));
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = Oi[tb][i] * (scale * sG[perm_row(tb, 4 * g + i)].x);
+        acc = mma_h(Aq[tb], vf0, acc);
+        if (tb >= 2) acc = mma_h(Aq[tb + 2], vf1, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<bf16_t*>(sO + perm_row(tb, 4 * g + i) * L::OROW + 2 * (16 * cb + n)) =
+              f2bf(acc[i]);
+      }
+      lds_barrier();
+    };
+    for (int c = 0; c < NC; c += 2) {
+      chunk(Stage0{}, c);
+      if (c + 1 < NC) chunk(Stage1{}, c + 1);
+    }
+  } else {
+    // =================== mover wave: global <-> LDS traffic
+    // Mover 0 loads k, 1 q, 2 Ainv and v, 3 Aqk and the gate rows, with
+    // direct-to-LDS loads into the stage of the next chunk; each stores a
+    // quarter of the o tile.
+    const int mv = w - 2 * NSW;
+    // per-lane byte offsets within a full chunk: LDS slot (row, unit')
+    // receives global unit unit' ^ swizzle(row)
+    uint32_t o_qk[NQK], o_a[8], o_v[4];
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const int row = i * L::QROWS + lane / (DK / 8);
+      o_qk[i] = (uint32_t)row * qk_row + 16 * ((lane % (DK / 8)) ^ qk_swz<DK>(row));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * i + lane / 8;
+      o_a[i] = (uint32_t)row * a_row + 16 * ((lane % 8) ^ a_swz(row));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o_v[i] = (uint32_t)(16 * i + lane / 4) * v_row + 16 * (lane % 4);
+    const bf16_t* xsrc = pick(mv == 0, k, q);         // movers 0, 1
+    const f16_t* asrc = pick(mv == 2, Ainv, Aqk);     // movers 2, 3
+
+    // loads of the chunk at token c0 into the given stage; in the last chunk
+    // of a sequence, rows past its end repeat its last row (masked later)
+    auto dma_chunk = [&](int c0, lchar* dK, lchar* dQ, lchar* dAi, lchar* dAq, lchar* dV, lchar* dG)
+        __attribute__((always_inline)) {
+      const int nr = eos - c0 < BT ? eos - c0 : BT;
+      if (mv < 2) {
+        lchar* dX = mv == 0 ? dK : dQ;
+        const char* xc = reinterpret_cast<const char*>(xsrc + ((size_t)c0 * Hk + jo) * DK);
+        if (nr == BT) {
+#pragma unroll
+          for (int i = 0; i < NQK; ++i) dma16(xc + o_qk[i], dX + 1024 * i);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NQK; ++i) {
+            const int row = i * L::QROWS + lane / (DK / 8);
+            const int rr = row < nr ? row : nr - 1;
+            dma16(xc + (uint32_t)rr * qk_row + 16 * ((lane % (DK / 8)) ^ qk_swz<DK>(row)), dX + 1024 * i);
+          }
+        }
+      } else {
+        lchar* dA = mv == 2 ? dAi : dAq;
+        const char* ac = reinterpret_cast<const char*>(asrc + ((size_t)c0 * HV + j) * BT);
+        if (nr == BT) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dma16(ac + o_a[i], dA + 1024 * i);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int row = 8 * i + lane / 8;
+            const int rr = row < nr ? row : nr - 1;
+            dma16(ac + (uint32_t)rr * a_row + 16 * ((lane % 8) ^ a_swz(row)), dA + 1024 * i);
+          }
+        }
+        if (mv == 2) {
+          const char* vc = reinterpret_cast<const char*>(v + ((size_t)c0 * HV + j) * V + v0);
+          if (nr == BT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dma16(vc + o_v[i], dV + 1024 * i);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = 16 * i + lane / 4;
+              const int rr = row < nr ? row : nr - 1;
+              dma16(vc + (uint32_t)rr * v_row + 16 * (lane % 4), dV + 1024 * i);
+            }
+          }
+        } else {
+          const int rr = lane < nr ? lane : nr - 1;
+          dma16(GF + (size_t)j * ttot + c0 + rr, dG);
+        }
+      }
+    };
+
+    // pull the lines of the chunk at token c0 into L2 ahead of its
+    // direct-to-LDS loads.  The head's q / k / Ainv / Aqk lines are cut into
+    // 64-line pieces, one per (work-group, mover) of the head (the others
+    // repeat one); movers 2 also take the lines of their v slice, movers 0,
+    // 1, 3 the gate rows.  Exactly kTouches instructions per mover.
+    auto touch_chunk = [&](int c0) __attribute__((always_inline)) {
+      const int nr = eos - c0 < BT ? eos - c0 : BT;
+      lchar* sink = (lchar*)sSink;
+      constexpr int QKP = DK / 64;               // 64-line pieces per q or k tile
+      const int piece = (NMV * vt + mv) % (2 * QKP + 2);
+      const char* p;
+      if (piece < 2 * QKP) {
+        const bf16_t* x = pick(piece < QKP, q, k);
+        const int row0 = (piece % QKP) * (64 / QKP) + lane / QKP;
+        const int row = row0 < nr ? row0 : nr - 1;
+        p = reinterpret_cast<const char*>(x + ((size_t)(c0 + row) * Hk + jo) * DK) + 128 * (lane % QKP);
+      } else {
+        const int row = lane < nr ? lane : nr - 1;
+        p = reinterpret_cast<const char*>(pick(piece == 2 * QKP, Ainv, Aqk) +
+                                          ((size_t)(c0 + row) * HV + j) * BT);
+      }
+      touch4(p, sink);
+      const int rr = lane < nr ? lane : nr - 1;
+      if (mv == 2) touch4(v + ((size_t)(c0 + rr) * HV + j) * V + v0, sink);
+      else touch4(reinterpret_cast<const char*>(GF + (size_t)j * ttot + c0) + 128 * (lane & 7), sink);
+    };
+
+    // a quarter of the o rows of the chunk at token c0, from the LDS tile
+    auto store_o = [&](int c0) __attribute__((always_inline)) {
+      const int nr = eos - c0 < BT ? eos - c0 : BT;
+      const int qq = mv * 64 + lane;
+      const int row = qq / (BV / 8), u = qq % (BV / 8);
+      if (row < nr)
+        *reinterpret_cast<uint4*>(o + ((size_t)(c0 + row) * HV + j) * V + v0 + 8 * u) =
+            *reinterpret_cast<const uint4*>(sO + row * L::OROW + 16 * u);
+    };
+
+    if (NC > 0) {
+      dma_chunk(bos, (lchar*)sK0, (lchar*)sQ0, (lchar*)sAi0, (lchar*)sAq0, (lchar*)sV0, (lchar*)sG0);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    auto chunk = [&](auto stg, int c) __attribute__((always_inline)) {
+      constexpr bool S1 = decltype(stg)::value;
+      const int c0 = bos + c * BT;
+      if (c > 0) store_o(c0 - BT);
+      if (c + 1 < NC) {
+        if constexpr (S1)
+          dma_chunk(c0 + BT, (lchar*)sK0, (lchar*)sQ0, (lchar*)sAi0, (lchar*)sAq0, (lchar*)sV0, (lchar*)sG0);
+        else
+          dma_chunk(c0 + BT, (lchar*)sK1, (lchar*)sQ1, (lchar*)sAi1, (lchar*)sAq1, (lchar*)sV1, (lchar*)sG1);
+      }
+      if (c + 2 < NC) touch_chunk(c0 + 2 * BT);
+      lds_barrier();
+      // this mover's loads of the next chunk (and its o store) are done;
+      // vector-memory operations complete in issue order, so the L2 prefetch
+      // loads issued after them may stay in flight
+      if (c + 2 < NC) {
+        static_assert(kTouches == 2, "vmcnt below");
+        __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2) expcnt(7) lgkmcnt(15)
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      lds_barrier();
+    };
+    for (int c = 0; c < NC; c += 2) {
+      chunk(Stage0{}, c);
+      if (c + 1 < NC) chunk(Stage1{}, c + 1);
+    }
+    if (NC > 0) store_o(bos + (NC - 1) * BT);
+  }
+}
+
+template <int DK>
+hipError_t launch_dk(const ChunkArgs& a, hipStream_t s) {
+  const int nvt = a.V / BV;
+  const int groups = a.N * a.HV;
+  const int nblk = ((groups + 7) / 8) * 8 * nvt;
+  hipLaunchKernelGGL((gdn_scan_bf16_kernel<DK>), dim3((unsigned)nblk), dim3(NTHR), 0, s,
+                     (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
+                     (const float4*)a.GF, (const f16_t*)a.Ainv, (const f16_t*)a.Aqk, a.scale, a.h0,
+                     a.ht, (bf16_t*)a.o, a.cu_seqlens, a.seq_order, a.T, a.B * a.T, a.N, a.Hk,
+                     a.HV, a.V);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan_gdn_bf16(const ChunkArgs& a, hipStream_t s) {
+  if (a.K == 128) return launch_dk<128>(a, s);
+  return launch_dk<64>(a, s);
+}
+
+}  // namespace gdn

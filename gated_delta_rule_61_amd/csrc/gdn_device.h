@@ -34,8 +34,13 @@ __device__ __forceinline__ float bf2f(bf16_t h) {
 __device__ __forceinline__ bf16_t f2bf(float x) {
   return __builtin_bit_cast(bf16_t, (__bf16)x);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two floats -> two round-to-nearest-even bf16 in one word (lo first): one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // ------------------------------------------------------- 16-lane reductions
@@ -148,11 +153,18 @@ template <typename T> struct ComputeOf;
 template <> struct ComputeOf<bf16_t> { typedef f16_t type; };
 template <> struct ComputeOf<float> { typedef float type; };
 
-// Two floats -> two 16-bit values of type T packed in a word (lo first).
+// Two floats -> two 16-bit values of type T packed in a word (lo first),
+// one packed conversion (fp16 saturating as from_f).
 template <typename T>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, from_f<T>(lo)) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, from_f<T>(hi)) << 16);
+__device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <>
+__device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi) { return pack_bf2(lo, hi); }
+template <>
+__device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) {
+  return __builtin_bit_cast(
+      uint32_t, __builtin_convertvector(f32x2_t{__builtin_amdgcn_fmed3f(lo, -65504.0f, 65504.0f),
+                                                __builtin_amdgcn_fmed3f(hi, -65504.0f, 65504.0f)},
+                                        f16x2_t));
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
