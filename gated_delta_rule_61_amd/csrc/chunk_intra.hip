@@ -46,7 +46,7 @@ template <typename T, int DK, typename C = typename ComputeOf<T>::type>
 __global__ __launch_bounds__(64) void gdn_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, C* __restrict__ Ainv,
-    C* __restrict__ Aqk, float4* __restrict__ GF, const int64_t* __restrict__ cu,
+    C* __restrict__ Aqk, float* __restrict__ GF, const int64_t* __restrict__ cu,
     const int32_t* __restrict__ coff, int Tlen, int ttot, int N, int NT, int Hk, int HV) {
   __shared__ __attribute__((aligned(16))) float sA[BT][AP];
   const int lane = threadIdx.x;
@@ -63,8 +63,14 @@ __global__ __launch_bounds__(64) void gdn_intra_kernel(
   // per-token gate factors for the scan: e^G, e^{G_last - G}, beta, e^{G_last}
   {
     const float Gl = __shfl(G, nrow - 1, 64);
-    if (lane < nrow)
-      GF[(size_t)j * ttot + c0 + lane] = make_float4(__expf(G), __expf(Gl - G), bl, __expf(Gl));
+    if (lane < nrow) {
+      const size_t gs = (size_t)gf_stride(ttot);
+      float* gp = GF + (size_t)j * 4 * gs + c0 + lane;
+      gp[0] = __expf(G);
+      gp[gs] = __expf(Gl - G);
+      gp[2 * gs] = bl;
+      gp[3 * gs] = __expf(Gl);
+    }
   }
 
   // Step 1: ten lower blocks of K K^T and Q K^T
@@ -152,23 +158,23 @@ hipError_t launch_intra_gdn(const ChunkArgs& a, hipStream_t s, int NT, int nslot
     if (a.K == 128)
       hipLaunchKernelGGL((gdn_intra_kernel<bf16_t, 128>), grid, dim3(64), 0, s,
                          (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, a.scale,
-                         (f16_t*)a.Ainv, (f16_t*)a.Aqk, (float4*)a.GF, a.cu_seqlens, a.chunk_off,
+                         (f16_t*)a.Ainv, (f16_t*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
                          a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
     else
       hipLaunchKernelGGL((gdn_intra_kernel<bf16_t, 64>), grid, dim3(64), 0, s,
                          (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, a.scale,
-                         (f16_t*)a.Ainv, (f16_t*)a.Aqk, (float4*)a.GF, a.cu_seqlens, a.chunk_off,
+                         (f16_t*)a.Ainv, (f16_t*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
                          a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
   } else {
     if (a.K == 128)
       hipLaunchKernelGGL((gdn_intra_kernel<float, 128>), grid, dim3(64), 0, s,
                          (const float*)a.q, (const float*)a.k, a.g, a.beta, a.scale,
-                         (float*)a.Ainv, (float*)a.Aqk, (float4*)a.GF, a.cu_seqlens, a.chunk_off,
+                         (float*)a.Ainv, (float*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
                          a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
     else
       hipLaunchKernelGGL((gdn_intra_kernel<float, 64>), grid, dim3(64), 0, s,
                          (const float*)a.q, (const float*)a.k, a.g, a.beta, a.scale,
-                         (float*)a.Ainv, (float*)a.Aqk, (float4*)a.GF, a.cu_seqlens, a.chunk_off,
+                         (float*)a.Ainv, (float*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
                          a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
   }
   return hipGetLastError();

@@ -190,7 +190,8 @@ struct ScanStreams {
   const OPT *x, *op, *t;                    // X operand, O operand, update operand (row-major)
   const typename C::IOT* v;
   const P *ai, *aq;
-  const float4* gf;
+  const float* gf;                          // gate-factor plane 0 at the chunk
+  uint32_t gs;                              // plane stride (floats)
   const float* dg;                          // KDA decay rows of the chunk
   uint32_t oA, oAi, oV[4], oG[4], oK[4], oD;  // element offsets within the chunk
 };
@@ -206,7 +207,7 @@ __device__ __forceinline__ void load_chunk(ScanRegs<C>& R, const ScanStreams<C>&
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) R.dg[rb] = *reinterpret_cast<const float4*>(S.dg + S.oD + 16 * rb);
   } else {
-    R.eGl = S.gf[0].w;  // row 0 of the chunk is always valid
+    R.eGl = S.gf[3 * S.gs];  // row 0 of the chunk is always valid
   }
   if (nrow == BT) {
 #pragma unroll
@@ -224,7 +225,7 @@ __device__ __forceinline__ void load_chunk(ScanRegs<C>& R, const ScanStreams<C>&
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int cb = 0; cb < C::CB; ++cb) R.vv[cb][i] = S.v[S.oV[i] + 16 * cb];
-      R.gf[i] = S.gf[S.oG[i]];
+      R.gf[i] = make_float4(S.gf[S.oG[i]], S.gf[S.oG[i] + S.gs], S.gf[S.oG[i] + 2 * S.gs], 0.f);
     }
 #pragma unroll
     for (int u = 0; u < C::TPT; ++u) R.kt[u].load(S.t + S.oK[u]);
@@ -253,7 +254,8 @@ __device__ __forceinline__ void load_chunk(ScanRegs<C>& R, const ScanStreams<C>&
     const bool ok = 16 * w + 4 * grp + i < nrow;
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb) R.vv[cb][i] = ok ? S.v[S.oV[i] + 16 * cb] : IOT(0);
-    R.gf[i] = ok ? S.gf[S.oG[i]] : make_float4(0.f, 0.f, 0.f, 0.f);
+    R.gf[i] = ok ? make_float4(S.gf[S.oG[i]], S.gf[S.oG[i] + S.gs], S.gf[S.oG[i] + 2 * S.gs], 0.f)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const int tg = tid % C::TG;
 #pragma unroll
@@ -277,7 +279,7 @@ template <typename C>
 __global__ __launch_bounds__(256) void chunk_scan_kernel(
     const typename C::OPT* __restrict__ xop, const typename C::OPT* __restrict__ oop,
     const typename C::OPT* __restrict__ top, int op_rows, int op_head_div,
-    const typename C::IOT* __restrict__ v, const float4* __restrict__ GF,
+    const typename C::IOT* __restrict__ v, const float* __restrict__ GF,
     const float* __restrict__ DG, float scale, const float* __restrict__ h0,
     float* __restrict__ ht, const typename C::P* __restrict__ Ainv,
     const typename C::P* __restrict__ Aqk, typename C::IOT* __restrict__ o,
@@ -363,7 +365,8 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
   St_.ai = Ainv + (size_t)bos * sA + (size_t)j * BT;
   St_.aq = Aqk + (size_t)bos * sA + (size_t)j * BT;
   St_.v = v + (size_t)bos * sV + (size_t)j * V + v0;
-  St_.gf = GF + (size_t)j * ttot + bos;
+  St_.gs = (uint32_t)gf_stride(ttot);
+  St_.gf = GF + (size_t)j * 4 * St_.gs + bos;
   St_.dg = DG ? DG + ((size_t)chunk0 * HV + j) * DK : nullptr;
   St_.oA = (uint32_t)(16 * w + row) * sQK + 8 * grp;
   St_.oAi = (uint32_t)(16 * w + row) * sA + 8 * grp;
@@ -526,7 +529,7 @@ hipError_t launch_scan_c(const ChunkArgs& a, const ScanArgs& sa, hipStream_t s) 
   const int nblk = ((groups + 7) / 8) * 8 * nvt;
   hipLaunchKernelGGL((chunk_scan_kernel<C>), dim3((unsigned)nblk), dim3(256), 0, s,
                      (const OPT*)sa.x, (const OPT*)sa.op, (const OPT*)sa.t, sa.op_rows,
-                     sa.op_head_div, (const IOT*)a.v, (const float4*)a.GF, sa.dg, a.scale, a.h0,
+                     sa.op_head_div, (const IOT*)a.v, (const float*)a.GF, sa.dg, a.scale, a.h0,
                      a.ht, (const P*)a.Ainv, (const P*)a.Aqk, (IOT*)a.o, a.cu_seqlens, sa.coff,
                      a.seq_order, a.T, a.B * a.T, sa.NT, a.N, a.HV, a.V);
   return hipGetLastError();

@@ -159,6 +159,11 @@ __device__ __forceinline__ void dma16(const void* src, lchar* lds) {
   typedef __attribute__((address_space(1))) const void gvoid;
   __builtin_amdgcn_global_load_lds((gvoid*)src, lds, 16, 0, 0);
 }
+// 4 bytes per lane, global -> LDS; lane l's bytes land at lds + 4 l
+__device__ __forceinline__ void dma4(const void* src, lchar* lds) {
+  typedef __attribute__((address_space(1))) const void gvoid;
+  __builtin_amdgcn_global_load_lds((gvoid*)src, lds, 4, 0, 0);
+}
 // one dword per lane into a landing area nobody reads: pulls the line into L2
 __device__ __forceinline__ void touch4(const void* src, lchar* sink) {
   typedef __attribute__((address_space(1))) const void gvoid;
@@ -183,7 +188,7 @@ struct Lds {
 template <int DK>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_scan_bf16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const float4* __restrict__ GF, const f16_t* __restrict__ Ainv, const f16_t* __restrict__ Aqk,
+    const float* __restrict__ GF, const f16_t* __restrict__ Ainv, const f16_t* __restrict__ Aqk,
     float scale, const float* __restrict__ h0, float* __restrict__ ht, bf16_t* __restrict__ o,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ order, int Tlen, int ttot, int N,
     int Hk, int HV, int V) {
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   __shared__ __attribute__((aligned(16))) char sK0[L::QK], sK1[L::QK], sQ0[L::QK], sQ1[L::QK];
   __shared__ __attribute__((aligned(16))) char sAi0[L::AT], sAi1[L::AT], sAq0[L::AT], sAq1[L::AT];
   __shared__ __attribute__((aligned(16))) char sV0[L::VT], sV1[L::VT];
-  __shared__ __attribute__((aligned(16))) float4 sG0[BT], sG1[BT];
+  __shared__ __attribute__((aligned(16))) float sG0[4][BT], sG1[4][BT];  // gate-factor planes
   __shared__ __attribute__((aligned(16))) u32x4 sSF[NSW][KS][2][64];  // S fragments (fp32)
   __shared__ __attribute__((aligned(16))) u32x4 sVnF[NSW][2][64];     // Vn fragments (fp16)
   __shared__ __attribute__((aligned(16))) char sO[BT * L::OROW];       // o tile
@@ -231,6 +236,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   const int v0 = vt * BV;
   const int NC = (eos - bos + BT - 1) / BT;
   const size_t hbase = ((size_t)ns * HV + j) * (size_t)V * DK;
+  const size_t gs = (size_t)gf_stride(ttot);   // gate-factor plane stride
   const uint32_t qk_row = (uint32_t)Hk * DK * 2, a_row = (uint32_t)HV * BT * 2,
                  v_row = (uint32_t)HV * V * 2;
 
@@ -283,8 +289,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       constexpr bool S1 = decltype(stg)::value;
       const char* sK = S1 ? sK1 : sK0;
       const char* sAi = S1 ? sAi1 : sAi0;
-      const bf16_t* sV = reinterpret_cast<const bf16_t*>(S1 ? sV1 : sV0);
-      const float4* sG = S1 ? sG1 : sG0;
+      const char* sV = S1 ? sV1 : sV0;
+      const float (*sG)[BT] = S1 ? sG1 : sG0;
       const int nrow = eos - (bos + c * BT) < BT ? eos - (bos + c * BT) : BT;
 
       // ---- K^T fragments of the state update, read first (they depend on the
@@ -317,17 +323,24 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) X[tb] = mma_bf(A[s][tb], Sh[s], X[tb]);
       // ---- R = beta (v - e^G X); rows past the end are zero
+      // lane's rows of block tb are the 4 consecutive tokens perm_row(tb, 4g) + i:
+      // one 16-byte read per gate plane, one transposing read of the v tile
+      // (this lane addresses columns 16cb + 4 (n % 4) .. + 3 of token
+      // perm_row(tb, 4g + n / 4))
       f32x4 R[4], eGt[4];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb) {
+        const int t0 = perm_row(tb, 4 * g);
+        const f32x4 ex = *reinterpret_cast<const f32x4*>(&sG[0][t0]);
+        const f32x4 ey = *reinterpret_cast<const f32x4*>(&sG[1][t0]);
+        const f32x4 bz = *reinterpret_cast<const f32x4*>(&sG[2][t0]);
+        const uint2 vr = ld_tr(sV + (perm_row(tb, 4 * g + (n >> 2)) * BV + 16 * cb + 4 * (n & 3)) * 2);
+        const float vv[4] = {__builtin_bit_cast(float, vr.x << 16), __builtin_bit_cast(float, vr.x & 0xFFFF0000u),
+                             __builtin_bit_cast(float, vr.y << 16), __builtin_bit_cast(float, vr.y & 0xFFFF0000u)};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = perm_row(tb, 4 * g + i);
-          const float4 gf = sG[t];
-          const float vv = bf2f(sV[t * BV + 16 * cb + n]);
-          R[tb][i] = gf.z * (vv - gf.x * X[tb][i]);
-          eGt[tb][i] = gf.y;
-        }
+        for (int i = 0; i < 4; ++i) R[tb][i] = bz[i] * (vv[i] - ex[i] * X[tb][i]);
+        eGt[tb] = ey;
+      }
       if (nrow < BT) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         split_bf(Vn[2 * s] * eGt[2 * s], Vn[2 * s + 1] * eGt[2 * s + 1], Vh[s], Vl[s]);
-      const float eGl = sG[0].w;
+      const float eGl = sG[3][0];
       lds_barrier();
 
       // ---- S^T <- e^{G_last} S^T + K^T Vt
@@ -390,7 +403,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       constexpr bool S1 = decltype(stg)::value;
       const char* sQ = S1 ? sQ1 : sQ0;
       const char* sAq = S1 ? sAq1 : sAq0;
-      const float4* sG = S1 ? sG1 : sG0;
+      const float (*sG)[BT] = S1 ? sG1 : sG0;
       // ---- Oi = Q S^T from the published fp32 S (split into bf16 hi + lo)
       f32x4 Oi[4];
 #pragma unroll
@@ -419,9 +432,10 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       Aq[5] = ld16(sAq + a_off(perm_row(3, n), 4 + g));
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
+        const f32x4 ex = *reinterpret_cast<const f32x4*>(&sG[0][perm_row(tb, 4 * g)]);
         f32x4 acc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = Oi[tb][i] * (scale * sG[perm_row(tb, 4 * g + i)].x);
+        for (int i = 0; i < 4; ++i) acc[i] = Oi[tb][i] * (scale * ex[i]);
         acc = mma_h(Aq[tb], vf0, acc);
         if (tb >= 2) acc = mma_h(Aq[tb + 2], vf1, acc);
 #pragma unroll
@@ -507,7 +521,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
           }
         } else {
           const int rr = lane < nr ? lane : nr - 1;
-          dma16(GF + (size_t)j * ttot + c0 + rr, dG);
+          const float* gp = GF + (size_t)j * 4 * gs + c0 + rr;
+#pragma unroll
+          for (int pl = 0; pl < 4; ++pl) dma4(gp + pl * gs, dG + 256 * pl);
         }
       }
     };
@@ -536,7 +552,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       touch4(p, sink);
       const int rr = lane < nr ? lane : nr - 1;
       if (mv == 2) touch4(v + ((size_t)(c0 + rr) * HV + j) * V + v0, sink);
-      else touch4(reinterpret_cast<const char*>(GF + (size_t)j * ttot + c0) + 128 * (lane & 7), sink);
+      else touch4(GF + (size_t)j * 4 * gs + (lane >> 1 & 3) * gs + c0 + (nr > 32 ? 32 * (lane & 1) : 0), sink);
     };
 
     // a quarter of the o rows of the chunk at token c0, from the LDS tile
@@ -592,7 +608,7 @@ hipError_t launch_dk(const ChunkArgs& a, hipStream_t s) {
   const int nblk = ((groups + 7) / 8) * 8 * nvt;
   hipLaunchKernelGGL((gdn_scan_bf16_kernel<DK>), dim3((unsigned)nblk), dim3(NTHR), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
-                     (const float4*)a.GF, (const f16_t*)a.Ainv, (const f16_t*)a.Aqk, a.scale, a.h0,
+                     (const float*)a.GF, (const f16_t*)a.Ainv, (const f16_t*)a.Aqk, a.scale, a.h0,
                      a.ht, (bf16_t*)a.o, a.cu_seqlens, a.seq_order, a.T, a.B * a.T, a.N, a.Hk,
                      a.HV, a.V);
   return hipGetLastError();

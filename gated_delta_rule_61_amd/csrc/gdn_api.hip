@@ -181,7 +181,7 @@ ChunkWorkspace chunk_workspace_layout(long long tokens, int HV, int K, int N, in
   w.ainv_off = 0;
   w.aqk_off = up(mat);
   w.gf_off = w.aqk_off + up(mat);
-  w.coff_off = w.gf_off + up((size_t)tokens * HV * 16);
+  w.coff_off = w.gf_off + up((size_t)gf_stride(tokens) * HV * 16);
   w.order_off = w.coff_off + up((size_t)(N + 1) * 4);
   size_t end = w.order_off + up((size_t)(N > 0 ? N : 1) * 4);
   w.qg_off = w.kg_off = w.kt_off = w.dg_off = 0;

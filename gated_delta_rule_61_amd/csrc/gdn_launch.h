@@ -38,12 +38,15 @@ struct ChunkArgs {
   void* o;
   void* Ainv;            // [B*T, HV, 64] compute dtype: (I + A)^-1 rows
   void* Aqk;             // [B*T, HV, 64] compute dtype: scale * gated causal Q K^T rows
-  void* GF;              // [HV, B*T] float4 (head-major): e^G, e^{G_last - G}, beta, e^{G_last}
+  void* GF;              // float [HV][4][B*T]: planes e^G, e^{G_last - G}, beta, e^{G_last}
+                         // per token (head-major)
   int32_t* chunk_off;    // [N + 1] varlen chunk offsets (workspace) or nullptr
   int32_t* seq_order;    // [N] sequences, longest first (workspace) or nullptr
   int max_chunks;        // upper bound of the total chunk count
 };
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t s);
+// Token stride of a gate-factor plane.
+__host__ __device__ inline long long gf_stride(long long tokens) { return tokens; }
 // bf16 GDN scan (direct-to-LDS staging, state / helper waves)
 hipError_t launch_scan_gdn_bf16(const ChunkArgs& a, hipStream_t s);
 

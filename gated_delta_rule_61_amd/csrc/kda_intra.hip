@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ gk,
     const float* __restrict__ beta, float scale, T* __restrict__ Aqk_out,
     T* __restrict__ Akk_out, P* __restrict__ Ainv_ws, P* __restrict__ Aqk_ws,
-    P* __restrict__ qg, P* __restrict__ kg, P* __restrict__ kt, float4* __restrict__ GF,
+    P* __restrict__ qg, P* __restrict__ kg, P* __restrict__ kt, float* __restrict__ GF,
     float* __restrict__ DG, const int64_t* __restrict__ cu, const int32_t* __restrict__ coff,
     int Tlen, int ttot, int N, int NT, int Hk, int HV) {
   constexpr int KS = DK / 32;   // 32-channel slabs
@@ -253,7 +253,14 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
         if (Aqk_out) Aqk_out[oo] = from_f<T>(aqk);
       }
     }
-  if (grp == 0 && tv) GF[(size_t)hv * ttot + c0 + t] = make_float4(1.f, 1.f, beta[(size_t)(c0 + t) * HV + hv], 1.f);
+  if (grp == 0 && tv) {
+    const size_t gs = (size_t)gf_stride(ttot);
+    float* gp = GF + (size_t)hv * 4 * gs + c0 + t;
+    gp[0] = 1.f;
+    gp[gs] = 1.f;
+    gp[2 * gs] = beta[(size_t)(c0 + t) * HV + hv];
+    gp[3 * gs] = 1.f;
+  }
   if (w == 0) {
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
@@ -275,7 +282,7 @@ hipError_t launch_t(const ChunkArgs& a, const KdaBuffers& kb, hipStream_t s, int
   const dim3 grid((unsigned)nslots, (unsigned)a.HV);
   hipLaunchKernelGGL((kda_intra_kernel<T, DK>), grid, dim3(256), 0, s, (const T*)a.q, (const T*)a.k,
                      a.gk, a.beta, a.scale, (T*)kb.Aqk_out, (T*)kb.Akk_out, (P*)a.Ainv, (P*)a.Aqk,
-                     (P*)kb.qg, (P*)kb.kg, (P*)kb.kt, (float4*)a.GF, kb.dg, a.cu_seqlens,
+                     (P*)kb.qg, (P*)kb.kg, (P*)kb.kt, (float*)a.GF, kb.dg, a.cu_seqlens,
                      a.chunk_off, a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
   return hipGetLastError();
 }
