@@ -42,8 +42,11 @@ using namespace intra;
 // -------------------------------------------------------------------------
 // GDN intra kernel (scalar gate)
 // -------------------------------------------------------------------------
+#ifndef GDN_INTRA_WPE
+#define GDN_INTRA_WPE 3
+#endif
 template <typename T, int DK, typename C = typename ComputeOf<T>::type>
-__global__ __launch_bounds__(64) void gdn_intra_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GDN_INTRA_WPE))) void gdn_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, C* __restrict__ Ainv,
     C* __restrict__ Aqk, float* __restrict__ GF, const int64_t* __restrict__ cu,
@@ -56,10 +59,31 @@ __global__ __launch_bounds__(64) void gdn_intra_kernel(
   const int jk = j / (HV / Hk);
   const int row = lane & 15, grp = lane >> 4;
 
+  // q / k fragments of one 32-channel slab: rows 16rb + row of the chunk;
+  // rows past the chunk end repeat its last row (loads stay unconditional,
+  // so they are all in flight at once): such rows reach A only through
+  // beta = 0, and Aqk only in rows and columns that are never stored
+  auto load_slab = [&](int s, Frag<T> (&kf)[4], Frag<T> (&qf)[4]) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = 16 * rb + row < nrow ? 16 * rb + row : nrow - 1;
+      const size_t off = ((size_t)(c0 + r) * Hk + jk) * DK + 32 * s + 8 * grp;
+      load8(kf[rb], k + off);
+      load8(qf[rb], q + off);
+    }
+  };
+  Frag<T> kf[2][4], qf[2][4];   // two slabs in flight
+  load_slab(0, kf[0], qf[0]);
+
   // chunk-local cumulative gate and beta, lane = token
-  const float gl = (g && lane < nrow) ? g[(size_t)(c0 + lane) * HV + j] : 0.f;
+  // (loads clamped to the chunk, values masked: no branch around a load)
+  const int tl = lane < nrow ? lane : nrow - 1;
+  const float g_raw = g ? g[(size_t)(c0 + tl) * HV + j] : 0.f;
+  const float b_raw = beta[(size_t)(c0 + tl) * HV + j];
+  if (DK / 32 > 1) load_slab(1, kf[1], qf[1]);
+  const float gl = lane < nrow ? g_raw : 0.f;
   const float G = wave_incl_scan(gl, lane);
-  const float bl = lane < nrow ? beta[(size_t)(c0 + lane) * HV + j] : 0.f;
+  const float bl = lane < nrow ? b_raw : 0.f;
   // per-token gate factors for the scan: e^G, e^{G_last - G}, beta, e^{G_last}
   {
     const float Gl = __shfl(G, nrow - 1, 64);
@@ -79,25 +103,13 @@ __global__ __launch_bounds__(64) void gdn_intra_kernel(
   for (int t = 0; t < 10; ++t) { KK[t] = zero4(); QK[t] = zero4(); }
 #pragma unroll
   for (int s = 0; s < DK / 32; ++s) {
-    Frag<T> kf[4], qf[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int r = 16 * rb + row;
-      if (r < nrow) {
-        const size_t off = ((size_t)(c0 + r) * Hk + jk) * DK + 32 * s + 8 * grp;
-        load8(kf[rb], k + off);
-        load8(qf[rb], q + off);
-      } else {
-        kf[rb].zero();
-        qf[rb].zero();
-      }
-    }
+    if (s >= 1 && s + 1 < DK / 32) load_slab(s + 1, kf[(s + 1) & 1], qf[(s + 1) & 1]);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int cb = 0; cb <= rb; ++cb) {
-        KK[tix(rb, cb)] = mma(kf[rb], kf[cb], KK[tix(rb, cb)]);
-        QK[tix(rb, cb)] = mma(qf[rb], kf[cb], QK[tix(rb, cb)]);
+        KK[tix(rb, cb)] = mma(kf[s & 1][rb], kf[s & 1][cb], KK[tix(rb, cb)]);
+        QK[tix(rb, cb)] = mma(qf[s & 1][rb], kf[s & 1][cb], QK[tix(rb, cb)]);
       }
   }
 

@@ -207,8 +207,22 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool is_state = w < NSW;
-  const int cb = w % NSW;                 // 16-column block (state, helper)
+  // wave roles; wave w runs on SIMD w % 4
+#ifndef GDN_SCAN_PLACEMENT
+#define GDN_SCAN_PLACEMENT 0
+#endif
+#if GDN_SCAN_PLACEMENT == 0   // state, state, helper, helper | 4 movers
+  const int role = w < 2 ? 0 : w < 4 ? 1 : 2;
+  const int ridx = w < 4 ? (w & 1) : w - 4;
+#elif GDN_SCAN_PLACEMENT == 1 // both state waves on SIMD 0, both helpers on SIMD 1
+  const int role = (w & 3) == 0 ? 0 : (w & 3) == 1 ? 1 : 2;
+  const int ridx = (w & 3) < 2 ? (w >> 2) : ((w >> 2) * 2 + (w & 3) - 2);
+#else                          // state + helper of the other block on SIMDs 0 and 1
+  const int role = w < 2 ? 0 : (w == 4 || w == 5) ? 1 : 2;
+  const int ridx = w < 2 ? w : (w == 4 || w == 5) ? 5 - w : (w < 4 ? w - 2 : w - 4);
+#endif
+  const bool is_state = role == 0;
+  const int cb = ridx;                    // 16-column block (state, helper) / mover index
   const int n = lane & 15, g = lane >> 4;
   const int NVT = V / BV;
 
@@ -396,7 +410,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         *reinterpret_cast<float4*>(ht + hbase + (size_t)(v0 + 16 * cb + n) * DK + perm_row(kb, 4 * g)) =
             make_float4(St[kb][0], St[kb][1], St[kb][2], St[kb][3]);
     }
-  } else if (w < 2 * NSW) {
+  } else if (role == 1) {
     // =================== helper wave: the output of 16 columns
     __syncthreads();
     auto chunk = [&](auto stg, int c) __attribute__((always_inline)) {
@@ -454,7 +468,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // Mover 0 loads k, 1 q, 2 Ainv and v, 3 Aqk and the gate rows, with
     // direct-to-LDS loads into the stage of the next chunk; each stores a
     // quarter of the o tile.
-    const int mv = w - 2 * NSW;
+    const int mv = ridx;
     // per-lane byte offsets within a full chunk: LDS slot (row, unit')
     // receives global unit unit' ^ swizzle(row)
     uint32_t o_qk[NQK], o_a[8], o_v[4];
