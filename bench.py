@@ -40,6 +40,20 @@ def scan_flops_per_token(d: int) -> int:
     return 6 * d * d + 2 * 80 * d
 
 
+# Algorithmic HBM bytes per launch (bf16 io: 2-byte q/k/v/o; Ainv and Aqk
+# staged as fp16 64-wide rows; gate factors as 4 fp32 planes; fp32 state):
+#   intra: reads q, k (per k-head), g, beta; writes Ainv, Aqk, gate factors
+#   scan:  reads q, k, v, Ainv, Aqk, gate factors (and h0); writes o, ht
+def intra_bytes(B, T, Hk, HV, K, V, io=2):
+    return 2 * B * T * Hk * K * io + 2 * B * T * HV * 4 + 2 * B * T * HV * 64 * 2 + B * T * HV * 16
+
+
+def scan_bytes(B, T, Hk, HV, K, V, N, io=2, h0=False):
+    state = N * HV * K * V * 4
+    return (2 * B * T * Hk * K * io + B * T * HV * V * io + 2 * B * T * HV * 64 * 2 + B * T * HV * 16
+            + B * T * HV * V * io + state * (2 if h0 else 1))
+
+
 # The headline "% MFMA" uses the method's algorithmic count per token per
 # v-head, 6 dk dv + 80 (3 dk + 2 dv) + 2048 (block-lower K K^T, Q K^T, w, u,
 # Aqk Vn, w h, K^T Vn, Q h and the merge).
@@ -151,7 +165,7 @@ def bench_decode(args, binding, workloads, torch, T):
         "kernel_state_GBps": round(state_bytes / (kms * 1e-3) / 1e9, 1),
         "kernel_total_GBps": round((state_bytes + other) / (kms * 1e-3) / 1e9, 1),
         "hbm_frac": round((state_bytes + other) / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(f"decode:T{T}"),
+        "measured_bytes": measured_traffic(f"decode:T{T}"),
     }
 
 
@@ -250,8 +264,24 @@ def main():
     prof = pf["prof"]
     stage_ms = {s: (prof[s][0] / prof[s][1] if prof[s][1] else 0.0) for s in ("intra", "scan")}
     flops = {"intra": intra_flops_per_token(K) * tokens * HV, "scan": scan_flops_per_token(K) * tokens * HV}
+    B, T, Hk = pf["inp"].dims[:3]
+    nbytes = {"intra": intra_bytes(B, T, Hk, HV, K, V), "scan": scan_bytes(B, T, Hk, HV, K, V, B)}
     dom = max(stage_ms, key=stage_ms.get)
-    ach = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    # roofline bound of the dominant kernel: arithmetic intensity vs the ridge
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    dur = stage_ms[dom] * 1e-3
+    meas = measured_traffic(f"prefill:{dom}")
+    if flops[dom] / nbytes[dom] >= ridge:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(flops[dom] / dur / 1e12, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(nbytes[dom] / dur / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None if meas is None else round(meas / dur / 1e9, 1)
+    roof["algorithmic_bytes"] = nbytes[dom]
+    roof["algorithmic_flops"] = flops[dom]
+    roof["measured_bytes"] = meas
     method = method_flops_per_token(K, V) * tokens * HV
     out = {
         "metric": "prefill tokens/s + % MFMA peak; decode tokens/s + state HBM GB/s (1 GPU)",
@@ -271,10 +301,9 @@ def main():
         "mfma_frac_method_flops": round(method / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "cold_ms_per_step": None if pf["cold_ms"] is None else round(pf["cold_ms"], 5),
         "kernels_ms": {s: round(v, 5) for s, v in stage_ms.items()},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(f"prefill:{dom}")},
+        "roofline": roof,
+        "kernels_hbm_frac": {s: round(nbytes[s] / (stage_ms[s] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                             for s in stage_ms if stage_ms[s] > 0},
     }
     if not args.skip_extra and args.only is None:
         out["decode"] = {"T1": bench_decode(args, binding, workloads, torch, 1),
