@@ -28,7 +28,8 @@
 //     S, R and Vn so become B operands in registers, and every A fragment is
 //     one 16-byte LDS read;
 //   * the K^T operand of the state update comes from the same k tile through
-//     gfx950's transposing LDS read (ds_read_b64_tr_b16);
+//     gfx950's transposing LDS read (ds_read_b64_tr_b16), after the
+//     mid-chunk barrier;
 //   * two helper waves compute O (no later step of the chunk needs it) from
 //     the S and Vn fragments the state waves publish in LDS;
 //   * four mover waves (the second wave on each SIMD) move the data: the next
@@ -45,6 +46,8 @@
 //     significant bits); K S^T takes S rounded to bf16 (its error enters R
 //     below R's own fp16 rounding); the 64 x 64 products (Ainv R, Aqk Vn) run
 //     in fp16;
+//   * a state wave issues every LDS read of a chunk's first half before its
+//     first product, so the chain waits out the LDS latency once;
 //   * two barriers per chunk; the work-groups of one (sequence, head) share an
 //     XCD (its L2), sequences are issued longest first.
 
@@ -307,28 +310,40 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       const float (*sG)[BT] = S1 ? sG1 : sG0;
       const int nrow = eos - (bos + c * BT) < BT ? eos - (bos + c * BT) : BT;
 
-      // ---- K^T fragments of the state update, read first (they depend on the
-      // k tile only): lane (n, g) of block kb holds channel perm_row(kb, n)
-      // of tokens 32s + 8g + e, e = 0..7, the slot order of Vt.  Two
-      // transposing reads each: this lane addresses channels
-      // perm_row(kb, 4 (n % 4)) .. + 3 of token 32s + 8g + n / 4 (+ 4).
-      u32x4 Kt[KB][2];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint2 lo = ld_tr(sK + o_tr[kb >> 1][s][0] + 8 * (kb & 1));
-          const uint2 hi = ld_tr(sK + o_tr[kb >> 1][s][1] + 8 * (kb & 1));
-          Kt[kb][s] = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
-      // ---- X = K S^T with S rounded to bf16 (its rounding error enters R
-      // below the fp16 rounding of R itself); block tb, lane: tokens
-      // perm_row(tb, 4g + i)
+      // ---- every LDS read of the first half, issued up front in the order
+      // of use (the compiler would otherwise issue each just before its use
+      // and wait out the LDS latency at every step of the chain)
+      // K row fragments: block tb, lane: tokens perm_row(tb, 4g + i)
       u32x4 A[KS][4];
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) A[s][tb] = ld16(sK + o_kf[s] + blk_rows(tb) * (2 * DK));
+      // lane's rows of block tb are the 4 consecutive tokens perm_row(tb, 4g) + i:
+      // one 16-byte read per gate plane, one transposing read of the v tile
+      // (this lane addresses columns 16cb + 4 (n % 4) .. + 3 of token
+      // perm_row(tb, 4g + n / 4))
+      f32x4 ex[4], ey[4], bz[4];
+      uint2 vr[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int t0 = perm_row(tb, 4 * g);
+        ex[tb] = *reinterpret_cast<const f32x4*>(&sG[0][t0]);
+        bz[tb] = *reinterpret_cast<const f32x4*>(&sG[2][t0]);
+        vr[tb] = ld_tr(sV + (perm_row(tb, 4 * g + (n >> 2)) * BV + 16 * cb + 4 * (n & 3)) * 2);
+      }
+      u32x4 Ai[6];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) Ai[tb] = ld16(sAi + o_ai0 + blk_rows(tb) * 128);
+      Ai[4] = ld16(sAi + o_ai1 + blk_rows(2) * 128);
+      Ai[5] = ld16(sAi + o_ai1 + blk_rows(3) * 128);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) ey[tb] = *reinterpret_cast<const f32x4*>(&sG[1][perm_row(tb, 4 * g)]);
+      const float eGl = sG[3][0];
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- X = K S^T with S rounded to bf16 (its rounding error enters R
+      // below the fp16 rounding of R itself)
       f32x4 X[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) X[tb] = zero4();
@@ -337,23 +352,14 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) X[tb] = mma_bf(A[s][tb], Sh[s], X[tb]);
       // ---- R = beta (v - e^G X); rows past the end are zero
-      // lane's rows of block tb are the 4 consecutive tokens perm_row(tb, 4g) + i:
-      // one 16-byte read per gate plane, one transposing read of the v tile
-      // (this lane addresses columns 16cb + 4 (n % 4) .. + 3 of token
-      // perm_row(tb, 4g + n / 4))
       f32x4 R[4], eGt[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const int t0 = perm_row(tb, 4 * g);
-        const f32x4 ex = *reinterpret_cast<const f32x4*>(&sG[0][t0]);
-        const f32x4 ey = *reinterpret_cast<const f32x4*>(&sG[1][t0]);
-        const f32x4 bz = *reinterpret_cast<const f32x4*>(&sG[2][t0]);
-        const uint2 vr = ld_tr(sV + (perm_row(tb, 4 * g + (n >> 2)) * BV + 16 * cb + 4 * (n & 3)) * 2);
-        const float vv[4] = {__builtin_bit_cast(float, vr.x << 16), __builtin_bit_cast(float, vr.x & 0xFFFF0000u),
-                             __builtin_bit_cast(float, vr.y << 16), __builtin_bit_cast(float, vr.y & 0xFFFF0000u)};
+        const float vv[4] = {__builtin_bit_cast(float, vr[tb].x << 16), __builtin_bit_cast(float, vr[tb].x & 0xFFFF0000u),
+                             __builtin_bit_cast(float, vr[tb].y << 16), __builtin_bit_cast(float, vr[tb].y & 0xFFFF0000u)};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R[tb][i] = bz[i] * (vv[i] - ex[i] * X[tb][i]);
-        eGt[tb] = ey;
+        for (int i = 0; i < 4; ++i) R[tb][i] = bz[tb][i] * (vv[i] - ex[tb][i] * X[tb][i]);
+        eGt[tb] = ey[tb];
       }
       if (nrow < BT) {
 #pragma unroll
@@ -367,11 +373,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       }
       const u32x4 Rf0 = pack_h(R[0], R[1]), Rf1 = pack_h(R[2], R[3]);
       // ---- Vn = Ainv R (block lower triangular in 32-token slabs)
-      u32x4 Ai[6];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) Ai[tb] = ld16(sAi + o_ai0 + blk_rows(tb) * 128);
-      Ai[4] = ld16(sAi + o_ai1 + blk_rows(2) * 128);
-      Ai[5] = ld16(sAi + o_ai1 + blk_rows(3) * 128);
       f32x4 Vn[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) Vn[tb] = mma_h(Ai[tb], Rf0, zero4());
@@ -384,9 +385,22 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         split_bf(Vn[2 * s] * eGt[2 * s], Vn[2 * s + 1] * eGt[2 * s + 1], Vh[s], Vl[s]);
-      const float eGl = sG[3][0];
       lds_barrier();
 
+      // ---- K^T fragments: lane (n, g) of block kb holds channel
+      // perm_row(kb, n) of tokens 32s + 8g + e, e = 0..7, the slot order of
+      // Vt.  Two transposing reads each: this lane addresses channels
+      // perm_row(kb, 4 (n % 4)) .. + 3 of token 32s + 8g + n / 4 (+ 4).
+      u32x4 Kt[KB][2];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const uint2 lo = ld_tr(sK + o_tr[kb >> 1][s][0] + 8 * (kb & 1));
+          const uint2 hi = ld_tr(sK + o_tr[kb >> 1][s][1] + 8 * (kb & 1));
+          Kt[kb][s] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+      __builtin_amdgcn_sched_barrier(0);
       // ---- S^T <- e^{G_last} S^T + K^T Vt
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) St[kb] = St[kb] * eGl;
