@@ -28,11 +28,12 @@ HIPCC_FLAGS = [
     "-Wno-unused-result", "-munsafe-fp-atomics",
 ]
 
-# The bf16 scan keeps its MFMA accumulators (the fp32 state) in ordinary
-# VGPRs, which its VALU work reads and writes every chunk; with the
+# The bf16 scan and the decode kernels keep MFMA accumulators in ordinary
+# VGPRs, which their VALU work reads and writes right away; with the
 # accumulation registers the compiler copies them back and forth.
 FILE_FLAGS = {
     "chunk_scan_gdn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 NOISE = "is not a recognized feature for this target"

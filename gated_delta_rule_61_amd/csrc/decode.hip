@@ -16,7 +16,9 @@
 //   access each, and all loads of the call are issued before any math.
 //
 // The state is streamed once per call (read 32 KiB, write 32 KiB per
-// (row, head)); the kernel is HBM-bound.
+// (row, head)); the kernel is HBM-bound.  That per-token kernel runs T = 1;
+// T = 2 .. 4 run the MFMA form further below, which replaces the T
+// sequential rank-1 steps by one pass of products over the state.
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -173,10 +175,304 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA form for T = 1 .. 4 tokens.  With G_t = alpha_1 ... alpha_t and
+// R_st = G_t / G_s = alpha_{s+1} ... alpha_t (a product, never a quotient),
+// the T sequential steps close up as
+//
+//   w_t = beta_t (v_t - G_t S0 k_t - sum_{s<t} R_st (k_s . k_t) w_s)
+//   o_t = G_t S0 q_t + sum_{s<=t} R_st (k_s . q_t) w_s
+//   S_T = G_T S0 + sum_s R_sT w_s k_s^T
+//
+// (the same recurrence unrolled; q and k normalised, q scaled).  One bf16
+// MFMA pass over the raw state gives S0 [k_1..k_T q_1..q_T] for every state
+// row, a second the Gram matrix of the raw q / k rows (their norms and the
+// dot products), the T-step solve runs per state row inside one lane, and a
+// fp32 MFMA applies the rank-T update S_T^T = G_T S0^T + K W^T.
+//
+// Work-group = one (batch row, v-head), 4 waves; wave w owns state rows
+// 32w .. 32w + 31 as two 16-row blocks rb.  Lane (n, g) = (lane % 16,
+// lane / 16) holds, for 32-channel block kb, the 8 bf16 state values
+// S0[32w + 16rb + n][32kb + 8g .. + 7] (one 16-byte LDS read; the state
+// reaches LDS in whole rows): the B operand of the bf16 16x16x32 product
+// (k-slots 8g + e, column n).  The update writes them back from two
+// 16 x 16 accumulator blocks of S^T whose rows are the channels
+// 32kb + 8 (r / 4) + (r % 4) and the same + 4, so that accumulator lane
+// (n, g) holds exactly the lane's 8 values again.
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mma32_bf(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ __forceinline__ float from_lane(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * l, __builtin_bit_cast(int, x)));
+}
+
+template <int NTOK>
+__global__ __launch_bounds__(256) void gdn_decode_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+    const bf16_t* __restrict__ v, const bf16_t* __restrict__ ga,
+    const bf16_t* __restrict__ gb, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, bf16_t* __restrict__ state,
+    const int32_t* __restrict__ idx, bf16_t* __restrict__ o,
+    int H, int HV, int pool, float scale, float sp_beta, float sp_thr,
+    int use_norm, float eps) {
+  constexpr int KB = DK / 32;
+  __shared__ uint4 sS[DV * DK / 8];   // the state of the (row, head), bf16
+  const int bh = blockIdx.x;
+  const int bi = bh / HV;
+  const int hv = bh - bi * HV;
+  const int hk = hv / (HV / H);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int row0 = 32 * (threadIdx.x >> 6);
+  const int slot = idx ? idx[bi] : bi;
+  const size_t tok0 = (size_t)bi * NTOK;
+
+  if (slot < 0 || slot >= pool) {   // o = 0, the pool is not touched
+    if (g == 0) {
+#pragma unroll
+      for (int tt = 0; tt < NTOK; ++tt)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) o[((tok0 + tt) * HV + hv) * DV + row0 + 16 * rb + n] = 0;
+    }
+    return;
+  }
+
+  // ---- every load of the call, issued up front (state first).  The wave's
+  // 32 state rows go straight to LDS, whole rows per load (lane l of a load
+  // lands at LDS byte 16 l: row 4i + l / 16, 16-byte slot l % 16), with
+  // 16-byte unit u of row r stored in slot u ^ (r % 16), so that the
+  // fragment reads below (16 rows at one unit) hit distinct banks.
+  bf16_t* sp = state + ((size_t)slot * HV + hv) * (size_t)(DV * DK);
+  {
+    typedef __attribute__((address_space(1))) const void gvoid;
+    typedef __attribute__((address_space(3))) char lchar;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = row0 + 4 * i + (lane >> 4);
+      const int u = (lane & 15) ^ (r & 15);
+      __builtin_amdgcn_global_load_lds((gvoid*)(sp + (size_t)r * DK + 8 * u),
+                                       (lchar*)(sS + (row0 + 4 * i) * 16), 16, 0, 0);
+    }
+  }
+  // A operand rows: j = n < 4 -> k of token j, 4 <= j < 8 -> q of token j - 4,
+  // other rows zero (loads of row j are clamped to a valid token, then masked)
+  const int jt = n & 3;
+  const bool jv = n < 8 && jt < NTOK;
+  const bf16_t* srcj = (n < 4 ? k : q) + ((tok0 + (jt < NTOK ? jt : 0)) * H + hk) * DK + 8 * g;
+  uint4 kq[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) kq[kb] = *reinterpret_cast<const uint4*>(srcj + 32 * kb);
+  // update operand: lane (n, g) holds k of token g at the channels of
+  // accumulator row n of the two blocks (h = 0, 1) of channel block kb
+  const bool gv = g < NTOK;
+  const bf16_t* srcg = k + ((tok0 + (gv ? g : 0)) * H + hk) * DK + 8 * (n >> 2) + (n & 3);
+  bf16_t kc[KB][2];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) kc[kb][h] = srcg[32 * kb + 4 * h];
+  // v of the lane's two state rows
+  bf16_t vr[2][NTOK];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) vr[rb][tt] = v[((tok0 + tt) * HV + hv) * DV + row0 + 16 * rb + n];
+
+  // the state fragments: lane (n, g) of block rb, kb holds S0[row][32kb + 8g
+  // .. + 7], row = row0 + 16rb + n (the wave's own rows: its loads are
+  // complete after its vector-memory wait)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // (read from LDS where used, here and in the update, not held in registers)
+  auto frag = [&](int rb, int kb) __attribute__((always_inline)) -> uint4& {
+    return sS[(row0 + 16 * rb + n) * 16 + ((4 * kb + g) ^ n)];
+  };
+
+  // ---- gates (compute_single_gate: softplus with threshold, then exp),
+  // one token per lane (lane l: token l % 4), then broadcast; hardware exp /
+  // log (a few ulp of fp32, far below the bf16 state's rounding)
+  float alpha[NTOK], beta[NTOK];
+  {
+    const int tl = (lane & 3) < NTOK ? (lane & 3) : 0;
+    const size_t tok = tok0 + tl;
+    const float x = bf2f(ga[tok * HV + hv]) + dt_bias[hv];
+    const float bx = sp_beta * x;
+    const float spv = (bx <= sp_thr) ? __logf(1.0f + __expf(bx)) / sp_beta : x;
+    const float al = __expf(-__expf(A_log[hv]) * spv);
+    const float be = 1.0f / (1.0f + __expf(-bf2f(gb[tok * HV + hv])));
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) {
+      alpha[tt] = lane_f(al, tt);
+      beta[tt] = lane_f(be, tt);
+    }
+  }
+
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    if (!jv) kq[kb] = make_uint4(0u, 0u, 0u, 0u);
+
+  // ---- Gram matrix of the raw rows and S0 [k | q] (fp32 accumulation of
+  // exact bf16 products).  Accumulator lane (n, g) holds row 4g + i, column n.
+  f32x4 Gm = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) Gm = mma32_bf(kq[kb], kq[kb], Gm);
+  f32x4 P[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    P[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) P[rb] = mma32_bf(kq[kb], frag(rb, kb), P[rb]);
+  }
+
+  // ---- per-call scalars: norms, normalised dot products, decay products
+  // Gram[s][t] sits in lane t (reg s), Gram[s][4 + t] in lane 4 + t (reg s),
+  // Gram[4 + t][4 + t] in lane 20 + t (reg t).
+  float ks[NTOK], qs[NTOK], kk[NTOK][NTOK], kqd[NTOK][NTOK];
+  {
+    // lane t < 4 holds Gram[t][t] in reg t, lane 20 + t Gram[4 + t][4 + t]
+    // in reg t: one inverse norm per lane, then broadcast
+    const int r = lane & 3;
+    const float sq = r == 0 ? Gm[0] : r == 1 ? Gm[1] : r == 2 ? Gm[2] : Gm[3];
+    const float inv = 1.0f / sqrtf(sq + eps);
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) {
+      ks[tt] = use_norm ? lane_f(inv, tt) : 1.0f;
+      qs[tt] = use_norm ? scale * lane_f(inv, 20 + tt) : scale;
+    }
+  }
+  {
+    // lane t < 4 holds Gram[s][t] (reg s), lane 4 + t holds Gram[s][4 + t]:
+    // each lane scales its column, then broadcast
+    const int c = lane & 3;
+    float cs = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) cs = c == tt ? (lane & 4 ? qs[tt] : ks[tt]) : cs;
+#pragma unroll
+    for (int s2 = 0; s2 < NTOK; ++s2) {
+      const float x = Gm[s2] * (ks[s2] * cs);
+#pragma unroll
+      for (int tt = 0; tt < NTOK; ++tt) {
+        kk[s2][tt] = lane_f(x, tt);
+        kqd[s2][tt] = lane_f(x, 4 + tt);
+      }
+    }
+  }
+  float Gt[NTOK], Rst[NTOK][NTOK];   // G_t; R_st = alpha_{s+1} .. alpha_t
+#pragma unroll
+  for (int tt = 0; tt < NTOK; ++tt) {
+    Gt[tt] = tt == 0 ? alpha[0] : Gt[tt - 1] * alpha[tt];
+    Rst[tt][tt] = 1.0f;
+#pragma unroll
+    for (int s2 = tt - 1; s2 >= 0; --s2) Rst[s2][tt] = Rst[s2 + 1][tt] * alpha[s2 + 1];
+  }
+
+  // ---- per state row: deltas w_t (valid in lanes g = 0, sent to all lanes
+  // of the row), outputs o_t (lanes g = 1), the update's B operand
+  float Bu[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float wv[NTOK], wa[NTOK];
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) {
+      float d = bf2f(vr[rb][tt]) - Gt[tt] * (P[rb][tt] * ks[tt]);
+#pragma unroll
+      for (int s2 = 0; s2 < tt; ++s2) d -= Rst[s2][tt] * kk[s2][tt] * wv[s2];
+      wv[tt] = beta[tt] * d;
+    }
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) wa[tt] = from_lane(wv[tt], n);
+    if (g == 1) {
+#pragma unroll
+      for (int tt = 0; tt < NTOK; ++tt) {
+        float ot = Gt[tt] * (P[rb][tt] * qs[tt]);
+#pragma unroll
+        for (int s2 = 0; s2 <= tt; ++s2) ot += Rst[s2][tt] * kqd[s2][tt] * wa[s2];
+        o[((tok0 + tt) * HV + hv) * DV + row0 + 16 * rb + n] = f2bf(ot);
+      }
+    }
+    float b = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < NTOK; ++s2) b = g == s2 ? Rst[s2][NTOK - 1] * wa[s2] : b;
+    Bu[rb] = b;
+  }
+
+  // ---- S_T^T = G_T S0^T + K W^T.  G_T S0^T: bf16 MFMA of the raw state
+  // fragments with G_T (as a bf16 hi + lo pair) on a selector: block h's A
+  // row r picks k-slot 8 (r / 4) + 4h + r % 4 of the 32-channel block.
+  // K W^T: fp32 MFMA (16x16x4: lane (n, g) holds the A element
+  // [channel row n][token g] and the B element [token g][row n]).
+  float ksg = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < NTOK; ++s2) ksg = g == s2 ? ks[s2] : ksg;
+  const float GT = Gt[NTOK - 1];
+  uint4 sel[2][2];   // [h][hi, lo]
+  {
+    const uint32_t gh = pack_bf2(GT, 0.f) & 0xFFFFu;
+    const uint32_t gl = pack_bf2(GT - __builtin_bit_cast(float, gh << 16), 0.f) & 0xFFFFu;
+    const bool on = g == (n >> 2);
+    const int e = n & 3;   // slot 4h + e of the lane's 8
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t gv2 = p == 0 ? gh : gl;
+        uint32_t wds[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int e0 = 2 * d - 4 * h;   // slots 2d, 2d + 1 relative to 4h
+          wds[d] = (on && e0 == (e & ~1)) ? (gv2 << (16 * (e & 1))) : 0u;
+        }
+        sel[h][p] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+      }
+  }
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    float ak[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ak[h] = gv ? bf2f(kc[kb][h]) * ksg : 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const uint4 r = frag(rb, kb);
+      uint32_t out[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 c = mma32_bf(sel[h][0], r, f32x4{0.f, 0.f, 0.f, 0.f});
+        c = mma32_bf(sel[h][1], r, c);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[h], Bu[rb], c, 0, 0, 0);
+        out[2 * h] = pack_bf2(c[0], c[1]);
+        out[2 * h + 1] = pack_bf2(c[2], c[3]);
+      }
+      frag(rb, kb) = make_uint4(out[0], out[1], out[2], out[3]);
+    }
+  }
+  // the wave's 32 rows back to the pool in whole rows (16-byte unit u of
+  // row r from slot u ^ (r % 16))
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = row0 + 4 * i + (lane >> 4);
+    const int u = lane & 15;
+    *reinterpret_cast<uint4*>(sp + (size_t)r * DK + 8 * u) = sS[r * 16 + (u ^ (r & 15))];
+  }
+}
+
+// T = 1 runs the per-token kernel (the rank-1 step has no products worth
+// MFMA work and its loads / stores cover whole rows); T = 2 .. 4 the MFMA form.
 template <int NTOK>
 hipError_t launch_n(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.HV));
-  hipLaunchKernelGGL(gdn_decode_kernel<NTOK>, grid, dim3(256), 0, s,
+  void (*kern)(const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*,
+               const float*, const float*, bf16_t*, const int32_t*, bf16_t*, int, int, int,
+               float, float, float, int, float);
+  if constexpr (NTOK == 1)
+    kern = gdn_decode_kernel<1>;
+  else
+    kern = gdn_decode_mfma_kernel<NTOK>;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
                      (const bf16_t*)a.a, (const bf16_t*)a.b, a.A_log, a.dt_bias,
                      (bf16_t*)a.state, a.idx, (bf16_t*)a.o, a.H, a.HV, a.pool,
