@@ -561,10 +561,7 @@ hipError_t launch_scan_kda(const ChunkArgs& a, const void* qg, const void* kg, c
   sa.dg = dg;
   sa.coff = a.chunk_off;
   sa.NT = (a.T + BT - 1) / BT;
-  if (a.bf16) {
-    if (a.K == 128) return launch_scan_c<ScanCfg<bf16_t, f16_t, 128, 16, true>>(a, sa, s);
-    return launch_scan_c<ScanCfg<bf16_t, f16_t, 64, 16, true>>(a, sa, s);
-  }
+  if (a.bf16) return launch_scan_kda_bf16(a, qg, kg, kt, dg, s);
   if (a.K == 128) return launch_scan_c<ScanCfg<float, float, 128, 16, true>>(a, sa, s);
   return launch_scan_c<ScanCfg<float, float, 64, 16, true>>(a, sa, s);
 }

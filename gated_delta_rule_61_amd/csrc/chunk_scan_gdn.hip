@@ -156,6 +156,28 @@ __device__ __forceinline__ u32x4 pack_h(f32x4 a, f32x4 b) {
   return u32x4{pack2<f16_t>(a[0], a[1]), pack2<f16_t>(a[2], a[3]), pack2<f16_t>(b[0], b[1]),
                pack2<f16_t>(b[2], b[3])};
 }
+// fp16 (low 16 bits of w) -> fp32 as its own instruction.  Written as a
+// C++ conversion inside x - hi, the compiler fuses it into a mixed-precision
+// FMA with an f16 operand, and that form left hi unsubtracted here (lo came
+// out equal to x).
+__device__ __forceinline__ float h16_to_f(uint32_t w) {
+  float f;
+  asm("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(w));
+  return f;
+}
+// ... as an fp16 hi + lo pair (about 22 significant bits)
+__device__ __forceinline__ void split_h(f32x4 a, f32x4 b, u32x4& hi, u32x4& lo) {
+  hi = pack_h(a, b);
+  f32x4 ra, rb;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    ra[2 * i] = a[2 * i] - h16_to_f(hi[i]);
+    ra[2 * i + 1] = a[2 * i + 1] - h16_to_f(hi[i] >> 16);
+    rb[2 * i] = b[2 * i] - h16_to_f(hi[2 + i]);
+    rb[2 * i + 1] = b[2 * i + 1] - h16_to_f(hi[2 + i] >> 16);
+  }
+  lo = pack_h(ra, rb);
+}
 
 // 16 bytes per lane, global -> LDS; lane l's bytes land at lds + 16 l
 __device__ __forceinline__ void dma16(const void* src, lchar* lds) {
@@ -188,22 +210,83 @@ struct Lds {
   static constexpr int QROWS = 512 / DK;        // q / k rows per 1 KB load
 };
 
+// Direct-to-LDS copies of one chunk's tiles (per-lane offsets precomputed;
+// in the last chunk of a sequence, rows past its end repeat its last row).
 template <int DK>
+__device__ __forceinline__ void dma_qk_tile(const char* xc, const uint32_t* o_qk, int nr, uint32_t qk_row,
+                                            lchar* dX, int lane) {
+  typedef Lds<DK> L;
+  if (nr == BT) {
+#pragma unroll
+    for (int i = 0; i < L::NQK; ++i) dma16(xc + o_qk[i], dX + 1024 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < L::NQK; ++i) {
+      const int row = i * L::QROWS + lane / (DK / 8);
+      const int rr = row < nr ? row : nr - 1;
+      dma16(xc + (uint32_t)rr * qk_row + 16 * ((lane % (DK / 8)) ^ qk_swz<DK>(row)), dX + 1024 * i);
+    }
+  }
+}
+__device__ __forceinline__ void dma_a_tile(const char* ac, const uint32_t* o_a, int nr, uint32_t a_row,
+                                           lchar* dA, int lane) {
+  if (nr == BT) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(ac + o_a[i], dA + 1024 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * i + lane / 8;
+      const int rr = row < nr ? row : nr - 1;
+      dma16(ac + (uint32_t)rr * a_row + 16 * ((lane % 8) ^ a_swz(row)), dA + 1024 * i);
+    }
+  }
+}
+__device__ __forceinline__ void dma_v_tile(const char* vc, const uint32_t* o_v, int nr, uint32_t v_row,
+                                           lchar* dV, int lane) {
+  if (nr == BT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(vc + o_v[i], dV + 1024 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * i + lane / 4;
+      const int rr = row < nr ? row : nr - 1;
+      dma16(vc + (uint32_t)rr * v_row + 16 * (lane % 4), dV + 1024 * i);
+    }
+  }
+}
+
+// KDA: the k / q tiles are the gated fp16 operands K o e^G and Q o e^G, a
+// third tile holds K o e^{G_last - G} for the state update, the scalar
+// gate factors are 1 except beta, and S^T decays row by row by the chunk's
+// e^{G_last} (one value per key channel).
+template <int DK, bool KDA>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_scan_bf16_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const float* __restrict__ GF, const f16_t* __restrict__ Ainv, const f16_t* __restrict__ Aqk,
-    float scale, const float* __restrict__ h0, float* __restrict__ ht, bf16_t* __restrict__ o,
-    const int64_t* __restrict__ cu, const int32_t* __restrict__ order, int Tlen, int ttot, int N,
-    int Hk, int HV, int V) {
+    const void* __restrict__ qop, const void* __restrict__ kop, const f16_t* __restrict__ ktop,
+    const bf16_t* __restrict__ v, const float* __restrict__ GF, const float* __restrict__ DG,
+    const f16_t* __restrict__ Ainv, const f16_t* __restrict__ Aqk, float scale,
+    const float* __restrict__ h0, float* __restrict__ ht, bf16_t* __restrict__ o,
+    const int64_t* __restrict__ cu, const int32_t* __restrict__ order, const int32_t* __restrict__ coff,
+    int Tlen, int ttot, int NT, int N, int Hk, int HV, int V) {
   typedef Lds<DK> L;
   constexpr int KS = L::KS, KB = L::KB, NQK = L::NQK;
+  // q / k tile sources (GDN: the raw bf16 inputs, one row per q / k head;
+  // KDA: the gated fp16 operands, one row per v-head)
+  const char* const qsrc = reinterpret_cast<const char*>(qop);
+  const char* const ksrc = reinterpret_cast<const char*>(kop);
   // two stages of the chunk inputs, separate arrays so that the compiler can
   // tell the stage being filled from the one being read
   __shared__ __attribute__((aligned(16))) char sK0[L::QK], sK1[L::QK], sQ0[L::QK], sQ1[L::QK];
   __shared__ __attribute__((aligned(16))) char sAi0[L::AT], sAi1[L::AT], sAq0[L::AT], sAq1[L::AT];
   __shared__ __attribute__((aligned(16))) char sV0[L::VT], sV1[L::VT];
   __shared__ __attribute__((aligned(16))) float sG0[4][BT], sG1[4][BT];  // gate-factor planes
-  __shared__ __attribute__((aligned(16))) u32x4 sSF[NSW][KS][2][64];  // S fragments (fp32)
+  // KDA: K o e^{G_last - G} tiles and the chunk's decay row e^{G_last}
+  __shared__ __attribute__((aligned(16))) char sT0[KDA ? L::QK : 16], sT1[KDA ? L::QK : 16];
+  __shared__ __attribute__((aligned(16))) float sD0[KDA ? DK : 4], sD1[KDA ? DK : 4];
+  // S fragments for the output: GDN fp32 (split there into bf16 hi + lo),
+  // KDA fp16 (the B operand itself)
+  __shared__ __attribute__((aligned(16))) u32x4 sSF[NSW][KS][KDA ? 1 : 2][64];
   __shared__ __attribute__((aligned(16))) u32x4 sVnF[NSW][2][64];     // Vn fragments (fp16)
   __shared__ __attribute__((aligned(16))) char sO[BT * L::OROW];       // o tile
   __shared__ __attribute__((aligned(16))) uint32_t sSink[64];          // L2-prefetch landing words
@@ -249,28 +332,34 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     bos = ns * Tlen;
     eos = bos + Tlen;
   }
-  const int jo = j / (HV / Hk);
+  const int jo = KDA ? j : j / (HV / Hk);   // row of the q / k tile sources
   const int v0 = vt * BV;
   const int NC = (eos - bos + BT - 1) / BT;
   const size_t hbase = ((size_t)ns * HV + j) * (size_t)V * DK;
   const size_t gs = (size_t)gf_stride(ttot);   // gate-factor plane stride
-  const uint32_t qk_row = (uint32_t)Hk * DK * 2, a_row = (uint32_t)HV * BT * 2,
+  const uint32_t qk_row = (uint32_t)(KDA ? HV : Hk) * DK * 2, a_row = (uint32_t)HV * BT * 2,
                  v_row = (uint32_t)HV * V * 2;
 
   if (is_state) {
     // =================== state wave: the recurrence of 16 columns
     // S^T blocks: block kb, lane: channels perm_row(kb, 4g + i), column 16cb + n
     f32x4 St[KB];
-    u32x4 Sh[KS];   // S rounded to bf16, B operand of X = K S^T
-    // publish S (fp32, fragment order) for the output; keep its bf16 rounding
+    u32x4 Sh[KS];   // S rounded to bf16 (KDA: fp16), B operand of X = K S^T
+    // publish S for the output (GDN: fp32; KDA: its fp16 rounding), keep
+    // the rounding
     auto publish_s = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sSF[cb][s][0][lane] = __builtin_bit_cast(u32x4, St[2 * s]);
-        sSF[cb][s][1][lane] = __builtin_bit_cast(u32x4, St[2 * s + 1]);
         const f32x4 a = St[2 * s], b = St[2 * s + 1];
-        Sh[s] = u32x4{pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(b[0], b[1]),
-                      pack_bf2(b[2], b[3])};
+        if constexpr (KDA) {
+          Sh[s] = pack_h(a, b);
+          sSF[cb][s][0][lane] = Sh[s];
+        } else {
+          sSF[cb][s][0][lane] = __builtin_bit_cast(u32x4, a);
+          sSF[cb][s][1][lane] = __builtin_bit_cast(u32x4, b);
+          Sh[s] = u32x4{pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(b[0], b[1]),
+                        pack_bf2(b[2], b[3])};
+        }
       }
     };
 #pragma unroll
@@ -305,9 +394,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     auto chunk = [&](auto stg, int c) __attribute__((always_inline)) {
       constexpr bool S1 = decltype(stg)::value;
       const char* sK = S1 ? sK1 : sK0;
+      const char* sKt = KDA ? (S1 ? sT1 : sT0) : sK;   // source of the update's K^T
       const char* sAi = S1 ? sAi1 : sAi0;
       const char* sV = S1 ? sV1 : sV0;
       const float (*sG)[BT] = S1 ? sG1 : sG0;
+      const float* sD = S1 ? sD1 : sD0;
       const int nrow = eos - (bos + c * BT) < BT ? eos - (bos + c * BT) : BT;
 
       // ---- every LDS read of the first half, issued up front in the order
@@ -328,7 +419,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const int t0 = perm_row(tb, 4 * g);
-        ex[tb] = *reinterpret_cast<const f32x4*>(&sG[0][t0]);
+        ex[tb] = KDA ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&sG[0][t0]);
         bz[tb] = *reinterpret_cast<const f32x4*>(&sG[2][t0]);
         vr[tb] = ld_tr(sV + (perm_row(tb, 4 * g + (n >> 2)) * BV + 16 * cb + 4 * (n & 3)) * 2);
       }
@@ -338,20 +429,22 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       Ai[4] = ld16(sAi + o_ai1 + blk_rows(2) * 128);
       Ai[5] = ld16(sAi + o_ai1 + blk_rows(3) * 128);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) ey[tb] = *reinterpret_cast<const f32x4*>(&sG[1][perm_row(tb, 4 * g)]);
-      const float eGl = sG[3][0];
+      for (int tb = 0; tb < 4; ++tb)
+        ey[tb] = KDA ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&sG[1][perm_row(tb, 4 * g)]);
+      const float eGl = KDA ? 1.f : sG[3][0];
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- X = K S^T with S rounded to bf16 (its rounding error enters R
-      // below the fp16 rounding of R itself)
+      // below the fp16 rounding of R itself); KDA: (K o e^G) S^T, fp16
       f32x4 X[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) X[tb] = zero4();
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) X[tb] = mma_bf(A[s][tb], Sh[s], X[tb]);
-      // ---- R = beta (v - e^G X); rows past the end are zero
+        for (int tb = 0; tb < 4; ++tb) X[tb] = KDA ? mma_h(A[s][tb], Sh[s], X[tb]) : mma_bf(A[s][tb], Sh[s], X[tb]);
+      // ---- R = beta (v - e^G X); rows past the end are zero (KDA: e^G is
+      // inside X, and e^{G_last - G} inside the update's K^T: ex = ey = 1)
       f32x4 R[4], eGt[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
@@ -378,13 +471,18 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       for (int tb = 0; tb < 4; ++tb) Vn[tb] = mma_h(Ai[tb], Rf0, zero4());
       Vn[2] = mma_h(Ai[4], Rf1, Vn[2]);
       Vn[3] = mma_h(Ai[5], Rf1, Vn[3]);
-      // publish Vn for the output; Vt = diag(e^{G_last - G}) Vn (zero past the end)
+      // publish Vn for the output; Vt = diag(e^{G_last - G}) Vn (zero past the
+      // end) as a bf16 (KDA: fp16) hi + lo pair
       sVnF[cb][0][lane] = pack_h(Vn[0], Vn[1]);
       sVnF[cb][1][lane] = pack_h(Vn[2], Vn[3]);
       u32x4 Vh[2], Vl[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-        split_bf(Vn[2 * s] * eGt[2 * s], Vn[2 * s + 1] * eGt[2 * s + 1], Vh[s], Vl[s]);
+      for (int s = 0; s < 2; ++s) {
+        if constexpr (KDA)
+          split_h(Vn[2 * s] * eGt[2 * s], Vn[2 * s + 1] * eGt[2 * s + 1], Vh[s], Vl[s]);
+        else
+          split_bf(Vn[2 * s] * eGt[2 * s], Vn[2 * s + 1] * eGt[2 * s + 1], Vh[s], Vl[s]);
+      }
       lds_barrier();
 
       // ---- K^T fragments: lane (n, g) of block kb holds channel
@@ -396,20 +494,33 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const uint2 lo = ld_tr(sK + o_tr[kb >> 1][s][0] + 8 * (kb & 1));
-          const uint2 hi = ld_tr(sK + o_tr[kb >> 1][s][1] + 8 * (kb & 1));
+          const uint2 lo = ld_tr(sKt + o_tr[kb >> 1][s][0] + 8 * (kb & 1));
+          const uint2 hi = ld_tr(sKt + o_tr[kb >> 1][s][1] + 8 * (kb & 1));
           Kt[kb][s] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- S^T <- e^{G_last} S^T + K^T Vt
+      // KDA: decay of the lane's state rows, channels perm_row(kb, 4g + i)
+      f32x4 dk[KDA ? KB : 1];
+      if constexpr (KDA) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) St[kb] = St[kb] * eGl;
+        for (int kb = 0; kb < KB; ++kb) dk[kb] = *reinterpret_cast<const f32x4*>(sD + perm_row(kb, 4 * g));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- S^T <- e^{G_last} S^T + K^T Vt  (KDA: diag(e^{G_last}) S^T + K^T Vn)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        if constexpr (KDA)
+          St[kb] = St[kb] * dk[kb];
+        else
+          St[kb] = St[kb] * eGl;
+      }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) St[kb] = mma_bf(Kt[kb][s], Vh[s], St[kb]);
+        for (int kb = 0; kb < KB; ++kb)
+          St[kb] = KDA ? mma_h(Kt[kb][s], Vh[s], St[kb]) : mma_bf(Kt[kb][s], Vh[s], St[kb]);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) St[kb] = mma_bf(Kt[kb][s], Vl[s], St[kb]);
+        for (int kb = 0; kb < KB; ++kb)
+          St[kb] = KDA ? mma_h(Kt[kb][s], Vl[s], St[kb]) : mma_bf(Kt[kb][s], Vl[s], St[kb]);
       }
       publish_s();
       lds_barrier();
@@ -432,22 +543,29 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       const char* sQ = S1 ? sQ1 : sQ0;
       const char* sAq = S1 ? sAq1 : sAq0;
       const float (*sG)[BT] = S1 ? sG1 : sG0;
-      // ---- Oi = Q S^T from the published fp32 S (split into bf16 hi + lo)
+      // ---- Oi = Q S^T from the published fp32 S (split into bf16 hi + lo);
+      // KDA: (Q o e^G) S^T with the published fp16 S
       f32x4 Oi[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) Oi[tb] = zero4();
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        u32x4 bh, bl;
-        split_bf(__builtin_bit_cast(f32x4, sSF[cb][s][0][lane]),
-                 __builtin_bit_cast(f32x4, sSF[cb][s][1][lane]), bh, bl);
         u32x4 A[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) A[tb] = ld16(sQ + qk_off<DK>(perm_row(tb, n), 4 * s + g));
+        if constexpr (KDA) {
+          const u32x4 bs = sSF[cb][s][0][lane];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) Oi[tb] = mma_bf(A[tb], bh, Oi[tb]);
+          for (int tb = 0; tb < 4; ++tb) Oi[tb] = mma_h(A[tb], bs, Oi[tb]);
+        } else {
+          u32x4 bh, bl;
+          split_bf(__builtin_bit_cast(f32x4, sSF[cb][s][0][lane]),
+                   __builtin_bit_cast(f32x4, sSF[cb][s][KDA ? 0 : 1][lane]), bh, bl);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) Oi[tb] = mma_bf(A[tb], bl, Oi[tb]);
+          for (int tb = 0; tb < 4; ++tb) Oi[tb] = mma_bf(A[tb], bh, Oi[tb]);
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) Oi[tb] = mma_bf(A[tb], bl, Oi[tb]);
+        }
       }
       lds_barrier();
 
@@ -460,7 +578,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       Aq[5] = ld16(sAq + a_off(perm_row(3, n), 4 + g));
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const f32x4 ex = *reinterpret_cast<const f32x4*>(&sG[0][perm_row(tb, 4 * g)]);
+        const f32x4 ex = KDA ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&sG[0][perm_row(tb, 4 * g)]);
         f32x4 acc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = Oi[tb][i] * (scale * ex[i]);
@@ -479,9 +597,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     }
   } else {
     // =================== mover wave: global <-> LDS traffic
-    // Mover 0 loads k, 1 q, 2 Ainv and v, 3 Aqk and the gate rows, with
-    // direct-to-LDS loads into the stage of the next chunk; each stores a
-    // quarter of the o tile.
+    // Direct-to-LDS loads of the next chunk into the other stage; each mover
+    // also stores a quarter of the o tile.  GDN: mover 0 loads k, 1 q,
+    // 2 Ainv and v, 3 Aqk and the gate rows.  KDA: mover 0 K o e^G and v,
+    // 1 Q o e^G, the beta row and the decay row, 2 K o e^{G_last - G},
+    // 3 Ainv and Aqk.
     const int mv = ridx;
     // per-lane byte offsets within a full chunk: LDS slot (row, unit')
     // receives global unit unit' ^ swizzle(row)
@@ -498,60 +618,47 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) o_v[i] = (uint32_t)(16 * i + lane / 4) * v_row + 16 * (lane % 4);
-    const bf16_t* xsrc = pick(mv == 0, k, q);         // movers 0, 1
-    const f16_t* asrc = pick(mv == 2, Ainv, Aqk);     // movers 2, 3
+    // KDA: global index of the sequence's first chunk (row of the decay rows)
+    const int chunk0 = KDA ? (coff ? coff[ns] : ns * NT) : 0;
 
-    // loads of the chunk at token c0 into the given stage; in the last chunk
-    // of a sequence, rows past its end repeat its last row (masked later)
-    auto dma_chunk = [&](int c0, lchar* dK, lchar* dQ, lchar* dAi, lchar* dAq, lchar* dV, lchar* dG)
-        __attribute__((always_inline)) {
+    // loads of the chunk at token c0 into the given stage
+    auto dma_chunk = [&](int c0, lchar* dK, lchar* dQ, lchar* dT, lchar* dAi, lchar* dAq, lchar* dV,
+                         lchar* dG, lchar* dD) __attribute__((always_inline)) {
       const int nr = eos - c0 < BT ? eos - c0 : BT;
-      if (mv < 2) {
-        lchar* dX = mv == 0 ? dK : dQ;
-        const char* xc = reinterpret_cast<const char*>(xsrc + ((size_t)c0 * Hk + jo) * DK);
-        if (nr == BT) {
+      const size_t xo = (size_t)c0 * qk_row + (size_t)jo * DK * 2;
+      const char* ac0 = reinterpret_cast<const char*>(Ainv + ((size_t)c0 * HV + j) * BT);
+      const char* ac1 = reinterpret_cast<const char*>(Aqk + ((size_t)c0 * HV + j) * BT);
+      const char* vc = reinterpret_cast<const char*>(v + ((size_t)c0 * HV + j) * V + v0);
+      // gate planes (KDA: only the beta plane is read); KDA decay row
+      const int rg = lane < nr ? lane : nr - 1;
+      const float* gp = GF + (size_t)j * 4 * gs + c0 + rg;
+      if constexpr (KDA) {
+        if (mv == 0) {
+          dma_qk_tile<DK>(ksrc + xo, o_qk, nr, qk_row, dK, lane);
+          dma_v_tile(vc, o_v, nr, v_row, dV, lane);
+        } else if (mv == 1) {
+          dma_qk_tile<DK>(qsrc + xo, o_qk, nr, qk_row, dQ, lane);
+          dma4(gp + 2 * gs, dG + 512);
+          const float* dp = DG + ((size_t)(chunk0 + (c0 - bos) / BT) * HV + j) * DK;
 #pragma unroll
-          for (int i = 0; i < NQK; ++i) dma16(xc + o_qk[i], dX + 1024 * i);
+          for (int i = 0; i < DK / 64; ++i) dma4(dp + 64 * i + lane, dD + 256 * i);
+        } else if (mv == 2) {
+          dma_qk_tile<DK>(reinterpret_cast<const char*>(ktop) + xo, o_qk, nr, qk_row, dT, lane);
         } else {
-#pragma unroll
-          for (int i = 0; i < NQK; ++i) {
-            const int row = i * L::QROWS + lane / (DK / 8);
-            const int rr = row < nr ? row : nr - 1;
-            dma16(xc + (uint32_t)rr * qk_row + 16 * ((lane % (DK / 8)) ^ qk_swz<DK>(row)), dX + 1024 * i);
-          }
+          dma_a_tile(ac0, o_a, nr, a_row, dAi, lane);
+          dma_a_tile(ac1, o_a, nr, a_row, dAq, lane);
         }
       } else {
-        lchar* dA = mv == 2 ? dAi : dAq;
-        const char* ac = reinterpret_cast<const char*>(asrc + ((size_t)c0 * HV + j) * BT);
-        if (nr == BT) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) dma16(ac + o_a[i], dA + 1024 * i);
+        if (mv < 2) {
+          dma_qk_tile<DK>(pick(mv == 0, ksrc, qsrc) + xo, o_qk, nr, qk_row, mv == 0 ? dK : dQ, lane);
         } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int row = 8 * i + lane / 8;
-            const int rr = row < nr ? row : nr - 1;
-            dma16(ac + (uint32_t)rr * a_row + 16 * ((lane % 8) ^ a_swz(row)), dA + 1024 * i);
-          }
-        }
-        if (mv == 2) {
-          const char* vc = reinterpret_cast<const char*>(v + ((size_t)c0 * HV + j) * V + v0);
-          if (nr == BT) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dma16(vc + o_v[i], dV + 1024 * i);
+          dma_a_tile(pick(mv == 2, ac0, ac1), o_a, nr, a_row, mv == 2 ? dAi : dAq, lane);
+          if (mv == 2) {
+            dma_v_tile(vc, o_v, nr, v_row, dV, lane);
           } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = 16 * i + lane / 4;
-              const int rr = row < nr ? row : nr - 1;
-              dma16(vc + (uint32_t)rr * v_row + 16 * (lane % 4), dV + 1024 * i);
-            }
+            for (int pl = 0; pl < 4; ++pl) dma4(gp + pl * gs, dG + 256 * pl);
           }
-        } else {
-          const int rr = lane < nr ? lane : nr - 1;
-          const float* gp = GF + (size_t)j * 4 * gs + c0 + rr;
-#pragma unroll
-          for (int pl = 0; pl < 4; ++pl) dma4(gp + pl * gs, dG + 256 * pl);
         }
       }
     };
@@ -565,21 +672,24 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       const int nr = eos - c0 < BT ? eos - c0 : BT;
       lchar* sink = (lchar*)sSink;
       constexpr int QKP = DK / 64;               // 64-line pieces per q or k tile
-      const int piece = (NMV * vt + mv) % (2 * QKP + 2);
+      constexpr int NXT = KDA ? 3 : 2;           // q / k-like tiles of a chunk
+      const int piece = (NMV * vt + mv) % (NXT * QKP + 2);
       const char* p;
-      if (piece < 2 * QKP) {
-        const bf16_t* x = pick(piece < QKP, q, k);
+      if (piece < NXT * QKP) {
+        const int t = piece / QKP;
+        const char* x = pick(t == 0, qsrc, pick(t == 1, ksrc, reinterpret_cast<const char*>(ktop)));
         const int row0 = (piece % QKP) * (64 / QKP) + lane / QKP;
         const int row = row0 < nr ? row0 : nr - 1;
-        p = reinterpret_cast<const char*>(x + ((size_t)(c0 + row) * Hk + jo) * DK) + 128 * (lane % QKP);
+        p = x + (size_t)(c0 + row) * qk_row + (size_t)jo * DK * 2 + 128 * (lane % QKP);
       } else {
         const int row = lane < nr ? lane : nr - 1;
-        p = reinterpret_cast<const char*>(pick(piece == 2 * QKP, Ainv, Aqk) +
+        p = reinterpret_cast<const char*>(pick(piece == NXT * QKP, Ainv, Aqk) +
                                           ((size_t)(c0 + row) * HV + j) * BT);
       }
       touch4(p, sink);
       const int rr = lane < nr ? lane : nr - 1;
-      if (mv == 2) touch4(v + ((size_t)(c0 + rr) * HV + j) * V + v0, sink);
+      if (mv == (KDA ? 0 : 2)) touch4(v + ((size_t)(c0 + rr) * HV + j) * V + v0, sink);
+      else if (KDA) touch4(GF + (size_t)j * 4 * gs + 2 * gs + c0 + rr, sink);
       else touch4(GF + (size_t)j * 4 * gs + (lane >> 1 & 3) * gs + c0 + (nr > 32 ? 32 * (lane & 1) : 0), sink);
     };
 
@@ -594,7 +704,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     };
 
     if (NC > 0) {
-      dma_chunk(bos, (lchar*)sK0, (lchar*)sQ0, (lchar*)sAi0, (lchar*)sAq0, (lchar*)sV0, (lchar*)sG0);
+      dma_chunk(bos, (lchar*)sK0, (lchar*)sQ0, (lchar*)sT0, (lchar*)sAi0, (lchar*)sAq0, (lchar*)sV0,
+                (lchar*)sG0, (lchar*)sD0);
       __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
@@ -604,9 +715,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       if (c > 0) store_o(c0 - BT);
       if (c + 1 < NC) {
         if constexpr (S1)
-          dma_chunk(c0 + BT, (lchar*)sK0, (lchar*)sQ0, (lchar*)sAi0, (lchar*)sAq0, (lchar*)sV0, (lchar*)sG0);
+          dma_chunk(c0 + BT, (lchar*)sK0, (lchar*)sQ0, (lchar*)sT0, (lchar*)sAi0, (lchar*)sAq0, (lchar*)sV0,
+                    (lchar*)sG0, (lchar*)sD0);
         else
-          dma_chunk(c0 + BT, (lchar*)sK1, (lchar*)sQ1, (lchar*)sAi1, (lchar*)sAq1, (lchar*)sV1, (lchar*)sG1);
+          dma_chunk(c0 + BT, (lchar*)sK1, (lchar*)sQ1, (lchar*)sT1, (lchar*)sAi1, (lchar*)sAq1, (lchar*)sV1,
+                    (lchar*)sG1, (lchar*)sD1);
       }
       if (c + 2 < NC) touch_chunk(c0 + 2 * BT);
       lds_barrier();
@@ -629,24 +742,31 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   }
 }
 
-template <int DK>
-hipError_t launch_dk(const ChunkArgs& a, hipStream_t s) {
+template <int DK, bool KDA>
+hipError_t launch_dk(const ChunkArgs& a, const void* qop, const void* kop, const void* ktop,
+                     const float* dg, hipStream_t s) {
   const int nvt = a.V / BV;
   const int groups = a.N * a.HV;
   const int nblk = ((groups + 7) / 8) * 8 * nvt;
-  hipLaunchKernelGGL((gdn_scan_bf16_kernel<DK>), dim3((unsigned)nblk), dim3(NTHR), 0, s,
-                     (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
-                     (const float*)a.GF, (const f16_t*)a.Ainv, (const f16_t*)a.Aqk, a.scale, a.h0,
-                     a.ht, (bf16_t*)a.o, a.cu_seqlens, a.seq_order, a.T, a.B * a.T, a.N, a.Hk,
-                     a.HV, a.V);
+  hipLaunchKernelGGL((gdn_scan_bf16_kernel<DK, KDA>), dim3((unsigned)nblk), dim3(NTHR), 0, s, qop, kop,
+                     (const f16_t*)ktop, (const bf16_t*)a.v, (const float*)a.GF, dg,
+                     (const f16_t*)a.Ainv, (const f16_t*)a.Aqk, a.scale, a.h0, a.ht, (bf16_t*)a.o,
+                     a.cu_seqlens, a.seq_order, a.chunk_off, a.T, a.B * a.T, (a.T + BT - 1) / BT, a.N,
+                     a.Hk, a.HV, a.V);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_scan_gdn_bf16(const ChunkArgs& a, hipStream_t s) {
-  if (a.K == 128) return launch_dk<128>(a, s);
-  return launch_dk<64>(a, s);
+  if (a.K == 128) return launch_dk<128, false>(a, a.q, a.k, nullptr, nullptr, s);
+  return launch_dk<64, false>(a, a.q, a.k, nullptr, nullptr, s);
+}
+
+hipError_t launch_scan_kda_bf16(const ChunkArgs& a, const void* qg, const void* kg, const void* kt,
+                                const float* dg, hipStream_t s) {
+  if (a.K == 128) return launch_dk<128, true>(a, qg, kg, kt, dg, s);
+  return launch_dk<64, true>(a, qg, kg, kt, dg, s);
 }
 
 }  // namespace gdn

@@ -47,8 +47,11 @@ struct ChunkArgs {
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t s);
 // Token stride of a gate-factor plane.
 __host__ __device__ inline long long gf_stride(long long tokens) { return tokens; }
-// bf16 GDN scan (direct-to-LDS staging, state / helper waves)
+// bf16 GDN and KDA scans (direct-to-LDS staging, state / helper / mover waves);
+// KDA reads the gated operands and decay rows of KdaBuffers
 hipError_t launch_scan_gdn_bf16(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_scan_kda_bf16(const ChunkArgs& a, const void* qg, const void* kg, const void* kt,
+                                const float* dg, hipStream_t s);
 
 // Extra buffers of the KDA path.
 struct KdaBuffers {
