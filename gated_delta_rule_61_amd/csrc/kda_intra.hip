@@ -30,7 +30,11 @@
 //     diagonal block exactly, pair by pair, in fp32;
 //   * beta / scale / causal masks on the fp32 accumulators; the 64 x 64
 //     solve is the same forward substitution + block merge as the GDN
-//     kernel.
+//     kernel;
+//   * every global load a wave needs (its 16 gate rows, its q / k row, beta)
+//     is issued at entry, so the memory latency is paid once;
+//   * Aqk is staged in LDS (in the cumsum tile, free by then) and, like
+//     Akk_inv, leaves in 16-byte row pieces, one tile per wave.
 
 #include "chunk_common.h"
 #include "gdn_device.h"
@@ -75,32 +79,52 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
   if (!locate_chunk(cu, coff, N, Tlen, NT, c0, nrow)) return;
   const int hk = hv / (HV / Hk);
 
+  // ---- every global load the wave needs before its math, issued up front
+  // (addresses of rows past nrow are clamped to the last row, the values
+  // masked where used): the wave's 16 gate rows, its operand row of q and
+  // k, and beta of its rows
+  const int cl = lane * CPL;
+  float gx[16][CPL];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int tok = 16 * w + u < nrow ? 16 * w + u : nrow - 1;
+    const float* gp = gk + ((size_t)(c0 + tok) * HV + hv) * DK + cl;
+    if constexpr (CPL == 2) {
+      const float2 v2 = *reinterpret_cast<const float2*>(gp);
+      gx[u][0] = v2.x;
+      gx[u][1] = v2.y;
+    } else {
+      gx[u][0] = gp[0];
+    }
+  }
+  const int t = 16 * w + row;  // token (within the chunk) of this lane's operand row
+  const bool tv = t < nrow;
+  const int tc = tv ? t : nrow - 1;
+  Frag<T> fq[KS], fk[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    load8(fq[s], q + ((size_t)(c0 + tc) * Hk + hk) * DK + 32 * s + 8 * grp);
+    load8(fk[s], k + ((size_t)(c0 + tc) * Hk + hk) * DK + 32 * s + 8 * grp);
+  }
+  float braw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * grp + i < nrow ? 16 * w + 4 * grp + i : nrow - 1;
+    braw[i] = beta[(size_t)(c0 + r) * HV + hv];
+  }
+  const float bt = beta[(size_t)(c0 + tc) * HV + hv];
+
   // ---- cumulative gate over the chunk, per channel (rows past nrow add 0)
   {
-    const int cl = lane * CPL;
     float acc[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int tok = 16 * w + u;
-      float x[CPL];
-      if (tok < nrow) {
-        const float* gp = gk + ((size_t)(c0 + tok) * HV + hv) * DK + cl;
-        if constexpr (CPL == 2) {
-          const float2 v2 = *reinterpret_cast<const float2*>(gp);
-          x[0] = v2.x;
-          x[1] = v2.y;
-        } else {
-          x[0] = gp[0];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) x[e] = 0.f;
-      }
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
-        acc[e] += x[e];
+        acc[e] += tok < nrow ? gx[u][e] : 0.f;
         sG[tok][cl + e] = acc[e];
       }
     }
@@ -120,23 +144,16 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
   }
 
   // ---- gated operands of this wave's block; row operands kept in registers
-  const int t = 16 * w + row;  // token (within the chunk) of this lane's operand row
-  const bool tv = t < nrow;
   float qa[KS][8], ka[KS][8];  // q, k scaled by exp(G[t] - G[n_w])
   float dmax = 0.f;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int cb = 32 * s + 8 * grp;
     float qv[8], kv[8];
-    if (tv) {
-      Frag<T> fq, fk;
-      load8(fq, q + ((size_t)(c0 + t) * Hk + hk) * DK + cb);
-      load8(fk, k + ((size_t)(c0 + t) * Hk + hk) * DK + cb);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { qv[e] = fq.get(e); kv[e] = fk.get(e); }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { qv[e] = 0.f; kv[e] = 0.f; }
+    for (int e = 0; e < 8; ++e) {
+      qv[e] = tv ? fq[s].get(e) : 0.f;
+      kv[e] = tv ? fk[s].get(e) : 0.f;
     }
     float vq[8], vk[8], vt[8], vc[8];
 #pragma unroll
@@ -231,12 +248,22 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
     }
   }
 
-  // ---- scale / beta / masks; Aqk to memory, A to LDS (upper blocks zero)
+  // ---- scale / beta / masks; Aqk and A to LDS (upper blocks zero).  Aqk
+  // (fp32) is staged in the cumsum tile, which nothing reads after this
+  // barrier (wave 0 keeps the last row for the decay first).
+  float dgv[CPL];
+  if (w == 0) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) dgv[e] = sG[BT - 1][lane * CPL + e];
+  }
+  __syncthreads();
+  float (*sQ)[AP] = reinterpret_cast<float (*)[AP]>(&sG[0][0]);
+  static_assert(sizeof(sG) >= sizeof(float) * BT * AP, "Aqk staging tile");
   float br[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * w + 4 * grp + i;
-    br[i] = r < nrow ? beta[(size_t)(c0 + r) * HV + hv] : 0.f;
+    br[i] = r < nrow ? braw[i] : 0.f;
   }
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb)
@@ -247,33 +274,32 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
       const float aqk = (in && sc <= r) ? scale * QK[jb][i] : 0.f;
       const float akk = (in && sc < r) ? br[i] * KK[jb][i] : 0.f;
       sA[r][sc] = akk;
-      if (r < nrow) {
-        const size_t oo = ((size_t)(c0 + r) * HV + hv) * BT + sc;
-        Aqk_ws[oo] = from_f<P>(aqk);
-        if (Aqk_out) Aqk_out[oo] = from_f<T>(aqk);
-      }
+      sQ[r][sc] = aqk;
     }
   if (grp == 0 && tv) {
     const size_t gs = (size_t)gf_stride(ttot);
     float* gp = GF + (size_t)hv * 4 * gs + c0 + t;
     gp[0] = 1.f;
     gp[gs] = 1.f;
-    gp[2 * gs] = beta[(size_t)(c0 + t) * HV + hv];
+    gp[2 * gs] = bt;
     gp[3 * gs] = 1.f;
   }
   if (w == 0) {
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
       const int c = lane * CPL + e;
-      DG[((size_t)blockIdx.x * HV + hv) * DK + c] = __expf(sG[BT - 1][c]);
+      DG[((size_t)blockIdx.x * HV + hv) * DK + c] = __expf(dgv[e]);
     }
   }
   __syncthreads();
 
-  // ---- (I + A)^-1 (wave 0), then rows to memory
+  // ---- (I + A)^-1 (wave 0), then the tiles to memory in 16-byte row pieces,
+  // one tile per wave
   solve_unit_lower_64(sA, lane, w == 0);
   if (w == 0) store_tile<P>(sA, Ainv_ws, c0, nrow, HV, hv, lane);
   if (w == 1 && Akk_out) store_tile<T>(sA, Akk_out, c0, nrow, HV, hv, lane);
+  if (w == 2) store_tile<P>(sQ, Aqk_ws, c0, nrow, HV, hv, lane);
+  if (w == 3 && Aqk_out) store_tile<T>(sQ, Aqk_out, c0, nrow, HV, hv, lane);
 }
 
 template <typename T, int DK>
