@@ -17,16 +17,14 @@
 // exp(g_last - g); "sglang srt/layers/attention/fla/chunk_fwd.py", the
 // intra-chunk A consumed by recompute_w_u).
 //
+// This kernel serves fp32 io (GDN and KDA); bf16 io runs the LDS-staged
+// kernel of chunk_scan_gdn.hip.
+//
 // gfx950 design: 4 waves (256 threads) per work-group, BV = 16 columns.
 //   * S^T stays in fp32 MFMA accumulators: wave w owns key rows
 //     [w*DK/4, (w+1)*DK/4); LDS holds S as the B operand of the next chunk's
 //     K S^T and Q S^T;
-//   * the products with the inputs (K S^T, Q S^T, K^T Vn) run in bf16 on the
-//     raw q / k, which are exact in bf16; their computed operands S and
-//     diag(e^{G_last-G}) Vn are split into bf16 hi + lo (two MFMAs, ~16
-//     significant bits) instead of converting every input element;
-//   * the small 64 x 64 products (Ainv R, Aqk Vn) run in fp16 (Ainv and Aqk
-//     are bounded by construction);
+//   * every product is an fp32 16x16x4 MFMA;
 //   * wave w owns tokens 16w..16w+15 of X, O, R, Vn; its q / k / Ainv / Aqk
 //     fragments, v, and gate factors are prefetched one chunk ahead into one
 //     of two register sets used in turn (no copies);
@@ -36,12 +34,11 @@
 //     intermediate;
 //   * work-groups of one (sequence, head) share an XCD (its L2), and
 //     sequences are issued longest first.
-// fp32 io runs the same schedule with fp32 operands everywhere.
 //
 // KDA (one log-gate per key channel) runs the same kernel: every scalar e^G
 // becomes a per-channel factor inside the contractions, so the intra kernel
-// writes the gated operands K o e^G, Q o e^G and K o e^{G_last - G} (fp16,
-// bounded by |k|, |q|) and a per-channel decay e^{G_last}; the scan reads
+// writes the gated operands K o e^G, Q o e^G and K o e^{G_last - G} (fp32
+// for fp32 io) and a per-channel decay e^{G_last}; the scan reads
 // those in place of q / k, skips the per-row gate scaling and decays S^T
 // row by row ("fla ops/common/chunk_h.py", USE_GK: h *= exp(gk_last)[:, None],
 // k *= exp(gk_last - gk)).
@@ -66,36 +63,15 @@ __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d) {
   }
 }
 
-// Store 4 consecutive values as bf16 hi and lo parts (x ~= hi + lo, about 16
-// significant bits); for fp16 / fp32 operands the value goes to `ph` alone.
+// Store 4 consecutive values of a computed operand (S, diag(.) Vn); `pl`
+// (a lo-part tile) is unused for fp32 operands.
 template <typename T>
-__device__ __forceinline__ void st4_split(T* ph, T* pl, float a, float b, float c, float d) {
-  if constexpr (__is_same(T, bf16_t)) {
-    const uint32_t h0 = pack_bf2(a, b), h1 = pack_bf2(c, d);
-    *reinterpret_cast<uint2*>(ph) = make_uint2(h0, h1);
-    const float la = a - __builtin_bit_cast(float, h0 << 16);
-    const float lb = b - __builtin_bit_cast(float, h0 & 0xFFFF0000u);
-    const float lc = c - __builtin_bit_cast(float, h1 << 16);
-    const float ld = d - __builtin_bit_cast(float, h1 & 0xFFFF0000u);
-    *reinterpret_cast<uint2*>(pl) = make_uint2(pack_bf2(la, lb), pack_bf2(lc, ld));
-  } else {
-    st4<T>(ph, a, b, c, d);
-  }
+__device__ __forceinline__ void st4_split(T* ph, T*, float a, float b, float c, float d) {
+  st4<T>(ph, a, b, c, d);
 }
 
-// raw 8-element row segment of the io type
+// raw 8-element row segment of the operand type
 template <typename T> struct Seg8;
-template <> struct Seg8<bf16_t> {
-  uint4 v;
-  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
-  __device__ __forceinline__ uint32_t word(int e) const {
-    return e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
-  }
-};
-template <> struct Seg8<f16_t> : Seg8<bf16_t> {
-  __device__ __forceinline__ void load(const f16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
-};
 template <> struct Seg8<float> {
   float4 a, b;
   __device__ __forceinline__ void load(const float* p) {
@@ -110,31 +86,7 @@ template <> struct Seg8<float> {
 };
 
 // Channel e of TPT consecutive tokens -> TPT consecutive elements of the
-// transposed tile row (pure bit moves for bf16).
-template <int TPT>
-__device__ __forceinline__ void put_channel(bf16_t* dst, const Seg8<bf16_t> (&src)[TPT], int e) {
-  auto pair = [&](int a, int b) -> uint32_t {
-    const uint32_t x = src[a].word(e), y = src[b].word(e);
-    return (e & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-  };
-  if constexpr (TPT == 4) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pair(0, 1), pair(2, 3));
-  } else {
-    *reinterpret_cast<uint32_t*>(dst) = pair(0, 1);
-  }
-}
-template <int TPT>
-__device__ __forceinline__ void put_channel(f16_t* dst, const Seg8<f16_t> (&src)[TPT], int e) {
-  auto pair = [&](int a, int b) -> uint32_t {
-    const uint32_t x = src[a].word(e), y = src[b].word(e);
-    return (e & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-  };
-  if constexpr (TPT == 4) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pair(0, 1), pair(2, 3));
-  } else {
-    *reinterpret_cast<uint32_t*>(dst) = pair(0, 1);
-  }
-}
+// transposed tile row.
 template <int TPT>
 __device__ __forceinline__ void put_channel(float* dst, const Seg8<float> (&src)[TPT], int e) {
   if constexpr (TPT == 4) {
@@ -147,8 +99,8 @@ __device__ __forceinline__ void put_channel(float* dst, const Seg8<float> (&src)
 // Types of one scan instantiation.
 //   IOT: io type of v and o;  OPT: type of the operand tensors the scan reads
 //   (q / k for GDN, the gated operands for KDA);  P: type of the small 64 x 64
-//   products.  SPLIT: computed operands (S, diag(.) Vn) go to LDS as bf16
-//   hi + lo; otherwise in OPT.
+//   products (all float here).  SPLIT (computed operands as a hi + lo pair)
+//   is off for fp32 operands.
 template <typename IOT_, typename OPT_, int DK_, int BV_, bool KDA_>
 struct ScanCfg {
   typedef IOT_ IOT;
