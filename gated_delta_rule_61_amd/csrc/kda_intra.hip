@@ -34,7 +34,10 @@
 //   * every global load a wave needs (its 16 gate rows, its q / k row, beta)
 //     is issued at entry, so the memory latency is paid once;
 //   * Aqk is staged in LDS (in the cumsum tile, free by then) and, like
-//     Akk_inv, leaves in 16-byte row pieces, one tile per wave.
+//     Akk_inv, leaves in 16-byte row pieces, one tile per wave;
+//   * the pairs' decay factors exp(G[n_i] - G[m_j]) are one LDS table built
+//     by all threads (they do not depend on the row), and the bounded
+//     operands convert to fp16 without clamping.
 
 #include "chunk_common.h"
 #include "gdn_device.h"
@@ -48,6 +51,22 @@ using namespace intra;
 
 constexpr float DIAG_MAX_DECAY = 10.0f;      // nats of decay inside a 16-token block
 constexpr float DIAG_MAX_OPERAND = 30000.0f;  // largest fp16 operand the fast path accepts
+
+// 16-bit (or fp32) conversions without clamping, for operands bounded by
+// |q|, |k| (every exponent here is <= 0, except the diagonal pair's, whose
+// operands the exact path takes over beyond DIAG_MAX_OPERAND)
+template <typename P> __device__ __forceinline__ P to_bounded(float x) { return from_f<P>(x); }
+template <> __device__ __forceinline__ f16_t to_bounded<f16_t>(float x) { return (_Float16)x; }
+template <typename P> __device__ __forceinline__ uint32_t pack2_bounded(float lo, float hi) {
+  return pack2<P>(lo, hi);
+}
+template <> __device__ __forceinline__ uint32_t pack2_bounded<f16_t>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+}
+template <typename P> __device__ __forceinline__ void set_bounded(Frag<P>& f, int e, float x) { f.set(e, x); }
+template <> __device__ __forceinline__ void set_bounded<f16_t>(Frag<f16_t>& f, int e, float x) {
+  f.v[e] = (_Float16)x;
+}
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -70,6 +89,8 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
   __shared__ __attribute__((aligned(16))) float sG[BT][GP];
   __shared__ __attribute__((aligned(16))) P sC[BT][CP];
   __shared__ __attribute__((aligned(16))) float sA[BT][AP];
+  // exp(G[n_i] - G[m_j]) of block pair (i, j), j <= i, per channel
+  __shared__ __attribute__((aligned(16))) float sE[10][DK];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,6 +164,15 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
     __syncthreads();
   }
 
+  // ---- the block pairs' decay factors (the same for the 16 rows of a
+  // block, so computed once here rather than in every lane)
+  for (int idx = tid; idx < 10 * DK; idx += 256) {
+    const int pr = idx / DK, c = idx - pr * DK;
+    const int i = pr >= 6 ? 3 : pr >= 3 ? 2 : pr >= 1 ? 1 : 0;
+    const int jj = pr - tix(i, 0);
+    sE[pr][c] = __expf(sG[16 * i][c] - sG[16 * jj + 15][c]);
+  }
+
   // ---- gated operands of this wave's block; row operands kept in registers
   float qa[KS][8], ka[KS][8];  // q, k scaled by exp(G[t] - G[n_w])
   float dmax = 0.f;
@@ -173,12 +203,15 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
     if (tv) {
       const size_t oo = ((size_t)(c0 + t) * HV + hv) * DK + cb;
       if constexpr (sizeof(P) == 2) {
-        *reinterpret_cast<uint4*>(qg + oo) = make_uint4(pack2<P>(vq[0], vq[1]), pack2<P>(vq[2], vq[3]),
-                                                        pack2<P>(vq[4], vq[5]), pack2<P>(vq[6], vq[7]));
-        *reinterpret_cast<uint4*>(kg + oo) = make_uint4(pack2<P>(vk[0], vk[1]), pack2<P>(vk[2], vk[3]),
-                                                        pack2<P>(vk[4], vk[5]), pack2<P>(vk[6], vk[7]));
-        *reinterpret_cast<uint4*>(kt + oo) = make_uint4(pack2<P>(vt[0], vt[1]), pack2<P>(vt[2], vt[3]),
-                                                        pack2<P>(vt[4], vt[5]), pack2<P>(vt[6], vt[7]));
+        *reinterpret_cast<uint4*>(qg + oo) =
+            make_uint4(pack2_bounded<P>(vq[0], vq[1]), pack2_bounded<P>(vq[2], vq[3]),
+                       pack2_bounded<P>(vq[4], vq[5]), pack2_bounded<P>(vq[6], vq[7]));
+        *reinterpret_cast<uint4*>(kg + oo) =
+            make_uint4(pack2_bounded<P>(vk[0], vk[1]), pack2_bounded<P>(vk[2], vk[3]),
+                       pack2_bounded<P>(vk[4], vk[5]), pack2_bounded<P>(vk[6], vk[7]));
+        *reinterpret_cast<uint4*>(kt + oo) =
+            make_uint4(pack2_bounded<P>(vt[0], vt[1]), pack2_bounded<P>(vt[2], vt[3]),
+                       pack2_bounded<P>(vt[4], vt[5]), pack2_bounded<P>(vt[6], vt[7]));
       } else {
 #pragma unroll
         for (int e = 0; e < 8; e += 4) {
@@ -189,7 +222,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sC[t][cb + e] = from_f<P>(vc[e]);
+    for (int e = 0; e < 8; ++e) sC[t][cb + e] = to_bounded<P>(vc[e]);
   }
   const float Dw = wave_max(dmax);
   __syncthreads();
@@ -206,14 +239,15 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
     for (int s = 0; s < KS; ++s) {
       const int cb = 32 * s + 8 * grp;
       Frag<P> fa, fb, fc;
+      const float4 sv0 = *reinterpret_cast<const float4*>(&sE[tix(w, jb)][cb]);
+      const float4 sv1 = *reinterpret_cast<const float4*>(&sE[tix(w, jb)][cb + 4]);
+      const float sv[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int c = cb + e;
-        const float sv = __expf(sG[16 * w][c] - sG[16 * jb + 15][c]);
-        const float xq = qa[s][e] * sv, xk = ka[s][e] * sv;
+        const float xq = qa[s][e] * sv[e], xk = ka[s][e] * sv[e];
         if (jb == w) opmax = fmaxf(opmax, fmaxf(fabsf(xq), fabsf(xk)));
-        fa.set(e, xq);
-        fb.set(e, xk);
+        set_bounded<P>(fa, e, xq);
+        set_bounded<P>(fb, e, xk);
       }
       load8(fc, &sC[16 * jb + row][cb]);
       QK[jb] = mma(fa, fc, QK[jb]);
