@@ -201,6 +201,10 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
 // (n, g) holds exactly the lane's 8 values again.
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 
+// 16 bytes as a plain vector (a copy of HIP's uint4 struct between memory
+// spaces becomes a memcpy that keeps arrays of them out of registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ f32x4 mma32_bf(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -222,14 +226,17 @@ __global__ __launch_bounds__(256) void gdn_decode_mfma_kernel(
     int H, int HV, int pool, float scale, float sp_beta, float sp_thr,
     int use_norm, float eps) {
   constexpr int KB = DK / 32;
-  __shared__ uint4 sS[DV * DK / 8];   // the state of the (row, head), bf16
+  // the state of the (row, head), bf16: rows 16 w + r of each wave's two
+  // 16-row blocks (block 0 in sS0, block 1 in sS1)
+  __shared__ uint4 sS0[DV * DK / 16], sS1[DV * DK / 16];
   const int bh = blockIdx.x;
   const int bi = bh / HV;
   const int hv = bh - bi * HV;
   const int hk = hv / (HV / H);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
-  const int row0 = 32 * (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int row0 = 32 * wv;
   const int slot = idx ? idx[bi] : bi;
   const size_t tok0 = (size_t)bi * NTOK;
 
@@ -243,33 +250,18 @@ __global__ __launch_bounds__(256) void gdn_decode_mfma_kernel(
     return;
   }
 
-  // ---- every load of the call, issued up front (state first).  The wave's
-  // 32 state rows go straight to LDS, whole rows per load (lane l of a load
-  // lands at LDS byte 16 l: row 4i + l / 16, 16-byte slot l % 16), with
-  // 16-byte unit u of row r stored in slot u ^ (r % 16), so that the
-  // fragment reads below (16 rows at one unit) hit distinct banks.
-  bf16_t* sp = state + ((size_t)slot * HV + hv) * (size_t)(DV * DK);
-  {
-    typedef __attribute__((address_space(1))) const void gvoid;
-    typedef __attribute__((address_space(3))) char lchar;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = row0 + 4 * i + (lane >> 4);
-      const int u = (lane & 15) ^ (r & 15);
-      __builtin_amdgcn_global_load_lds((gvoid*)(sp + (size_t)r * DK + 8 * u),
-                                       (lchar*)(sS + (row0 + 4 * i) * 16), 16, 0, 0);
-    }
-  }
-  // A operand rows: j = n < 4 -> k of token j, 4 <= j < 8 -> q of token j - 4,
-  // other rows zero (loads of row j are clamped to a valid token, then masked)
+  // ---- the small loads first: the A operand rows (j = n < 4 -> k of token
+  // j, 4 <= j < 8 -> q of token j - 4, other rows zero; loads of row j are
+  // clamped to a valid token, then masked), k at the update's channel rows
+  // (lane (n, g): token g at the channels of accumulator row n of the two
+  // blocks h = 0, 1 of channel block kb), v of the lane's two state rows,
+  // and the gate inputs of token lane % 4
   const int jt = n & 3;
   const bool jv = n < 8 && jt < NTOK;
   const bf16_t* srcj = (n < 4 ? k : q) + ((tok0 + (jt < NTOK ? jt : 0)) * H + hk) * DK + 8 * g;
   uint4 kq[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) kq[kb] = *reinterpret_cast<const uint4*>(srcj + 32 * kb);
-  // update operand: lane (n, g) holds k of token g at the channels of
-  // accumulator row n of the two blocks (h = 0, 1) of channel block kb
   const bool gv = g < NTOK;
   const bf16_t* srcg = k + ((tok0 + (gv ? g : 0)) * H + hk) * DK + 8 * (n >> 2) + (n & 3);
   bf16_t kc[KB][2];
@@ -277,34 +269,43 @@ __global__ __launch_bounds__(256) void gdn_decode_mfma_kernel(
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int h = 0; h < 2; ++h) kc[kb][h] = srcg[32 * kb + 4 * h];
-  // v of the lane's two state rows
   bf16_t vr[2][NTOK];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int tt = 0; tt < NTOK; ++tt) vr[rb][tt] = v[((tok0 + tt) * HV + hv) * DV + row0 + 16 * rb + n];
+  const int tl = (lane & 3) < NTOK ? (lane & 3) : 0;
+  const bf16_t ga_r = ga[(tok0 + tl) * HV + hv], gb_r = gb[(tok0 + tl) * HV + hv];
 
-  // the state fragments: lane (n, g) of block rb, kb holds S0[row][32kb + 8g
-  // .. + 7], row = row0 + 16rb + n (the wave's own rows: its loads are
-  // complete after its vector-memory wait)
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  // (read from LDS where used, here and in the update, not held in registers)
-  auto frag = [&](int rb, int kb) __attribute__((always_inline)) -> uint4& {
-    return sS[(row0 + 16 * rb + n) * 16 + ((4 * kb + g) ^ n)];
-  };
+  // ---- then the wave's 32 state rows in whole rows, in two 16-row blocks:
+  // lane l of load i covers row 4i + l / 16 of the block, 16-byte unit u =
+  // (l % 16) ^ (row % 16), stored in LDS slot l % 16, so that the fragment
+  // reads (16 rows at one unit) hit distinct banks.  Block 0 goes straight
+  // to LDS; block 1 into registers, written to LDS after block 0's math (an
+  // LDS read after a direct-to-LDS load waits for every such load in flight).
+  bf16_t* sp = state + ((size_t)slot * HV + hv) * (size_t)(DV * DK);
+  {
+    typedef __attribute__((address_space(1))) const void gvoid;
+    typedef __attribute__((address_space(3))) char lchar;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0 + 4 * i + (lane >> 4);
+      const int u = (lane & 15) ^ (r & 15);
+      __builtin_amdgcn_global_load_lds((gvoid*)(sp + (size_t)r * DK + 8 * u),
+                                       (lchar*)(sS0 + (16 * wv + 4 * i) * 16), 16, 0, 0);
+    }
+  }
 
   // ---- gates (compute_single_gate: softplus with threshold, then exp),
-  // one token per lane (lane l: token l % 4), then broadcast; hardware exp /
-  // log (a few ulp of fp32, far below the bf16 state's rounding)
+  // one token per lane, then broadcast; hardware exp / log (a few ulp of
+  // fp32, far below the bf16 state's rounding)
   float alpha[NTOK], beta[NTOK];
   {
-    const int tl = (lane & 3) < NTOK ? (lane & 3) : 0;
-    const size_t tok = tok0 + tl;
-    const float x = bf2f(ga[tok * HV + hv]) + dt_bias[hv];
+    const float x = bf2f(ga_r) + dt_bias[hv];
     const float bx = sp_beta * x;
     const float spv = (bx <= sp_thr) ? __logf(1.0f + __expf(bx)) / sp_beta : x;
     const float al = __expf(-__expf(A_log[hv]) * spv);
-    const float be = 1.0f / (1.0f + __expf(-bf2f(gb[tok * HV + hv])));
+    const float be = 1.0f / (1.0f + __expf(-bf2f(gb_r)));
 #pragma unroll
     for (int tt = 0; tt < NTOK; ++tt) {
       alpha[tt] = lane_f(al, tt);
@@ -316,22 +317,13 @@ __global__ __launch_bounds__(256) void gdn_decode_mfma_kernel(
   for (int kb = 0; kb < KB; ++kb)
     if (!jv) kq[kb] = make_uint4(0u, 0u, 0u, 0u);
 
-  // ---- Gram matrix of the raw rows and S0 [k | q] (fp32 accumulation of
-  // exact bf16 products).  Accumulator lane (n, g) holds row 4g + i, column n.
+  // ---- Gram matrix of the raw rows (fp32 accumulation of exact bf16
+  // products).  Accumulator lane (n, g) holds row 4g + i, column n.
   f32x4 Gm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) Gm = mma32_bf(kq[kb], kq[kb], Gm);
-  f32x4 P[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    P[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) P[rb] = mma32_bf(kq[kb], frag(rb, kb), P[rb]);
-  }
 
   // ---- per-call scalars: norms, normalised dot products, decay products
-  // Gram[s][t] sits in lane t (reg s), Gram[s][4 + t] in lane 4 + t (reg s),
-  // Gram[4 + t][4 + t] in lane 20 + t (reg t).
   float ks[NTOK], qs[NTOK], kk[NTOK][NTOK], kqd[NTOK][NTOK];
   {
     // lane t < 4 holds Gram[t][t] in reg t, lane 20 + t Gram[4 + t][4 + t]
@@ -371,41 +363,12 @@ __global__ __launch_bounds__(256) void gdn_decode_mfma_kernel(
     for (int s2 = tt - 1; s2 >= 0; --s2) Rst[s2][tt] = Rst[s2 + 1][tt] * alpha[s2 + 1];
   }
 
-  // ---- per state row: deltas w_t (valid in lanes g = 0, sent to all lanes
-  // of the row), outputs o_t (lanes g = 1), the update's B operand
-  float Bu[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    float wv[NTOK], wa[NTOK];
-#pragma unroll
-    for (int tt = 0; tt < NTOK; ++tt) {
-      float d = bf2f(vr[rb][tt]) - Gt[tt] * (P[rb][tt] * ks[tt]);
-#pragma unroll
-      for (int s2 = 0; s2 < tt; ++s2) d -= Rst[s2][tt] * kk[s2][tt] * wv[s2];
-      wv[tt] = beta[tt] * d;
-    }
-#pragma unroll
-    for (int tt = 0; tt < NTOK; ++tt) wa[tt] = from_lane(wv[tt], n);
-    if (g == 1) {
-#pragma unroll
-      for (int tt = 0; tt < NTOK; ++tt) {
-        float ot = Gt[tt] * (P[rb][tt] * qs[tt]);
-#pragma unroll
-        for (int s2 = 0; s2 <= tt; ++s2) ot += Rst[s2][tt] * kqd[s2][tt] * wa[s2];
-        o[((tok0 + tt) * HV + hv) * DV + row0 + 16 * rb + n] = f2bf(ot);
-      }
-    }
-    float b = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < NTOK; ++s2) b = g == s2 ? Rst[s2][NTOK - 1] * wa[s2] : b;
-    Bu[rb] = b;
-  }
-
-  // ---- S_T^T = G_T S0^T + K W^T.  G_T S0^T: bf16 MFMA of the raw state
-  // fragments with G_T (as a bf16 hi + lo pair) on a selector: block h's A
-  // row r picks k-slot 8 (r / 4) + 4h + r % 4 of the 32-channel block.
-  // K W^T: fp32 MFMA (16x16x4: lane (n, g) holds the A element
-  // [channel row n][token g] and the B element [token g][row n]).
+  // ---- the update's constant operands.  S_T^T = G_T S0^T + K W^T:
+  // G_T S0^T is a bf16 MFMA of the raw state fragments with G_T (as a bf16
+  // hi + lo pair) on a selector (block h's A row r picks k-slot
+  // 8 (r / 4) + 4h + r % 4 of the 32-channel block); K W^T an fp32 MFMA
+  // (16x16x4: lane (n, g) holds the A element [channel row n][token g] and
+  // the B element [token g][row n]).
   float ksg = 0.f;
 #pragma unroll
   for (int s2 = 0; s2 < NTOK; ++s2) ksg = g == s2 ? ks[s2] : ksg;
@@ -430,34 +393,100 @@ __global__ __launch_bounds__(256) void gdn_decode_mfma_kernel(
         sel[h][p] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
       }
   }
+  float ak[KB][2];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    float ak[2];
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) ak[h] = gv ? bf2f(kc[kb][h]) * ksg : 0.f;
+    for (int h = 0; h < 2; ++h) ak[kb][h] = gv ? bf2f(kc[kb][h]) * ksg : 0.f;
+
+  // ---- one 16-row block: S0 [k | q] (accumulator lane (n, g): row 4g + i
+  // of [k | q], state row n), the deltas w_t (valid in lanes g = 0, sent to
+  // all lanes of the row), o_t (lanes g = 1, returned), the rank-T update
+  // written back over the block's LDS rows.  `mid` runs once the block's
+  // fragments have been read.
+  auto block = [&](int rb, uint4* sb, float (&ov)[NTOK], auto mid) __attribute__((always_inline)) {
+    // lane (n, g) of channel block kb: S0[row][32kb + 8g .. + 7]
+    auto frag = [&](int kb) __attribute__((always_inline)) -> uint4& {
+      return sb[(16 * wv + n) * 16 + ((4 * kb + g) ^ n)];
+    };
+    uint4 fr[KB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const uint4 r = frag(rb, kb);
+    for (int kb = 0; kb < KB; ++kb) fr[kb] = frag(kb);
+    __builtin_amdgcn_sched_barrier(0);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 P = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) P = mma32_bf(kq[kb], fr[kb], P);
+    float wv2[NTOK], wa[NTOK];
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) {
+      float d = bf2f(vr[rb][tt]) - Gt[tt] * (P[tt] * ks[tt]);
+#pragma unroll
+      for (int s2 = 0; s2 < tt; ++s2) d -= Rst[s2][tt] * kk[s2][tt] * wv2[s2];
+      wv2[tt] = beta[tt] * d;
+    }
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) wa[tt] = from_lane(wv2[tt], n);
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) {
+      float ot = Gt[tt] * (P[tt] * qs[tt]);
+#pragma unroll
+      for (int s2 = 0; s2 <= tt; ++s2) ot += Rst[s2][tt] * kqd[s2][tt] * wa[s2];
+      ov[tt] = ot;
+    }
+    float bu = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < NTOK; ++s2) bu = g == s2 ? Rst[s2][NTOK - 1] * wa[s2] : bu;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint4 r = fr[kb];
       uint32_t out[4];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         f32x4 c = mma32_bf(sel[h][0], r, f32x4{0.f, 0.f, 0.f, 0.f});
         c = mma32_bf(sel[h][1], r, c);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[h], Bu[rb], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[kb][h], bu, c, 0, 0, 0);
         out[2 * h] = pack_bf2(c[0], c[1]);
         out[2 * h + 1] = pack_bf2(c[2], c[3]);
       }
-      frag(rb, kb) = make_uint4(out[0], out[1], out[2], out[3]);
+      frag(kb) = make_uint4(out[0], out[1], out[2], out[3]);
     }
-  }
-  // the wave's 32 rows back to the pool in whole rows (16-byte unit u of
-  // row r from slot u ^ (r % 16))
+  };
+  // a block's rows back to the pool in whole rows (16-byte unit u of row r
+  // from slot u ^ (r % 16)), and its o values
+  auto store_block = [&](int rb, const uint4* sb, const float (&ov)[NTOK]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = row0 + 4 * i + (lane >> 4);
-    const int u = lane & 15;
-    *reinterpret_cast<uint4*>(sp + (size_t)r * DK + 8 * u) = sS[r * 16 + (u ^ (r & 15))];
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int rl = 4 * i + (lane >> 4);   // row within the block
+      const int u = lane & 15;
+      *reinterpret_cast<uint4*>(sp + (size_t)(row0 + 16 * rb + rl) * DK + 8 * u) =
+          sb[(16 * wv + rl) * 16 + (u ^ rl)];
+    }
+    if (g == 1) {
+#pragma unroll
+      for (int tt = 0; tt < NTOK; ++tt) o[((tok0 + tt) * HV + hv) * DV + row0 + 16 * rb + n] = f2bf(ov[tt]);
+    }
+  };
+
+  // block 1's rows are loaded into registers once block 0's fragments are
+  // read (the wait before those reads covers every load in flight), so
+  // they arrive during block 0's math
+  float ov0[NTOK], ov1[NTOK];
+  u32x4 raw1[4];
+  block(0, sS0, ov0, [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0 + 16 + 4 * i + (lane >> 4);
+      const int u = (lane & 15) ^ (r & 15);
+      raw1[i] = *reinterpret_cast<const u32x4*>(sp + (size_t)r * DK + 8 * u);
+    }
+  });
+#pragma unroll
+  for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(sS1)[(16 * wv + 4 * i) * 16 + lane] = raw1[i];
+  store_block(0, sS0, ov0);
+  block(1, sS1, ov1, []() {});
+  store_block(1, sS1, ov1);
 }
 
 // T = 1 runs the per-token kernel (the rank-1 step has no products worth
