@@ -21,12 +21,25 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
   return x;
 }
 
-// Locate the chunk of this work-group: sets [c0, c0 + nrow) and returns false
-// when the slot is past the last chunk.
-__device__ __forceinline__ bool locate_chunk(const int64_t* __restrict__ cu,
+// Work-group -> (chunk slot, v-head).  Work-group ids are dealt round-robin
+// to the 8 XCDs, each with its own L2.  The order below puts the HV heads of
+// a chunk slot on one XCD, next to each other in time, so that per-token
+// arrays with the head innermost ([tokens, HV] gates and beta) come from HBM
+// about once instead of once per head.  Returns false for padding ids.
+__device__ __forceinline__ bool slot_of_block(int nslots, int HV, int& slot, int& j) {
+  const int id = blockIdx.x;
+  const int rest = id >> 3;
+  j = rest % HV;
+  slot = (rest / HV) * 8 + (id & 7);
+  return slot < nslots;
+}
+inline unsigned intra_blocks(int nslots, int HV) { return (unsigned)(((nslots + 7) / 8) * 8 * HV); }
+
+// Locate chunk slot c: sets [c0, c0 + nrow) and returns false when the slot
+// is past the last chunk.
+__device__ __forceinline__ bool locate_chunk(int c, const int64_t* __restrict__ cu,
                                              const int32_t* __restrict__ coff,
                                              int N, int T, int NT, int& c0, int& nrow) {
-  const int c = blockIdx.x;
   int bos, eos, it;
   if (cu) {
     if (c >= coff[N]) return false;

@@ -50,12 +50,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GDN_INTRA_WP
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, C* __restrict__ Ainv,
     C* __restrict__ Aqk, float* __restrict__ GF, const int64_t* __restrict__ cu,
-    const int32_t* __restrict__ coff, int Tlen, int ttot, int N, int NT, int Hk, int HV) {
+    const int32_t* __restrict__ coff, int Tlen, int ttot, int N, int NT, int nslots, int Hk, int HV) {
   __shared__ __attribute__((aligned(16))) float sA[BT][AP];
   const int lane = threadIdx.x;
-  const int j = blockIdx.y;
-  int c0, nrow;
-  if (!locate_chunk(cu, coff, N, Tlen, NT, c0, nrow)) return;
+  int slot, j, c0, nrow;
+  if (!slot_of_block(nslots, HV, slot, j)) return;
+  if (!locate_chunk(slot, cu, coff, N, Tlen, NT, c0, nrow)) return;
   const int jk = j / (HV / Hk);
   const int row = lane & 15, grp = lane >> 4;
 
@@ -165,29 +165,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GDN_INTRA_WP
 }  // namespace
 
 hipError_t launch_intra_gdn(const ChunkArgs& a, hipStream_t s, int NT, int nslots) {
-  const dim3 grid((unsigned)nslots, (unsigned)a.HV);
+  const dim3 grid(intra_blocks(nslots, a.HV));
   if (a.bf16) {
     if (a.K == 128)
       hipLaunchKernelGGL((gdn_intra_kernel<bf16_t, 128>), grid, dim3(64), 0, s,
                          (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, a.scale,
                          (f16_t*)a.Ainv, (f16_t*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
-                         a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
+                         a.T, a.B * a.T, a.N, NT, nslots, a.Hk, a.HV);
     else
       hipLaunchKernelGGL((gdn_intra_kernel<bf16_t, 64>), grid, dim3(64), 0, s,
                          (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, a.scale,
                          (f16_t*)a.Ainv, (f16_t*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
-                         a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
+                         a.T, a.B * a.T, a.N, NT, nslots, a.Hk, a.HV);
   } else {
     if (a.K == 128)
       hipLaunchKernelGGL((gdn_intra_kernel<float, 128>), grid, dim3(64), 0, s,
                          (const float*)a.q, (const float*)a.k, a.g, a.beta, a.scale,
                          (float*)a.Ainv, (float*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
-                         a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
+                         a.T, a.B * a.T, a.N, NT, nslots, a.Hk, a.HV);
     else
       hipLaunchKernelGGL((gdn_intra_kernel<float, 64>), grid, dim3(64), 0, s,
                          (const float*)a.q, (const float*)a.k, a.g, a.beta, a.scale,
                          (float*)a.Ainv, (float*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
-                         a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
+                         a.T, a.B * a.T, a.N, NT, nslots, a.Hk, a.HV);
   }
   return hipGetLastError();
 }

@@ -543,6 +543,10 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       const char* sQ = S1 ? sQ1 : sQ0;
       const char* sAq = S1 ? sAq1 : sAq0;
       const float (*sG)[BT] = S1 ? sG1 : sG0;
+      // the state waves' reads at the start of a chunk head the chain; the
+      // helpers (which have slack) and the movers stay off the LDS meanwhile
+      // (about 500 and 250 cycles; measured at DK = 128)
+      if constexpr (DK == 128) __builtin_amdgcn_s_sleep(8);
       // ---- Oi = Q S^T from the published fp32 S (split into bf16 hi + lo);
       // KDA: (Q o e^G) S^T with the published fp16 S
       f32x4 Oi[4];
@@ -712,6 +716,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     auto chunk = [&](auto stg, int c) __attribute__((always_inline)) {
       constexpr bool S1 = decltype(stg)::value;
       const int c0 = bos + c * BT;
+      if constexpr (DK == 128) __builtin_amdgcn_s_sleep(4);   // see the helper waves
       if (c > 0) store_o(c0 - BT);
       if (c + 1 < NC) {
         if constexpr (S1)

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
     T* __restrict__ Akk_out, P* __restrict__ Ainv_ws, P* __restrict__ Aqk_ws,
     P* __restrict__ qg, P* __restrict__ kg, P* __restrict__ kt, float* __restrict__ GF,
     float* __restrict__ DG, const int64_t* __restrict__ cu, const int32_t* __restrict__ coff,
-    int Tlen, int ttot, int N, int NT, int Hk, int HV) {
+    int Tlen, int ttot, int N, int NT, int nslots, int Hk, int HV) {
   constexpr int KS = DK / 32;   // 32-channel slabs
   constexpr int CPL = DK / 64;  // channels per lane in the cumsum
   constexpr int GP = DK + 4;    // padded fp32 row of the cumsum tile
@@ -95,9 +95,9 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = lane & 15, grp = lane >> 4;
-  const int hv = blockIdx.y;
-  int c0, nrow;
-  if (!locate_chunk(cu, coff, N, Tlen, NT, c0, nrow)) return;
+  int slot, hv, c0, nrow;
+  if (!slot_of_block(nslots, HV, slot, hv)) return;
+  if (!locate_chunk(slot, cu, coff, N, Tlen, NT, c0, nrow)) return;
   const int hk = hv / (HV / Hk);
 
   // ---- every global load the wave needs before its math, issued up front
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
       const int c = lane * CPL + e;
-      DG[((size_t)blockIdx.x * HV + hv) * DK + c] = __expf(dgv[e]);
+      DG[((size_t)slot * HV + hv) * DK + c] = __expf(dgv[e]);
     }
   }
   __syncthreads();
@@ -339,11 +339,11 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
 template <typename T, int DK>
 hipError_t launch_t(const ChunkArgs& a, const KdaBuffers& kb, hipStream_t s, int NT, int nslots) {
   typedef typename ComputeOf<T>::type P;
-  const dim3 grid((unsigned)nslots, (unsigned)a.HV);
+  const dim3 grid(intra_blocks(nslots, a.HV));
   hipLaunchKernelGGL((kda_intra_kernel<T, DK>), grid, dim3(256), 0, s, (const T*)a.q, (const T*)a.k,
                      a.gk, a.beta, a.scale, (T*)kb.Aqk_out, (T*)kb.Akk_out, (P*)a.Ainv, (P*)a.Aqk,
                      (P*)kb.qg, (P*)kb.kg, (P*)kb.kt, (float*)a.GF, kb.dg, a.cu_seqlens,
-                     a.chunk_off, a.T, a.B * a.T, a.N, NT, a.Hk, a.HV);
+                     a.chunk_off, a.T, a.B * a.T, a.N, NT, nslots, a.Hk, a.HV);
   return hipGetLastError();
 }
 
