@@ -602,11 +602,15 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   } else {
     // =================== mover wave: global <-> LDS traffic
     // Direct-to-LDS loads of the next chunk into the other stage; each mover
-    // also stores a quarter of the o tile.  GDN: mover 0 loads k, 1 q,
-    // 2 Ainv and v, 3 Aqk and the gate rows.  KDA: mover 0 K o e^G and v,
+    // also stores a quarter of the o tile.  Load sets (mr): GDN: 0 k, 1 q,
+    // 2 Ainv and v, 3 Aqk and the gate rows.  KDA: 0 K o e^G and v,
     // 1 Q o e^G, the beta row and the decay row, 2 K o e^{G_last - G},
     // 3 Ainv and Aqk.
     const int mv = ridx;
+    // load set of this mover: movers 0 and 1 share SIMDs with the state
+    // waves, which leave them fewer issue slots, so they take the lighter
+    // sets (GDN: Ainv + v, Aqk + gates; KDA: K o e^{G_last - G}, Ainv + Aqk)
+    const int mr = (mv + 2) & 3;
     // per-lane byte offsets within a full chunk: LDS slot (row, unit')
     // receives global unit unit' ^ swizzle(row)
     uint32_t o_qk[NQK], o_a[8], o_v[4];
@@ -637,27 +641,27 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       const int rg = lane < nr ? lane : nr - 1;
       const float* gp = GF + (size_t)j * 4 * gs + c0 + rg;
       if constexpr (KDA) {
-        if (mv == 0) {
+        if (mr == 0) {
           dma_qk_tile<DK>(ksrc + xo, o_qk, nr, qk_row, dK, lane);
           dma_v_tile(vc, o_v, nr, v_row, dV, lane);
-        } else if (mv == 1) {
+        } else if (mr == 1) {
           dma_qk_tile<DK>(qsrc + xo, o_qk, nr, qk_row, dQ, lane);
           dma4(gp + 2 * gs, dG + 512);
           const float* dp = DG + ((size_t)(chunk0 + (c0 - bos) / BT) * HV + j) * DK;
 #pragma unroll
           for (int i = 0; i < DK / 64; ++i) dma4(dp + 64 * i + lane, dD + 256 * i);
-        } else if (mv == 2) {
+        } else if (mr == 2) {
           dma_qk_tile<DK>(reinterpret_cast<const char*>(ktop) + xo, o_qk, nr, qk_row, dT, lane);
         } else {
           dma_a_tile(ac0, o_a, nr, a_row, dAi, lane);
           dma_a_tile(ac1, o_a, nr, a_row, dAq, lane);
         }
       } else {
-        if (mv < 2) {
-          dma_qk_tile<DK>(pick(mv == 0, ksrc, qsrc) + xo, o_qk, nr, qk_row, mv == 0 ? dK : dQ, lane);
+        if (mr < 2) {
+          dma_qk_tile<DK>(pick(mr == 0, ksrc, qsrc) + xo, o_qk, nr, qk_row, mr == 0 ? dK : dQ, lane);
         } else {
-          dma_a_tile(pick(mv == 2, ac0, ac1), o_a, nr, a_row, mv == 2 ? dAi : dAq, lane);
-          if (mv == 2) {
+          dma_a_tile(pick(mr == 2, ac0, ac1), o_a, nr, a_row, mr == 2 ? dAi : dAq, lane);
+          if (mr == 2) {
             dma_v_tile(vc, o_v, nr, v_row, dV, lane);
           } else {
 #pragma unroll
@@ -692,7 +696,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       }
       touch4(p, sink);
       const int rr = lane < nr ? lane : nr - 1;
-      if (mv == (KDA ? 0 : 2)) touch4(v + ((size_t)(c0 + rr) * HV + j) * V + v0, sink);
+      if (mr == (KDA ? 0 : 2)) touch4(v + ((size_t)(c0 + rr) * HV + j) * V + v0, sink);
       else if (KDA) touch4(GF + (size_t)j * 4 * gs + 2 * gs + c0 + rr, sink);
       else touch4(GF + (size_t)j * 4 * gs + (lane >> 1 & 3) * gs + c0 + (nr > 32 ? 32 * (lane & 1) : 0), sink);
     };
