@@ -178,9 +178,11 @@ def bench_kda(args, binding, workloads, torch):
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     gk, beta = inp.gk.to(dev), inp.beta.to(dev)
     B, T, Hk, HV, K, V = inp.dims
+    ws = torch.empty(binding.workspace_bytes(B, T, Hk, HV, K, V, B, torch.bfloat16, kda=True),
+                     dtype=torch.uint8, device=dev)
 
     def step():
-        binding.kda_chunk_fwd(q, k, v, gk, beta, scale=inp.scale)
+        binding.kda_chunk_fwd(q, k, v, gk, beta, scale=inp.scale, workspace=ws)
 
     ms, _ = timed(step, max(args.steps // 2, 1), 1)
     flops = method_flops_per_token(K, V) * B * T * HV
