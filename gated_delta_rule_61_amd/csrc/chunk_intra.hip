@@ -42,11 +42,8 @@ using namespace intra;
 // -------------------------------------------------------------------------
 // GDN intra kernel (scalar gate)
 // -------------------------------------------------------------------------
-#ifndef GDN_INTRA_WPE
-#define GDN_INTRA_WPE 3
-#endif
 template <typename T, int DK, typename C = typename ComputeOf<T>::type>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GDN_INTRA_WPE))) void gdn_intra_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void gdn_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, C* __restrict__ Ainv,
     C* __restrict__ Aqk, float* __restrict__ GF, const int64_t* __restrict__ cu,

@@ -293,20 +293,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // wave roles; wave w runs on SIMD w % 4
-#ifndef GDN_SCAN_PLACEMENT
-#define GDN_SCAN_PLACEMENT 0
-#endif
-#if GDN_SCAN_PLACEMENT == 0   // state, state, helper, helper | 4 movers
+  // wave roles; wave w runs on SIMD w % 4: state waves on SIMDs 0 and 1,
+  // helpers on 2 and 3, one mover on each SIMD (placing both state waves
+  // on one SIMD, or a state wave beside the other block's helper, was slower)
   const int role = w < 2 ? 0 : w < 4 ? 1 : 2;
   const int ridx = w < 4 ? (w & 1) : w - 4;
-#elif GDN_SCAN_PLACEMENT == 1 // both state waves on SIMD 0, both helpers on SIMD 1
-  const int role = (w & 3) == 0 ? 0 : (w & 3) == 1 ? 1 : 2;
-  const int ridx = (w & 3) < 2 ? (w >> 2) : ((w >> 2) * 2 + (w & 3) - 2);
-#else                          // state + helper of the other block on SIMDs 0 and 1
-  const int role = w < 2 ? 0 : (w == 4 || w == 5) ? 1 : 2;
-  const int ridx = w < 2 ? w : (w == 4 || w == 5) ? 5 - w : (w < 4 ? w - 2 : w - 4);
-#endif
   const bool is_state = role == 0;
   const int cb = ridx;                    // 16-column block (state, helper) / mover index
   const int n = lane & 15, g = lane >> 4;

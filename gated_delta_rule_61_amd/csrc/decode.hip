@@ -216,8 +216,11 @@ __device__ __forceinline__ float from_lane(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * l, __builtin_bit_cast(int, x)));
 }
 
+// At most 128 VGPRs, so that 4 work-groups share a CU (144 without the cap,
+// 3 per CU; the cap costs no spills, and the fourth work-group hides more of
+// each one's load latency: -4 % at T = 4).
 template <int NTOK>
-__global__ __launch_bounds__(256) void gdn_decode_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gdn_decode_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ ga,
     const bf16_t* __restrict__ gb, const float* __restrict__ A_log,
@@ -364,34 +367,30 @@ __global__ __launch_bounds__(256) void gdn_decode_mfma_kernel(
   }
 
   // ---- the update's constant operands.  S_T^T = G_T S0^T + K W^T:
-  // G_T S0^T is a bf16 MFMA of the raw state fragments with G_T (as a bf16
-  // hi + lo pair) on a selector (block h's A row r picks k-slot
-  // 8 (r / 4) + 4h + r % 4 of the 32-channel block); K W^T an fp32 MFMA
+  // S0^T comes out of a bf16 MFMA of the raw state fragments with a 0 / 1
+  // selector (block h's A row r picks k-slot 8 (r / 4) + 4h + r % 4 of the
+  // 32-channel block; exact), scaled by G_T in fp32; K W^T is an fp32 MFMA
   // (16x16x4: lane (n, g) holds the A element [channel row n][token g] and
   // the B element [token g][row n]).
   float ksg = 0.f;
 #pragma unroll
   for (int s2 = 0; s2 < NTOK; ++s2) ksg = g == s2 ? ks[s2] : ksg;
   const float GT = Gt[NTOK - 1];
-  uint4 sel[2][2];   // [h][hi, lo]
+  uint4 sel[2];   // [h]: bf16 1.0 in the selected slot
   {
-    const uint32_t gh = pack_bf2(GT, 0.f) & 0xFFFFu;
-    const uint32_t gl = pack_bf2(GT - __builtin_bit_cast(float, gh << 16), 0.f) & 0xFFFFu;
+    constexpr uint32_t kOne = 0x3F80u;   // bf16 1.0
     const bool on = g == (n >> 2);
     const int e = n & 3;   // slot 4h + e of the lane's 8
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      uint32_t wds[4];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const uint32_t gv2 = p == 0 ? gh : gl;
-        uint32_t wds[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int e0 = 2 * d - 4 * h;   // slots 2d, 2d + 1 relative to 4h
-          wds[d] = (on && e0 == (e & ~1)) ? (gv2 << (16 * (e & 1))) : 0u;
-        }
-        sel[h][p] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+      for (int d = 0; d < 4; ++d) {
+        const int e0 = 2 * d - 4 * h;   // slots 2d, 2d + 1 relative to 4h
+        wds[d] = (on && e0 == (e & ~1)) ? (kOne << (16 * (e & 1))) : 0u;
       }
+      sel[h] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+    }
   }
   float ak[KB][2];
 #pragma unroll
@@ -444,8 +443,9 @@ __global__ __launch_bounds__(256) void gdn_decode_mfma_kernel(
       uint32_t out[4];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        f32x4 c = mma32_bf(sel[h][0], r, f32x4{0.f, 0.f, 0.f, 0.f});
-        c = mma32_bf(sel[h][1], r, c);
+        f32x4 c = mma32_bf(sel[h], r, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] *= GT;
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[kb][h], bu, c, 0, 0, 0);
         out[2 * h] = pack_bf2(c[0], c[1]);
         out[2 * h + 1] = pack_bf2(c[2], c[3]);
