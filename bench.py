@@ -7,7 +7,8 @@ bf16 q/k/v, fp32 gate/beta/state, zero h0, final state stored; inputs are
 seeded synthetic tensors already resident in HBM.  ``value`` is prefill
 tokens/s (B*T per call).  The same JSON line also carries the decode step
 (B=256, HV=32, K=V=128, bf16 state, T=1 and T=4: tokens/s and state GB/s),
-the KDA prefill (B=2 T=8192 H=32) when built, the per-kernel roofline of the
+the varlen GQA prefill (8 packed sequences, Hk=16, HV=32, h0 in), the KDA
+prefill (B=2 T=8192 H=32), the per-kernel roofline of the
 dominant prefill kernel (live HIP-event timing inside the library, on the
 launch stream) and the fp64 CPU oracle timed on a bounded sample.
 
@@ -69,9 +70,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=16384)
     p.add_argument("--skip-extra", action="store_true", help="prefill workload only")
-    p.add_argument("--only", choices=["prefill", "decode", "kda", "copy"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "kda", "varlen", "copy"], default=None,
                    help="run one workload (for profiling) and print its figures")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache prefill timing")
+    p.add_argument("--decode-batch", type=int, default=256, help="batch of --only decode")
     return p.parse_args()
 
 
@@ -132,8 +134,9 @@ def bench_prefill(args, binding, workloads, torch):
                 cold_ms=sorted(cold)[len(cold) // 2] if cold else None)
 
 
-def bench_decode(args, binding, workloads, torch, T):
-    inp = workloads.decode_b256(T)
+def bench_decode(args, binding, workloads, torch, T, B=256):
+    inp = (workloads.decode_b256(T) if B == 256 else
+           workloads.make_decode(B, T, 16, 32, 128, 128, seed=1004, name=f"decode_b{B}"))
     dev = "cuda:0"
     t = {n: getattr(inp, n).to(dev) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
     state = inp.state.to(dev)
@@ -189,6 +192,44 @@ def bench_kda(args, binding, workloads, torch):
     return {"workload": f"kda_chunk_fwd B={B} T={T} H={HV} K=V={K} bf16",
             "ms_per_call": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "mfma_frac_method_flops": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def bench_varlen(args, binding, workloads, torch):
+    """GDN varlen + GQA: 8 packed sequences, h0 in, ht out."""
+    inp = workloads.gdn_varlen_gqa()
+    dev = "cuda:0"
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    g, beta, h0 = inp.g.to(dev), inp.beta.to(dev), inp.h0.to(dev)
+    cu = inp.cu_seqlens.to(dev)
+    B, T, Hk, HV, K, V = inp.dims
+    N = inp.num_seqs
+    o = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.workspace_bytes(B, T, Hk, HV, K, V, N, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.gdn_chunk_fwd(q, k, v, g, beta, scale=inp.scale, h0=h0, cu_seqlens=cu, out=o,
+                              workspace=ws)
+
+    ms, _ = timed(step, max(args.steps // 2, 1), 1)
+    binding.profile_read()
+    binding.profile_enable(True)
+    for _ in range(max(args.steps // 2, 1)):
+        step()
+    torch.cuda.synchronize()
+    prof = binding.profile_read()
+    binding.profile_enable(False)
+    stage_ms = {s: prof[s][0] / prof[s][1] for s in prof if prof[s][1]}
+    flops = method_flops_per_token(K, V) * T * HV
+    sb = scan_bytes(B, T, Hk, HV, K, V, N, h0=True)
+    lens = (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1]).tolist()
+    return {"workload": f"gdn_chunk_fwd varlen {N} seqs (lengths {lens}), T={T}, Hk={Hk} HV={HV} "
+                        f"K=V={K} bf16, h0 in, ht out",
+            "ms_per_call": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "mfma_frac_method_flops": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kernels_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+            "scan_hbm_frac": round(sb / (stage_ms["scan"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            if stage_ms.get("scan") else None}
 
 
 def source_hash() -> str:
@@ -247,8 +288,9 @@ def main():
     assert torch.cuda.is_available(), "needs a GPU"
 
     if args.only == "decode":
-        print(json.dumps({"decode": {"T1": bench_decode(args, binding, workloads, torch, 1),
-                                     "T4": bench_decode(args, binding, workloads, torch, 4)}}), flush=True)
+        B = args.decode_batch
+        print(json.dumps({"decode": {"T1": bench_decode(args, binding, workloads, torch, 1, B),
+                                     "T4": bench_decode(args, binding, workloads, torch, 4, B)}}), flush=True)
         return
     if args.only == "copy":
         # calibration for the HBM byte counters: a plain 512 MiB device copy
@@ -261,6 +303,9 @@ def main():
         return
     if args.only == "kda":
         print(json.dumps({"kda": bench_kda(args, binding, workloads, torch)}), flush=True)
+        return
+    if args.only == "varlen":
+        print(json.dumps({"varlen": bench_varlen(args, binding, workloads, torch)}), flush=True)
         return
     pf = bench_prefill(args, binding, workloads, torch)
     ms = pf["ms"]
@@ -313,6 +358,11 @@ def main():
     if not args.skip_extra and args.only is None:
         out["decode"] = {"T1": bench_decode(args, binding, workloads, torch, 1),
                          "T4": bench_decode(args, binding, workloads, torch, 4)}
+        # small batches are latency-bound: the kernel's own duration
+        # (kernel_ms_bracketed) is the figure; the loop rate is launch-bound
+        out["decode_b1"] = {"T1": bench_decode(args, binding, workloads, torch, 1, 1),
+                            "T4": bench_decode(args, binding, workloads, torch, 4, 1)}
+        out["varlen"] = bench_varlen(args, binding, workloads, torch)
         try:
             out["kda"] = bench_kda(args, binding, workloads, torch)
         except Exception as e:  # KDA path reports its own status

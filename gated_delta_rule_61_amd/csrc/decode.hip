@@ -6,7 +6,9 @@
 // T <= 4 tokens and written back to bf16 once).  The mapping is wave64-native
 // rather than the page's 4 x 32-lane-warp layout:
 //
-//   one work-group of 256 threads per (batch row, v-head);
+//   one work-group of 256 threads per (batch row, v-head), or, with fewer
+//   pairs than CUs, four work-groups of 64 threads (32 value rows each;
+//   value rows are independent);
 //   thread t owns key columns 8*(t%16) .. +7 of the 8 consecutive value rows
 //   8*(t/16) .. +7, i.e. 64 fp32 state values in registers;
 //   a 16-lane DPP row holds full 128-wide state rows, so pred = S k and
@@ -39,8 +41,8 @@ __device__ __forceinline__ void unpack8(const uint4& r, float (&f)[8]) {
   }
 }
 
-template <int NTOK>
-__global__ __launch_bounds__(256) void gdn_decode_kernel(
+template <int NTOK, int TPB>
+__global__ __launch_bounds__(TPB) void gdn_decode_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ ga,
     const bf16_t* __restrict__ gb, const float* __restrict__ A_log,
@@ -48,12 +50,14 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
     const int32_t* __restrict__ idx, bf16_t* __restrict__ o,
     int H, int HV, int pool, float scale, float sp_beta, float sp_thr,
     int use_norm, float eps) {
-  const int bh = blockIdx.x;
+  constexpr int SPL = 256 / TPB;   // work-groups per (batch row, v-head)
+  const int bh = blockIdx.x / SPL;
+  const int part = blockIdx.x - bh * SPL;
   const int bi = bh / HV;
   const int hv = bh - bi * HV;
   const int hk = hv / (HV / H);
   const int t = threadIdx.x;
-  const int rg = t >> 4;   // row group: value rows 8*rg .. 8*rg + 7
+  const int rg = part * (TPB / 16) + (t >> 4);   // row group: value rows 8*rg .. 8*rg + 7
   const int cl = t & 15;   // key columns 8*cl .. 8*cl + 7
   const int slot = idx ? idx[bi] : bi;
   const bool valid = slot >= 0 && slot < pool;
@@ -190,8 +194,9 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
 // dot products), the T-step solve runs per state row inside one lane, and a
 // fp32 MFMA applies the rank-T update S_T^T = G_T S0^T + K W^T.
 //
-// Work-group = one (batch row, v-head), 4 waves; wave w owns state rows
-// 32w .. 32w + 31 as two 16-row blocks rb.  Lane (n, g) = (lane % 16,
+// Work-group = one (batch row, v-head), 4 waves, or (small batches) one of
+// its waves; wave w owns state rows 32w .. 32w + 31 as two 16-row blocks rb
+// and shares nothing with the other waves.  Lane (n, g) = (lane % 16,
 // lane / 16) holds, for 32-channel block kb, the 8 bf16 state values
 // S0[32w + 16rb + n][32kb + 8g .. + 7] (one 16-byte LDS read; the state
 // reaches LDS in whole rows): the B operand of the bf16 16x16x32 product
@@ -219,8 +224,8 @@ __device__ __forceinline__ float from_lane(float x, int l) {
 // At most 128 VGPRs, so that 4 work-groups share a CU (144 without the cap,
 // 3 per CU; the cap costs no spills, and the fourth work-group hides more of
 // each one's load latency: -4 % at T = 4).
-template <int NTOK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gdn_decode_mfma_kernel(
+template <int NTOK, int WPB>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(4))) void gdn_decode_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ ga,
     const bf16_t* __restrict__ gb, const float* __restrict__ A_log,
@@ -229,16 +234,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
     int H, int HV, int pool, float scale, float sp_beta, float sp_thr,
     int use_norm, float eps) {
   constexpr int KB = DK / 32;
-  // the state of the (row, head), bf16: rows 16 w + r of each wave's two
-  // 16-row blocks (block 0 in sS0, block 1 in sS1)
-  __shared__ uint4 sS0[DV * DK / 16], sS1[DV * DK / 16];
-  const int bh = blockIdx.x;
+  // the state rows of the work-group's waves, bf16: rows 16 lw + r of each
+  // wave's two 16-row blocks (block 0 in sS0, block 1 in sS1)
+  __shared__ uint4 sS0[WPB * 16 * DK / 8], sS1[WPB * 16 * DK / 8];
+  constexpr int SPL = 4 / WPB;   // work-groups per (batch row, v-head)
+  const int bh = blockIdx.x / SPL;
   const int bi = bh / HV;
   const int hv = bh - bi * HV;
   const int hk = hv / (HV / H);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
-  const int wv = threadIdx.x >> 6;
+  const int lw = threadIdx.x >> 6;                        // wave in the work-group
+  const int wv = (blockIdx.x - bh * SPL) * WPB + lw;      // wave of the (row, head)
   const int row0 = 32 * wv;
   const int slot = idx ? idx[bi] : bi;
   const size_t tok0 = (size_t)bi * NTOK;
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
       const int r = row0 + 4 * i + (lane >> 4);
       const int u = (lane & 15) ^ (r & 15);
       __builtin_amdgcn_global_load_lds((gvoid*)(sp + (size_t)r * DK + 8 * u),
-                                       (lchar*)(sS0 + (16 * wv + 4 * i) * 16), 16, 0, 0);
+                                       (lchar*)(sS0 + (16 * lw + 4 * i) * 16), 16, 0, 0);
     }
   }
 
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
   auto block = [&](int rb, uint4* sb, float (&ov)[NTOK], auto mid) __attribute__((always_inline)) {
     // lane (n, g) of channel block kb: S0[row][32kb + 8g .. + 7]
     auto frag = [&](int kb) __attribute__((always_inline)) -> uint4& {
-      return sb[(16 * wv + n) * 16 + ((4 * kb + g) ^ n)];
+      return sb[(16 * lw + n) * 16 + ((4 * kb + g) ^ n)];
     };
     uint4 fr[KB];
 #pragma unroll
@@ -461,7 +468,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
       const int rl = 4 * i + (lane >> 4);   // row within the block
       const int u = lane & 15;
       *reinterpret_cast<uint4*>(sp + (size_t)(row0 + 16 * rb + rl) * DK + 8 * u) =
-          sb[(16 * wv + rl) * 16 + (u ^ rl)];
+          sb[(16 * lw + rl) * 16 + (u ^ rl)];
     }
     if (g == 1) {
 #pragma unroll
@@ -483,25 +490,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
     }
   });
 #pragma unroll
-  for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(sS1)[(16 * wv + 4 * i) * 16 + lane] = raw1[i];
+  for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(sS1)[(16 * lw + 4 * i) * 16 + lane] = raw1[i];
   store_block(0, sS0, ov0);
   block(1, sS1, ov1, []() {});
   store_block(1, sS1, ov1);
 }
 
+// With fewer (batch row, v-head) pairs than the 256 CUs, each pair is split
+// over four 64-thread work-groups (measured: -5 % at B = 1, T = 1 and -12 %
+// at B = 1, T = 4 with 32 v-heads; no gain from 16 rows of 32 v-heads on).
+#ifndef GDN_DECODE_SPLIT_BELOW
+#define GDN_DECODE_SPLIT_BELOW 256
+#endif
+
 // T = 1 runs the per-token kernel (the rank-1 step has no products worth
 // MFMA work and its loads / stores cover whole rows); T = 2 .. 4 the MFMA form.
 template <int NTOK>
 hipError_t launch_n(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.B * a.HV));
+  const bool split = (long long)a.B * a.HV < GDN_DECODE_SPLIT_BELOW;
+  const dim3 grid((unsigned)(a.B * a.HV * (split ? 4 : 1)));
   void (*kern)(const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*,
                const float*, const float*, bf16_t*, const int32_t*, bf16_t*, int, int, int,
                float, float, float, int, float);
   if constexpr (NTOK == 1)
-    kern = gdn_decode_kernel<1>;
+    kern = split ? gdn_decode_kernel<1, 64> : gdn_decode_kernel<1, 256>;
   else
-    kern = gdn_decode_mfma_kernel<NTOK>;
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s,
+    kern = split ? gdn_decode_mfma_kernel<NTOK, 1> : gdn_decode_mfma_kernel<NTOK, 4>;
+  hipLaunchKernelGGL(kern, grid, dim3(split ? 64 : 256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
                      (const bf16_t*)a.a, (const bf16_t*)a.b, a.A_log, a.dt_bias,
                      (bf16_t*)a.state, a.idx, (bf16_t*)a.o, a.H, a.HV, a.pool,

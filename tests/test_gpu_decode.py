@@ -48,6 +48,26 @@ def test_decode_small(T):
     _ulp_consistent(s, s_ref)
 
 
+@pytest.mark.parametrize("B,T", [(1, 1), (1, 4), (7, 1), (7, 3), (8, 2), (31, 4)])
+def test_decode_split_grid_sizes(B, T):
+    """Batches on both sides of the work-group split (fewer than 256
+    (batch row, v-head) pairs run four 64-thread work-groups per pair), with
+    the workload's head shape (16 q/k heads, 32 v-heads) and a pool larger
+    than the batch with shuffled slots."""
+    print(f"decode split-grid B={B} T={T}", flush=True)
+    rng = np.random.default_rng(70 + B + T)
+    pool = B + 3
+    idx = rng.permutation(pool)[:B].tolist()
+    inp = workloads.make_decode(B, T, 16, 32, 128, 128, seed=71 + B, pool=pool, indices=idx)
+    o, s, o_ref, s_ref = _run(inp)
+    check("o", o, o_ref, torch.bfloat16)
+    used = np.zeros(pool, bool)
+    used[idx] = True
+    tused = torch.from_numpy(used)
+    check("state", s[tused], s_ref[used], torch.bfloat16)
+    assert torch.equal(s[~tused], inp.state[~tused]), "slots outside the batch changed"
+
+
 def test_decode_no_norm():
     inp = workloads.make_decode(2, 2, 1, 2, 128, 128, seed=61)
     inp.q = (inp.q.float() * 0.1).to(torch.bfloat16)
