@@ -171,7 +171,7 @@ def bench_decode(args, binding, workloads, torch, T, B=256):
         "total_GBps": round((state_bytes + other) / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round((state_bytes + other) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_ms_bracketed": round(kms, 5),
-        "measured_bytes": measured_traffic(f"decode:T{T}"),
+        "measured_bytes": measured_traffic(f"decode:T{T}" if B == 256 else f"decode_b{B}:T{T}"),
     }
 
 
@@ -229,7 +229,8 @@ def bench_varlen(args, binding, workloads, torch):
             "mfma_frac_method_flops": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "kernels_ms": {s: round(v, 5) for s, v in stage_ms.items()},
             "scan_hbm_frac": round(sb / (stage_ms["scan"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-            if stage_ms.get("scan") else None}
+            if stage_ms.get("scan") else None,
+            "scan_measured_bytes": measured_traffic("varlen:scan")}
 
 
 def source_hash() -> str:
