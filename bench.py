@@ -8,7 +8,8 @@ seeded synthetic tensors already resident in HBM.  ``value`` is prefill
 tokens/s (B*T per call).  The same JSON line also carries the decode step
 (B=256, HV=32, K=V=128, bf16 state, T=1 and T=4: tokens/s and state GB/s),
 the varlen GQA prefill (8 packed sequences, Hk=16, HV=32, h0 in), the KDA
-prefill (B=2 T=8192 H=32), the per-kernel roofline of the
+prefill (B=2 T=8192 H=32), the prefill -> decode state handoff (256 states
+into a bf16 pool), the per-kernel roofline of the
 dominant prefill kernel (live HIP-event timing inside the library, on the
 launch stream) and the fp64 CPU oracle timed on a bounded sample.
 
@@ -70,7 +71,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=16384)
     p.add_argument("--skip-extra", action="store_true", help="prefill workload only")
-    p.add_argument("--only", choices=["prefill", "decode", "kda", "varlen", "copy"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "kda", "varlen", "handoff", "copy"], default=None,
                    help="run one workload (for profiling) and print its figures")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache prefill timing")
     p.add_argument("--decode-batch", type=int, default=256, help="batch of --only decode")
@@ -233,6 +234,28 @@ def bench_varlen(args, binding, workloads, torch):
             "scan_measured_bytes": measured_traffic("varlen:scan")}
 
 
+def bench_handoff(args, binding, workloads, torch):
+    """Prefill -> decode handoff: 256 sequences' fp32 final states (32 heads,
+    K = V = 128) into a shuffled 256-slot bf16 pool."""
+    dev = "cuda:0"
+    N, HV, K, V = 256, 32, 128, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1005)
+    ht = torch.randn((N, HV, V, K), generator=gen, device=dev) * 0.1
+    pool = torch.zeros((N, HV, V, K), dtype=torch.bfloat16, device=dev)
+    idx = torch.randperm(N, generator=gen, device=dev).to(torch.int32)
+
+    def step():
+        binding.state_to_pool(ht, pool, idx)
+
+    ms, _ = timed(step, args.steps, args.warmup)
+    nbytes = N * HV * V * K * (4 + 2)
+    return {"workload": f"gdn_state_to_pool N={N} HV={HV} K=V={K}, fp32 -> bf16, shuffled slots",
+            "ms_per_call": round(ms, 5), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes, "measured_bytes": measured_traffic("handoff")}
+
+
 def source_hash() -> str:
     """Hash of the kernel sources (the same hash the profile summaries record)."""
     import glob
@@ -305,6 +328,9 @@ def main():
     if args.only == "kda":
         print(json.dumps({"kda": bench_kda(args, binding, workloads, torch)}), flush=True)
         return
+    if args.only == "handoff":
+        print(json.dumps({"handoff": bench_handoff(args, binding, workloads, torch)}), flush=True)
+        return
     if args.only == "varlen":
         print(json.dumps({"varlen": bench_varlen(args, binding, workloads, torch)}), flush=True)
         return
@@ -364,6 +390,7 @@ def main():
         out["decode_b1"] = {"T1": bench_decode(args, binding, workloads, torch, 1, 1),
                             "T4": bench_decode(args, binding, workloads, torch, 4, 1)}
         out["varlen"] = bench_varlen(args, binding, workloads, torch)
+        out["handoff"] = bench_handoff(args, binding, workloads, torch)
         try:
             out["kda"] = bench_kda(args, binding, workloads, torch)
         except Exception as e:  # KDA path reports its own status

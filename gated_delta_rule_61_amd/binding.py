@@ -47,6 +47,8 @@ _SIGNATURES = {
                             _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_float, _c_float, _c_float, _c_int, _c_float, _c_void_p]),
+    "gdn_state_to_pool": (_c_int, [_c_void_p, _c_void_p, _c_void_p,
+                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
 }
 
 _lib = None
@@ -110,7 +112,7 @@ def _need(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype], sh
         raise ValueError(f"{name} must be contiguous")
 
 
-STAGES = ("varlen_tables", "intra", "scan", "decode")
+STAGES = ("varlen_tables", "intra", "scan", "decode", "handoff")
 
 
 def profile_enable(on: bool = True) -> None:
@@ -244,3 +246,23 @@ def gdn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tenso
                             float(scale), float(softplus_beta), float(softplus_threshold),
                             1 if use_qk_l2norm else 0, float(eps), _stream(dev)))
     return o
+
+
+def state_to_pool(ht: torch.Tensor, pool_state: torch.Tensor,
+                  indices: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Write final prefill states ``ht`` [N,HV,V,K] fp32 into the bf16 decode
+    pool ``pool_state`` [pool,HV,V,K] (in place) at slots ``indices`` [N]
+    (int32; None = slot n), rounded to nearest bf16.  Returns ``pool_state``."""
+    if ht.dim() != 4 or pool_state.dim() != 4:
+        raise ValueError("ht must be [N, HV, V, K] and pool_state [pool, HV, V, K]")
+    N, HV, V, K = ht.shape
+    dev = ht.device
+    _need(ht, "ht", torch.float32, None, dev)
+    _need(pool_state, "pool_state", torch.bfloat16, (pool_state.shape[0], HV, V, K), dev)
+    if indices is not None:
+        if indices.dtype != torch.int32:
+            indices = indices.to(torch.int32)
+        _need(indices, "indices", torch.int32, (N,), dev)
+    _check(lib().gdn_state_to_pool(_ptr(ht), _ptr(indices), _ptr(pool_state),
+                                   N, HV, K, V, pool_state.shape[0], _stream(dev)))
+    return pool_state

@@ -400,6 +400,28 @@ int gdn_decode(const void* q, const void* k, const void* v, const void* a, const
   return ok();
 }
 
+int gdn_state_to_pool(const float* ht, const int32_t* indices, void* pool_state, int N, int HV,
+                      int K, int V, int pool, void* stream) {
+  if (N < 0 || HV <= 0 || K <= 0 || V <= 0 || pool < 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "sizes must be positive: N=%d HV=%d K=%d V=%d pool=%d", N,
+                HV, K, V, pool);
+  if (((long long)V * K) % 8 != 0)
+    return fail(GDN_ERR_UNSUPPORTED, "V * K must be a multiple of 8 (got V=%d K=%d)", V, K);
+  if (!indices && pool < N)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "identity slots need pool >= N (pool=%d N=%d)", pool, N);
+  if ((long long)(N > pool ? N : pool) * HV * V * K >= (1LL << 40))
+    return fail(GDN_ERR_UNSUPPORTED, "state arrays too large");
+  if (N == 0) return ok();
+  if (!ht || !pool_state) return fail(GDN_ERR_INVALID_ARGUMENT, "ht and pool_state are required");
+  if (!aligned16(ht) || !aligned16(pool_state))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "ht and pool_state must be 16-byte aligned");
+  prof_begin(GDN_STAGE_HANDOFF, (hipStream_t)stream);
+  const hipError_t e = launch_state_to_pool(ht, indices, pool_state, N, HV, K, V, pool, (hipStream_t)stream);
+  prof_end(GDN_STAGE_HANDOFF, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int gdn_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;

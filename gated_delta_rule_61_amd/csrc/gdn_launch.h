@@ -24,6 +24,10 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// prefill -> decode handoff: fp32 [N, HV, V, K] into bf16 pool slots
+hipError_t launch_state_to_pool(const float* ht, const int32_t* idx, void* pool_state, int N, int HV,
+                                int K, int V, int pool, hipStream_t s);
+
 // One chunked prefill problem (GDN: gk == nullptr; KDA: g == nullptr).
 struct ChunkArgs {
   const void *q, *k, *v;

@@ -182,6 +182,29 @@ int gdn_decode(const void* q, const void* k, const void* v,
                void* stream);
 
 /*
+ * Prefill -> decode handoff: write final prefill states into a bf16 decode
+ * state pool (the prefill's ht fp32 layout and the decode pool's layout are
+ * both [*, HV, V, K], K contiguous: "fla ops/common/chunk_h.py" ht with the
+ * state-V-first layout; "flashinfer gdn_kernels/gdn_decode_bf16_state.py"
+ * initial_state_source / initial_state_indices).
+ *
+ *   ht          [N, HV, V, K]    fp32, caller-owned device memory (read)
+ *   indices     [N] int32 device array: pool slot of sequence n, or NULL
+ *               for slot n (then pool >= N is required).  A slot outside
+ *               [0, pool) is skipped.  Two sequences naming the same slot
+ *               race (undefined result).
+ *   pool_state  [pool, HV, V, K] bf16, written IN PLACE at the named slots
+ *               only; each value is rounded to nearest bf16, ties to even
+ *
+ * Both arrays must be 16-byte aligned and V * K a multiple of 8.  Errors:
+ * GDN_ERR_INVALID_ARGUMENT (sizes, NULL or misaligned pointers),
+ * GDN_ERR_UNSUPPORTED (V * K not a multiple of 8), GDN_ERR_LAUNCH.  Runs
+ * asynchronously on `stream`; allocates nothing.
+ */
+int gdn_state_to_pool(const float* ht, const int32_t* indices, void* pool_state,
+                      int N, int HV, int K, int V, int pool, void* stream);
+
+/*
  * Per-stage timing for measurement tools.  While enabled, every call of the
  * entry points above records a pair of HIP events on the caller's stream
  * around each kernel it launches (stage ids below); this adds two event
@@ -197,7 +220,8 @@ enum {
   GDN_STAGE_INTRA = 1,         /* per-chunk (I + A)^-1 and Aqk                 */
   GDN_STAGE_SCAN = 2,          /* chunk-state scan fused with the output       */
   GDN_STAGE_DECODE = 3,        /* decode step                                  */
-  GDN_STAGE_COUNT = 4
+  GDN_STAGE_HANDOFF = 4,       /* prefill state -> decode pool (bf16)          */
+  GDN_STAGE_COUNT = 5
 };
 int gdn_profile_enable(int on);
 int gdn_profile_read(double* ms, int* counts);

@@ -17,7 +17,8 @@ Sources (cited by page and function in each module):
 * "vLLM kimi_k3 amd ops kda/chunk_intra" -- KDA inter-sub-chunk Aqk/Akk +
   solve_tril fused kernel;
 * "flashinfer gdn_kernels/gdn_decode_bf16_state.py" -- GDN decode with a bf16
-  state (gate, q/k normalisation, per-token state update).
+  state (gate, q/k normalisation, per-token state update) and its state pool,
+  into which a prefill's final state is handed over.
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
 something other than itself (brute-force products of the per-token transition
@@ -30,10 +31,11 @@ from .recurrence import delta_rule_recurrent, gdn_recurrent, kda_recurrent
 from .intra import chunk_intra_matrices
 from .decode import decode_gate, decode_normalize, gdn_decode
 from .bf16 import round_to_bf16
+from .handoff import state_to_pool
 
 __all__ = [
     "delta_rule_recurrent", "gdn_recurrent", "kda_recurrent",
     "chunk_intra_matrices",
     "decode_gate", "decode_normalize", "gdn_decode",
-    "round_to_bf16",
+    "round_to_bf16", "state_to_pool",
 ]

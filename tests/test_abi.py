@@ -116,3 +116,24 @@ def test_binding_raises_without_cuda_tensors():
     q = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError):
         binding.gdn_chunk_fwd(q, q, q, None, torch.zeros(1, 4, 1))
+
+
+def _pool(L, ht=None, idx=None, pool_state=None, N=2, HV=2, K=128, V=128, pool=2, st=None):
+    return L.gdn_state_to_pool(ht, idx, pool_state, N, HV, K, V, pool, st)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(N=-1), 1, b"sizes must be positive"),
+    (dict(HV=0), 1, b"sizes must be positive"),
+    (dict(K=3, V=5, ht=FAKE, pool_state=FAKE), 2, b"multiple of 8"),
+    (dict(pool=1, ht=FAKE, pool_state=FAKE), 1, b"pool >= N"),
+    (dict(ht=None, pool_state=FAKE), 1, b"required"),
+    (dict(ht=FAKE + 4, pool_state=FAKE), 1, b"16-byte aligned"),
+])
+def test_state_to_pool_rejects(L, kw, status, msg):
+    assert _pool(L, **kw) == status
+    assert msg in L.gdn_last_error()
+
+
+def test_state_to_pool_empty_is_a_no_op(L):
+    assert _pool(L, N=0, pool=0) == 0

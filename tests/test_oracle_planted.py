@@ -70,3 +70,36 @@ def test_intra_mutant_is_caught(old, new):
     ok_q = np.allclose(Aqk, Aqk_l, atol=1e-10)
     ok_i = np.allclose(Ainv[0, :, 0, :9], X, atol=1e-10)
     assert not (ok_q and ok_i)
+
+
+HANDOFF_MUTATIONS = [
+    ("out[p] = round_to_bf16(ht[n])", "out[p] = np.floor(ht[n] * 128) / 128"),   # not the bf16 rounding
+    ("out[p] = round_to_bf16(ht[n])", "out[n] = round_to_bf16(ht[n])"),          # slot index ignored
+    ("if 0 <= p < P:", "if 0 <= p <= P - 2:"),                                   # last slot skipped
+]
+
+
+@pytest.mark.parametrize("old,new", HANDOFF_MUTATIONS)
+def test_handoff_mutant_is_caught(old, new):
+    import oracle.handoff as handoff
+    from tests import test_oracle_handoff as pins
+    src = inspect.getsource(handoff)
+    assert old in src, old
+    src = src.replace(old, new, 1).replace("from .bf16 import", "from oracle.bf16 import")
+    src = src.replace("from .recurrence import", "from oracle.recurrence import")
+    m = types.ModuleType("handoff_mutant")
+    exec(compile(src, "<mutant>", "exec"), m.__dict__)
+    real = pins.oracle.state_to_pool
+    pins.oracle.state_to_pool = m.state_to_pool
+    try:
+        failed = 0
+        for t in (pins.test_handoff_matches_torch_cast_and_index_copy,
+                  pins.test_handoff_identity_and_skipped_slots,
+                  pins.test_handoff_rounding_is_nearest_even_at_planted_ties):
+            try:
+                t()
+            except AssertionError:
+                failed += 1
+        assert failed > 0, "the handoff pins accepted a planted mistake"
+    finally:
+        pins.oracle.state_to_pool = real

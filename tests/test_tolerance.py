@@ -43,3 +43,27 @@ def test_fp32_bar():
     check("o", ref + 9e-5, ref, torch.float32)
     with pytest.raises(AssertionError):
         check("o", ref + 1.1e-4, ref, torch.float32)
+
+
+def test_two_stores_bar():
+    """Two paths that store a value as bf16 twice (the second store after a
+    factor near 1) may land a full ulp apart at the first store; stores=2
+    accepts that and still rejects a planted 3 % * RMS error."""
+    rng = np.random.default_rng(4)
+    x = _heavy_tailed(1 << 16, 5)
+    bf = lambda a: torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).double().numpy()
+    ref_mid = bf(x)                                  # oracle path: exact value stored once
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(ref_mid) + 1e-300)) - 7)
+    gpu_mid = ref_mid + ulp * rng.choice([-1.0, 1.0], x.size)   # the other path: one ulp away
+    f = 0.97
+    ref = ref_mid * f                                # second step, unrounded on the oracle side
+    got = bf(gpu_mid * f)                            # ... stored again on the GPU side
+    with pytest.raises(AssertionError):
+        check("s", got, ref, torch.bfloat16)
+    check("s", got, ref, torch.bfloat16, stores=2)
+    rms = np.sqrt(np.mean(ref ** 2))
+    bad = got.copy()
+    i = int(np.argmin(np.abs(np.abs(ref) - rms)))
+    bad[i] += 0.03 * rms + 3 * 2.0 ** -8 * abs(ref[i])
+    with pytest.raises(AssertionError):
+        check("s", bad, ref, torch.bfloat16, stores=2)
