@@ -9,7 +9,7 @@ tokens/s (B*T per call).  The same JSON line also carries the decode step
 (B=256, HV=32, K=V=128, bf16 state, T=1 and T=4: tokens/s and state GB/s),
 the varlen GQA prefill (8 packed sequences, Hk=16, HV=32, h0 in), the KDA
 prefill (B=2 T=8192 H=32), the prefill -> decode state handoff (256 states
-into a bf16 pool), the per-kernel roofline of the
+into a bf16 pool), the prefill with state snapshots, the per-kernel roofline of the
 dominant prefill kernel (live HIP-event timing inside the library, on the
 launch stream) and the fp64 CPU oracle timed on a bounded sample.
 
@@ -234,6 +234,32 @@ def bench_varlen(args, binding, workloads, torch):
             "scan_measured_bytes": measured_traffic("varlen:scan")}
 
 
+def bench_snapshots(args, binding, workloads, torch, base_ms):
+    """The headline prefill with fp32 state snapshots every 64 tokens (every
+    chunk, the densest setting) and every 1024 tokens."""
+    inp = workloads.gdn_bf16_b4_t4096()
+    dev = "cuda:0"
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    g, beta = inp.g.to(dev), inp.beta.to(dev)
+    B, T, Hk, HV, K, V = inp.dims
+    o = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.workspace_bytes(B, T, Hk, HV, K, V, B, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+    res = {}
+    for S in (64, 1024):
+        hs = torch.empty((binding.snapshot_count(B, T, S), HV, V, K), dtype=torch.float32, device=dev)
+
+        def step():
+            binding.gdn_chunk_fwd(q, k, v, g, beta, scale=inp.scale, out=o, workspace=ws,
+                                  split_size=S, h_snap=hs)
+
+        ms, _ = timed(step, max(args.steps // 2, 1), 1)
+        res[f"split{S}"] = {"ms_per_call": round(ms, 5), "overhead_vs_no_snapshots": round(ms / base_ms - 1, 4),
+                            "snapshot_MB": round(hs.numel() * 4 / 1e6, 1)}
+        del hs
+    return res
+
+
 def bench_handoff(args, binding, workloads, torch):
     """Prefill -> decode handoff: 256 sequences' fp32 final states (32 heads,
     K = V = 128) into a shuffled 256-slot bf16 pool."""
@@ -391,6 +417,7 @@ def main():
                             "T4": bench_decode(args, binding, workloads, torch, 4, 1)}
         out["varlen"] = bench_varlen(args, binding, workloads, torch)
         out["handoff"] = bench_handoff(args, binding, workloads, torch)
+        out["snapshots"] = bench_snapshots(args, binding, workloads, torch, ms)
         try:
             out["kda"] = bench_kda(args, binding, workloads, torch)
         except Exception as e:  # KDA path reports its own status

@@ -34,11 +34,11 @@ _SIGNATURES = {
     "gdn_chunk_fwd_workspace_bytes": (_c_size_t, [_c_int] * 8),
     "kda_chunk_fwd_workspace_bytes": (_c_size_t, [_c_int] * 8),
     "gdn_chunk_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float,
-                               _c_void_p, _c_void_p, _c_void_p, _c_int,
+                               _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_int,
                                _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "kda_chunk_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float,
-                               _c_void_p, _c_void_p, _c_void_p, _c_int,
+                               _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_int,
                                _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "gdn_profile_enable": (_c_int, [_c_int]),
@@ -156,13 +156,40 @@ def _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, gate, gate_shape_ta
     return B, T, Hk, HV, K, V, N, dev, io
 
 
+def snapshot_count(B: int, T: int, split_size: int, cu_seqlens: Optional[torch.Tensor] = None) -> int:
+    """Number of state snapshots of a call: sum over sequences of
+    ceil(length / split_size).  With ``cu_seqlens`` this reads the (device)
+    boundaries back to the host."""
+    if cu_seqlens is None:
+        return B * ((T + split_size - 1) // split_size)
+    cu = cu_seqlens.cpu().clamp(0, T)
+    lens = (cu[1:] - cu[:-1]).clamp(min=0)
+    return int(((lens + split_size - 1) // split_size).sum())
+
+
+def _snapshots(B, T, HV, V, K, N, dev, split_size, h_snap, cu_seqlens):
+    if split_size is None:
+        return None
+    if split_size <= 0 or split_size % 64:
+        raise ValueError("split_size must be a positive multiple of 64")
+    if h_snap is None:
+        h_snap = torch.empty((snapshot_count(B, T, split_size, cu_seqlens), HV, V, K),
+                             dtype=torch.float32, device=dev)
+    _need(h_snap, "h_snap", torch.float32, (h_snap.shape[0], HV, V, K), dev)
+    return h_snap
+
+
 def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
                   beta: torch.Tensor, scale: Optional[float] = None,
                   h0: Optional[torch.Tensor] = None, output_final_state: bool = True,
                   cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
-                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """GDN chunked prefill.  Returns (o [B,T,HV,V], ht [N,HV,V,K] fp32 or None)."""
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  split_size: Optional[int] = None, h_snap: Optional[torch.Tensor] = None):
+    """GDN chunked prefill.  Returns (o [B,T,HV,V], ht [N,HV,V,K] fp32 or None),
+    and the state snapshots [S,HV,V,K] fp32 as a third element when
+    ``split_size`` is given (``h_snap`` may be passed preallocated)."""
     B, T, Hk, HV, K, V, N, dev, io = _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, g, (), "g")
+    hs = _snapshots(B, T, HV, V, K, N, dev, split_size, h_snap, cu_seqlens)
     if scale is None:
         scale = K ** -0.5
     o = torch.empty((B, T, HV, V), dtype=io, device=dev) if out is None else out
@@ -172,23 +199,26 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _check(lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
-                               _ptr(h0), _ptr(ht), _ptr(cu_seqlens), N,
+                               _ptr(h0), _ptr(ht), _ptr(hs), split_size or 0, _ptr(cu_seqlens), N,
                                B, T, Hk, HV, K, V, chunk_size, _io_code(io),
                                _ptr(o), _ptr(workspace), workspace.numel(), _stream(dev)))
-    return o, ht
+    return (o, ht) if hs is None else (o, ht, hs)
 
 
 def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,
                   beta: torch.Tensor, scale: Optional[float] = None,
                   h0: Optional[torch.Tensor] = None, output_final_state: bool = True,
                   cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
-                  return_intra: bool = True, workspace: Optional[torch.Tensor] = None):
+                  return_intra: bool = True, workspace: Optional[torch.Tensor] = None,
+                  split_size: Optional[int] = None, h_snap: Optional[torch.Tensor] = None):
     """KDA chunked prefill.  Returns (o, ht, Aqk, Akk_inv); the last two are
-    [B,T,HV,64] in the io dtype (None when ``return_intra`` is False)."""
+    [B,T,HV,64] in the io dtype (None when ``return_intra`` is False).  With
+    ``split_size`` the state snapshots follow as a fifth element."""
     if gk is None:
         raise ValueError("gk is required")
     B, T, Hk, HV, K, V, N, dev, io = _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, gk,
                                                    (q.shape[-1],), "gk")
+    hs = _snapshots(B, T, HV, V, K, N, dev, split_size, h_snap, cu_seqlens)
     if scale is None:
         scale = K ** -0.5
     o = torch.empty((B, T, HV, V), dtype=io, device=dev)
@@ -201,11 +231,11 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.T
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _check(lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gk), _ptr(beta), float(scale),
-                               _ptr(h0), _ptr(ht), _ptr(cu_seqlens), N,
+                               _ptr(h0), _ptr(ht), _ptr(hs), split_size or 0, _ptr(cu_seqlens), N,
                                B, T, Hk, HV, K, V, chunk_size, _io_code(io),
                                _ptr(o), _ptr(Aqk), _ptr(Akk), _ptr(workspace), workspace.numel(),
                                _stream(dev)))
-    return o, ht, Aqk, Akk
+    return (o, ht, Aqk, Akk) if hs is None else (o, ht, Aqk, Akk, hs)
 
 
 def gdn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor, b: torch.Tensor,

@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     const typename C::OPT* __restrict__ top, int op_rows, int op_head_div,
     const typename C::IOT* __restrict__ v, const float* __restrict__ GF,
     const float* __restrict__ DG, float scale, const float* __restrict__ h0,
-    float* __restrict__ ht, const typename C::P* __restrict__ Ainv,
+    float* __restrict__ ht, float* __restrict__ hs, int nts, const typename C::P* __restrict__ Ainv,
     const typename C::P* __restrict__ Aqk, typename C::IOT* __restrict__ o,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ coff,
     const int32_t* __restrict__ order, int Tlen, int ttot, int NT, int N, int HV, int V) {
@@ -333,11 +333,22 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
                cG = (size_t)BT * sG, cD = (size_t)HV * DK;
 
   const int NC = (eos - bos + BT - 1) / BT;
+  // state snapshots: the state at the start of every nts-th chunk
+  const size_t sbase = hs ? (size_t)snapshot_offset(cu, n, Tlen, nts * BT) : 0;
 
   // One chunk: compute from `cur`, prefetch the next chunk into `nxt`.
   auto step = [&](RT& cur, RT& nxt, int ic) {
     const int c0 = bos + ic * BT;
     const int nrow = eos - c0 < BT ? eos - c0 : BT;
+    if (hs && ic % nts == 0) {
+      float* hp = hs + ((sbase + ic / nts) * HV + j) * (size_t)V * DK;
+#pragma unroll
+      for (int rb2 = 0; rb2 < RB; ++rb2)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          *reinterpret_cast<float4*>(hp + (size_t)(v0 + 16 * cb + row) * DK + WR * w + 16 * rb2 + 4 * grp) =
+              make_float4(St[rb2][cb][0], St[rb2][cb][1], St[rb2][cb][2], St[rb2][cb][3]);
+    }
     // update operand^T into LDS from the loader registers
 #pragma unroll
     for (int e = 0; e < 8; ++e) put_channel<C::TPT>(&sKt[8 * cg + e][C::TPT * tg], cur.kt, e);
@@ -482,7 +493,7 @@ hipError_t launch_scan_c(const ChunkArgs& a, const ScanArgs& sa, hipStream_t s) 
   hipLaunchKernelGGL((chunk_scan_kernel<C>), dim3((unsigned)nblk), dim3(256), 0, s,
                      (const OPT*)sa.x, (const OPT*)sa.op, (const OPT*)sa.t, sa.op_rows,
                      sa.op_head_div, (const IOT*)a.v, (const float*)a.GF, sa.dg, a.scale, a.h0,
-                     a.ht, (const P*)a.Ainv, (const P*)a.Aqk, (IOT*)a.o, a.cu_seqlens, sa.coff,
+                     a.ht, a.hs, a.split_chunks, (const P*)a.Ainv, (const P*)a.Aqk, (IOT*)a.o, a.cu_seqlens, sa.coff,
                      a.seq_order, a.T, a.B * a.T, sa.NT, a.N, a.HV, a.V);
   return hipGetLastError();
 }

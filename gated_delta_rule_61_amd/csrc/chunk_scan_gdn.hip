@@ -266,7 +266,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     const void* __restrict__ qop, const void* __restrict__ kop, const f16_t* __restrict__ ktop,
     const bf16_t* __restrict__ v, const float* __restrict__ GF, const float* __restrict__ DG,
     const f16_t* __restrict__ Ainv, const f16_t* __restrict__ Aqk, float scale,
-    const float* __restrict__ h0, float* __restrict__ ht, bf16_t* __restrict__ o,
+    const float* __restrict__ h0, float* __restrict__ ht, float* __restrict__ hs, int nts,
+    bf16_t* __restrict__ o,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ order, const int32_t* __restrict__ coff,
     int Tlen, int ttot, int NT, int N, int Hk, int HV, int V) {
   typedef Lds<DK> L;
@@ -382,10 +383,19 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         for (int h = 0; h < 2; ++h)
           o_tr[kh][s][h] = qk_off<DK>(32 * s + 8 * g + (n >> 2) + 4 * h, 4 * kh + (n & 3));
 
+    // state snapshots: the state at the start of every nts-th chunk
+    const size_t sbase = hs ? (size_t)snapshot_offset(cu, ns, Tlen, nts * BT) : 0;
     auto chunk = [&](auto stg, int c) __attribute__((always_inline)) {
       constexpr bool S1 = decltype(stg)::value;
       const char* sK = S1 ? sK1 : sK0;
       const char* sKt = KDA ? (S1 ? sT1 : sT0) : sK;   // source of the update's K^T
+      if (hs && c % nts == 0) {
+        float* hp = hs + ((sbase + c / nts) * HV + j) * (size_t)V * DK;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          *reinterpret_cast<float4*>(hp + (size_t)(v0 + 16 * cb + n) * DK + perm_row(kb, 4 * g)) =
+              make_float4(St[kb][0], St[kb][1], St[kb][2], St[kb][3]);
+      }
       const char* sAi = S1 ? sAi1 : sAi0;
       const char* sV = S1 ? sV1 : sV0;
       const float (*sG)[BT] = S1 ? sG1 : sG0;
@@ -750,7 +760,8 @@ hipError_t launch_dk(const ChunkArgs& a, const void* qop, const void* kop, const
   const int nblk = ((groups + 7) / 8) * 8 * nvt;
   hipLaunchKernelGGL((gdn_scan_bf16_kernel<DK, KDA>), dim3((unsigned)nblk), dim3(NTHR), 0, s, qop, kop,
                      (const f16_t*)ktop, (const bf16_t*)a.v, (const float*)a.GF, dg,
-                     (const f16_t*)a.Ainv, (const f16_t*)a.Aqk, a.scale, a.h0, a.ht, (bf16_t*)a.o,
+                     (const f16_t*)a.Ainv, (const f16_t*)a.Aqk, a.scale, a.h0, a.ht, a.hs, a.split_chunks,
+                     (bf16_t*)a.o,
                      a.cu_seqlens, a.seq_order, a.chunk_off, a.T, a.B * a.T, (a.T + BT - 1) / BT, a.N,
                      a.Hk, a.HV, a.V);
   return hipGetLastError();

@@ -101,6 +101,7 @@ struct Problem {
 
 int check_chunk(const void* q, const void* k, const void* v, const float* gate,
                 bool gate_required, const float* beta, const float* h0, float* ht,
+                const float* h_snap, int split_size,
                 const int64_t* cu, int num_seqs, int B, int T, int Hk, int HV, int K, int V,
                 int chunk_size, int dtype, const void* o, Problem& P) {
   if (B < 0 || T < 0 || Hk <= 0 || HV <= 0 || K <= 0 || V <= 0)
@@ -127,7 +128,9 @@ int check_chunk(const void* q, const void* k, const void* v, const float* gate,
   if (work && (!q || !k || !v || !beta || !o))
     return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, beta and o are required");
   if (work && gate_required && !gate) return fail(GDN_ERR_INVALID_ARGUMENT, "gk is required");
-  const void* ptrs[] = {q, k, v, gate, beta, h0, ht, o};
+  if (h_snap && (split_size <= 0 || split_size % 64 != 0))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "split_size must be a positive multiple of 64 (got %d)", split_size);
+  const void* ptrs[] = {q, k, v, gate, beta, h0, ht, h_snap, o};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(GDN_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   P.B = B; P.T = T; P.Hk = Hk; P.HV = HV; P.K = K; P.V = V;
@@ -285,12 +288,13 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
 }
 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                  float scale, const float* h0, float* ht, const int64_t* cu_seqlens,
+                  float scale, const float* h0, float* ht, float* h_snap, int split_size,
+                  const int64_t* cu_seqlens,
                   int num_seqs, int B, int T, int Hk, int HV, int K, int V, int chunk_size,
                   int dtype, void* o, void* workspace, size_t workspace_bytes, void* stream) {
   Problem P;
-  int st = check_chunk(q, k, v, g, false, beta, h0, ht, cu_seqlens, num_seqs, B, T, Hk, HV, K, V,
-                       chunk_size, dtype, o, P);
+  int st = check_chunk(q, k, v, g, false, beta, h0, ht, h_snap, split_size, cu_seqlens, num_seqs, B, T,
+                       Hk, HV, K, V, chunk_size, dtype, o, P);
   if (st != GDN_OK) return st;
   const int eb = dtype == GDN_DTYPE_BF16 ? 2 : 4;
   const ChunkWorkspace L = chunk_workspace_layout((long long)B * T, HV, K, P.N,
@@ -305,6 +309,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   ChunkArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.gk = nullptr; a.beta = beta; a.scale = scale;
   a.h0 = h0; a.ht = ht; a.cu_seqlens = cu_seqlens; a.N = P.N;
+  a.hs = h_snap; a.split_chunks = h_snap ? split_size / 64 : 1;
   a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
   a.bf16 = dtype == GDN_DTYPE_BF16;
   a.o = o;
@@ -320,13 +325,14 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* gk, const float* beta,
-                  float scale, const float* h0, float* ht, const int64_t* cu_seqlens,
+                  float scale, const float* h0, float* ht, float* h_snap, int split_size,
+                  const int64_t* cu_seqlens,
                   int num_seqs, int B, int T, int Hk, int HV, int K, int V, int chunk_size,
                   int dtype, void* o, void* Aqk, void* Akk_inv, void* workspace,
                   size_t workspace_bytes, void* stream) {
   Problem P;
-  int st = check_chunk(q, k, v, gk, true, beta, h0, ht, cu_seqlens, num_seqs, B, T, Hk, HV, K, V,
-                       chunk_size, dtype, o, P);
+  int st = check_chunk(q, k, v, gk, true, beta, h0, ht, h_snap, split_size, cu_seqlens, num_seqs, B, T,
+                       Hk, HV, K, V, chunk_size, dtype, o, P);
   if (st != GDN_OK) return st;
   if ((Aqk && !aligned16(Aqk)) || (Akk_inv && !aligned16(Akk_inv)))
     return fail(GDN_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
@@ -343,6 +349,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* gk, 
   ChunkArgs a;
   a.q = q; a.k = k; a.v = v; a.g = nullptr; a.gk = gk; a.beta = beta; a.scale = scale;
   a.h0 = h0; a.ht = ht; a.cu_seqlens = cu_seqlens; a.N = P.N;
+  a.hs = h_snap; a.split_chunks = h_snap ? split_size / 64 : 1;
   a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
   a.bf16 = dtype == GDN_DTYPE_BF16;
   a.o = o;

@@ -35,6 +35,8 @@ struct ChunkArgs {
   float scale;
   const float* h0;
   float* ht;
+  float* hs;             // [splits, HV, V, K] fp32 state snapshots or nullptr
+  int split_chunks;      // chunks per snapshot (split_size / 64)
   const int64_t* cu_seqlens;
   int N;                 // sequences (B without cu_seqlens)
   int B, T, Hk, HV, K, V;
@@ -51,6 +53,21 @@ struct ChunkArgs {
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t s);
 // Token stride of a gate-factor plane.
 __host__ __device__ inline long long gf_stride(long long tokens) { return tokens; }
+
+// First state snapshot of sequence n: a sequence of L tokens has
+// ceil(L / S) snapshots (S = split tokens), stored back to back in sequence
+// order.  Varlen boundaries are clamped as the scans clamp them.
+__device__ inline long long snapshot_offset(const int64_t* cu, int n, int Tlen, int S) {
+  if (!cu) return (long long)n * ((Tlen + S - 1) / S);
+  long long acc = 0;
+  for (int m = 0; m < n; ++m) {
+    long long b0 = cu[m], b1 = cu[m + 1];
+    b0 = b0 < 0 ? 0 : (b0 > Tlen ? Tlen : b0);
+    b1 = b1 < b0 ? b0 : (b1 > Tlen ? Tlen : b1);
+    acc += (b1 - b0 + S - 1) / S;
+  }
+  return acc;
+}
 // bf16 GDN and KDA scans (direct-to-LDS staging, state / helper / mover waves);
 // KDA reads the gated operands and decay rows of KdaBuffers
 hipError_t launch_scan_gdn_bf16(const ChunkArgs& a, hipStream_t s);

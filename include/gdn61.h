@@ -93,6 +93,22 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
  *   scale       output scale (callers usually pass K^-0.5)
  *   h0          [N, HV, V, K]   fp32 initial state, or NULL for zeros
  *   ht          [N, HV, V, K]   fp32 final state out, or NULL to skip
+ *   h_snap      [S, HV, V, K]   fp32 state snapshots out, or NULL to skip:
+ *                               the state before the first token of every
+ *                               split of split_size tokens of a sequence
+ *                               ("fla ops/common/chunk_h.py",
+ *                               chunk_fwd_kernel_h: h is stored at every
+ *                               chunk whose index is a multiple of
+ *                               split_size / chunk_size, before that chunk's
+ *                               update).  Sequence n of length L_n owns
+ *                               ceil(L_n / split_size) consecutive entries,
+ *                               after those of sequences 0..n-1, so
+ *                               S = sum_n ceil(L_n / split_size)
+ *                               (B * ceil(T / split_size) without
+ *                               cu_seqlens); its first entry is h0 (or
+ *                               zeros).  The caller sizes the buffer.
+ *   split_size  tokens per snapshot, a positive multiple of 64; read only
+ *               when h_snap is not NULL
  *   cu_seqlens  [N + 1]         int64 device array of packed sequence
  *                               boundaries, or NULL.  With it B must be 1 and
  *                               num_seqs = N; the values must satisfy
@@ -110,7 +126,7 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
  */
 int gdn_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* g, const float* beta, float scale,
-                  const float* h0, float* ht,
+                  const float* h0, float* ht, float* h_snap, int split_size,
                   const int64_t* cu_seqlens, int num_seqs,
                   int B, int T, int Hk, int HV, int K, int V,
                   int chunk_size, int dtype,
@@ -136,7 +152,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v,
  */
 int kda_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* gk, const float* beta, float scale,
-                  const float* h0, float* ht,
+                  const float* h0, float* ht, float* h_snap, int split_size,
                   const int64_t* cu_seqlens, int num_seqs,
                   int B, int T, int Hk, int HV, int K, int V,
                   int chunk_size, int dtype,

@@ -54,7 +54,8 @@ def sequences(B: int, T: int, cu_seqlens) -> list:
 
 
 def delta_rule_recurrent(q, k, v, beta, scale: float, g=None, gk=None, h0=None,
-                         cu_seqlens=None, heads: Optional[list] = None):
+                         cu_seqlens=None, heads: Optional[list] = None,
+                         split_size: Optional[int] = None):
     """Run the recurrence token by token.
 
     q, k: [B, T, Hk, K]; v: [B, T, HV, V]; beta: [B, T, HV];
@@ -62,7 +63,12 @@ def delta_rule_recurrent(q, k, v, beta, scale: float, g=None, gk=None, h0=None,
     ``heads`` restricts the run to a subset of v-heads (outputs of the other
     heads are left 0) -- used to sample large problems.
 
-    Returns o [B, T, HV, V] and ht [N, HV, V, K], both float64.
+    Returns o [B, T, HV, V] and ht [N, HV, V, K], both float64.  With
+    ``split_size`` also the state snapshots [S, HV, V, K]: the state before
+    token 0, split_size, 2 split_size, ... of every sequence, sequence after
+    sequence ("fla ops/common/chunk_h.py", chunk_fwd_kernel_h stores h at the
+    chunks whose index is a multiple of split_size / chunk_size, before their
+    update; S = sum over sequences of ceil(length / split_size)).
     """
     q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
     g, gk, h0 = _f64(g), _f64(gk), _f64(h0)
@@ -75,9 +81,14 @@ def delta_rule_recurrent(q, k, v, beta, scale: float, g=None, gk=None, h0=None,
     seqs = sequences(B, T, cu_seqlens)
     o = np.zeros((B, T, HV, V))
     ht = np.zeros((len(seqs), HV, V, K))
+    snaps = []
     for n, (b, bos, eos) in enumerate(seqs):
         S = np.zeros((len(hs), V, K)) if h0 is None else h0[n, hs].copy()
         for t in range(bos, eos):
+            if split_size is not None and (t - bos) % split_size == 0:
+                snap = np.zeros((HV, V, K))
+                snap[hs] = S
+                snaps.append(snap)
             qt, kt = q[b, t, kh], k[b, t, kh]          # [h, K]
             if g is not None:
                 S *= np.exp(g[b, t, hs])[:, None, None]
@@ -88,16 +99,18 @@ def delta_rule_recurrent(q, k, v, beta, scale: float, g=None, gk=None, h0=None,
             S += delta[:, :, None] * kt[:, None, :]
             o[b, t, hs] = scale * np.einsum("hvk,hk->hv", S, qt)
         ht[n, hs] = S
+    if split_size is not None:
+        return o, ht, (np.stack(snaps) if snaps else np.zeros((0, HV, V, K)))
     return o, ht
 
 
-def gdn_recurrent(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, heads=None):
+def gdn_recurrent(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, heads=None, split_size=None):
     """Scalar-gate (GDN) recurrence; ``g`` may be None (no decay)."""
     return delta_rule_recurrent(q, k, v, beta, scale, g=g, h0=h0,
-                                cu_seqlens=cu_seqlens, heads=heads)
+                                cu_seqlens=cu_seqlens, heads=heads, split_size=split_size)
 
 
-def kda_recurrent(q, k, v, gk, beta, scale, h0=None, cu_seqlens=None, heads=None):
+def kda_recurrent(q, k, v, gk, beta, scale, h0=None, cu_seqlens=None, heads=None, split_size=None):
     """Per-channel-gate (KDA) recurrence."""
     return delta_rule_recurrent(q, k, v, beta, scale, gk=gk, h0=h0,
-                                cu_seqlens=cu_seqlens, heads=heads)
+                                cu_seqlens=cu_seqlens, heads=heads, split_size=split_size)

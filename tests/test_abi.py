@@ -47,11 +47,11 @@ def test_version_and_status_strings(L):
 
 
 def _chunk(L, **kw):
-    a = dict(q=None, k=None, v=None, g=None, beta=None, scale=1.0, h0=None, ht=None, cu=None, ns=0,
+    a = dict(q=None, k=None, v=None, g=None, beta=None, scale=1.0, h0=None, ht=None, hs=None, ss=0, cu=None, ns=0,
              B=1, T=64, Hk=2, HV=2, K=64, V=64, cs=64, dt=1, o=None, ws=None, wsb=0, st=None)
     a.update(kw)
     return L.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["h0"], a["ht"],
-                           a["cu"], a["ns"], a["B"], a["T"], a["Hk"], a["HV"], a["K"], a["V"], a["cs"],
+                           a["hs"], a["ss"], a["cu"], a["ns"], a["B"], a["T"], a["Hk"], a["HV"], a["K"], a["V"], a["cs"],
                            a["dt"], a["o"], a["ws"], a["wsb"], a["st"])
 
 
@@ -68,6 +68,9 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced (checks
     (dict(), 1, b"required"),
     (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE), 3, b"workspace"),
     (dict(q=FAKE + 4, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, ws=FAKE, wsb=1 << 40), 1, b"aligned"),
+    (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE, ss=96), 1, b"split_size"),
+    (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE, ss=0), 1, b"split_size"),
+    (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE + 8, ss=64, ws=FAKE, wsb=1 << 40), 1, b"aligned"),
 ])
 def test_chunk_fwd_rejects(L, kw, status, msg):
     assert _chunk(L, **kw) == status
@@ -75,7 +78,7 @@ def test_chunk_fwd_rejects(L, kw, status, msg):
 
 
 def test_kda_requires_gate(L):
-    r = L.kda_chunk_fwd(FAKE, FAKE, FAKE, None, FAKE, 1.0, None, None, None, 0, 1, 64, 1, 1, 64, 64, 64, 1,
+    r = L.kda_chunk_fwd(FAKE, FAKE, FAKE, None, FAKE, 1.0, None, None, None, 0, None, 0, 1, 64, 1, 1, 64, 64, 64, 1,
                         FAKE, None, None, FAKE, 1 << 40, None)
     assert r == 1 and b"gk" in L.gdn_last_error()
 

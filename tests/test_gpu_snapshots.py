@@ -1,0 +1,77 @@
+"""GPU parity of the state snapshots (h_snap every split_size tokens) of the
+GDN and KDA chunked prefill against the fp64 oracle, through the C ABI, on
+all four scan paths (bf16 / fp32 io, scalar / per-channel gate)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_61_amd import binding, workloads
+from tests.tolerance import check
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+dv = lambda t: None if t is None else t.to(DEV)
+
+
+def _gdn(inp, S):
+    print(f"snapshots GDN {inp.name} dims={inp.dims} split={S}", flush=True)
+    o, ht, hs = binding.gdn_chunk_fwd(dv(inp.q), dv(inp.k), dv(inp.v), dv(inp.g), dv(inp.beta),
+                                      scale=inp.scale, h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens),
+                                      split_size=S)
+    torch.cuda.synchronize()
+    o_ref, ht_ref, hs_ref = oracle.gdn_recurrent(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale,
+                                                 h0=inp.h0, cu_seqlens=inp.cu_seqlens, split_size=S)
+    assert hs.shape == hs_ref.shape
+    dt = inp.q.dtype
+    check("o", o.cpu(), o_ref, dt)
+    check("ht", ht.cpu(), ht_ref, dt)
+    print("  h_snap", check("h_snap", hs.cpu(), hs_ref, dt), flush=True)
+
+
+def _kda(inp, S):
+    print(f"snapshots KDA {inp.name} dims={inp.dims} split={S}", flush=True)
+    o, ht, _, _, hs = binding.kda_chunk_fwd(dv(inp.q), dv(inp.k), dv(inp.v), dv(inp.gk), dv(inp.beta),
+                                            scale=inp.scale, h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens),
+                                            return_intra=False, split_size=S)
+    torch.cuda.synchronize()
+    o_ref, ht_ref, hs_ref = oracle.kda_recurrent(inp.q, inp.k, inp.v, inp.gk, inp.beta, inp.scale,
+                                                 h0=inp.h0, cu_seqlens=inp.cu_seqlens, split_size=S)
+    assert hs.shape == hs_ref.shape
+    dt = inp.q.dtype
+    check("o", o.cpu(), o_ref, dt)
+    print("  h_snap", check("h_snap", hs.cpu(), hs_ref, dt), flush=True)
+
+
+@pytest.mark.parametrize("S", [64, 128])
+def test_gdn_bf16_varlen_snapshots(S):
+    inp = workloads.make_prefill(1, 400, 2, 4, 128, 128, dtype=torch.bfloat16, seed=S, h0=True,
+                                 seqlens=[130, 64, 1, 205], name="bf16_varlen")
+    _gdn(inp, S)
+
+
+def test_gdn_bf16_fixed_snapshots_every_chunk():
+    inp = workloads.make_prefill(2, 200, 1, 2, 64, 64, dtype=torch.bfloat16, seed=5, h0=True,
+                                 name="bf16_K64")
+    _gdn(inp, 64)
+
+
+def test_gdn_fp32_snapshots():
+    inp = workloads.make_prefill(2, 150, 1, 2, 64, 64, dtype=torch.float32, seed=6, h0=True,
+                                 name="fp32_K64")
+    _gdn(inp, 64)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_kda_snapshots(dtype):
+    inp = workloads.make_prefill(1, 260, 2, 2, 128, 128, dtype=dtype, seed=7, gate="kda", h0=True,
+                                 seqlens=[70, 190], name=f"kda_{dtype}")
+    _kda(inp, 128 if dtype == torch.bfloat16 else 64)
+
+
+def test_snapshot_buffer_untouched_without_snapshots():
+    """split_size given but the call has no tokens: no snapshot exists."""
+    inp = workloads.make_prefill(1, 64, 1, 2, 64, 64, dtype=torch.bfloat16, seed=8, h0=True,
+                                 seqlens=[0, 64], name="empty_first")
+    _gdn(inp, 64)
