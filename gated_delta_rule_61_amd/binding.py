@@ -33,7 +33,7 @@ _SIGNATURES = {
     "gdn_version": (ctypes.c_char_p, []),
     "gdn_chunk_fwd_workspace_bytes": (_c_size_t, [_c_int] * 8),
     "kda_chunk_fwd_workspace_bytes": (_c_size_t, [_c_int] * 8),
-    "gdn_chunk_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float,
+    "gdn_chunk_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float,
                                _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_int,
                                _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
@@ -184,11 +184,18 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
                   h0: Optional[torch.Tensor] = None, output_final_state: bool = True,
                   cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  split_size: Optional[int] = None, h_snap: Optional[torch.Tensor] = None):
+                  split_size: Optional[int] = None, h_snap: Optional[torch.Tensor] = None,
+                  g_gamma: Optional[torch.Tensor] = None):
     """GDN chunked prefill.  Returns (o [B,T,HV,V], ht [N,HV,V,K] fp32 or None),
     and the state snapshots [S,HV,V,K] fp32 as a third element when
-    ``split_size`` is given (``h_snap`` may be passed preallocated)."""
+    ``split_size`` is given (``h_snap`` may be passed preallocated).
+    ``g_gamma`` [HV] (fp32) is a fixed per-head log-decay at every token, in
+    place of ``g``."""
     B, T, Hk, HV, K, V, N, dev, io = _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, g, (), "g")
+    if g_gamma is not None:
+        if g is not None:
+            raise ValueError("pass g or g_gamma, not both")
+        _need(g_gamma, "g_gamma", torch.float32, (HV,), dev)
     hs = _snapshots(B, T, HV, V, K, N, dev, split_size, h_snap, cu_seqlens)
     if scale is None:
         scale = K ** -0.5
@@ -198,7 +205,7 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     nbytes = workspace_bytes(B, T, Hk, HV, K, V, N, io)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    _check(lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+    _check(lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma), _ptr(beta), float(scale),
                                _ptr(h0), _ptr(ht), _ptr(hs), split_size or 0, _ptr(cu_seqlens), N,
                                B, T, Hk, HV, K, V, chunk_size, _io_code(io),
                                _ptr(o), _ptr(workspace), workspace.numel(), _stream(dev)))

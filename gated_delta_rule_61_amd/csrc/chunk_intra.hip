@@ -45,7 +45,7 @@ using namespace intra;
 template <typename T, int DK, typename C = typename ComputeOf<T>::type>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void gdn_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, float scale, C* __restrict__ Ainv,
+    const float* __restrict__ gamma, const float* __restrict__ beta, float scale, C* __restrict__ Ainv,
     C* __restrict__ Aqk, float* __restrict__ GF, const int64_t* __restrict__ cu,
     const int32_t* __restrict__ coff, int Tlen, int ttot, int N, int NT, int nslots, int Hk, int HV) {
   __shared__ __attribute__((aligned(16))) float sA[BT][AP];
@@ -75,7 +75,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void gd
   // chunk-local cumulative gate and beta, lane = token
   // (loads clamped to the chunk, values masked: no branch around a load)
   const int tl = lane < nrow ? lane : nrow - 1;
-  const float g_raw = g ? g[(size_t)(c0 + tl) * HV + j] : 0.f;
+  // per-token log-gate, or the head's fixed log-decay for every token
+  // ("fla ops/common/chunk_h.py", USE_G_GAMMA: G = gamma * (t + 1) in a chunk)
+  const float g_raw = g ? g[(size_t)(c0 + tl) * HV + j] : (gamma ? gamma[j] : 0.f);
   const float b_raw = beta[(size_t)(c0 + tl) * HV + j];
   if (DK / 32 > 1) load_slab(1, kf[1], qf[1]);
   const float gl = lane < nrow ? g_raw : 0.f;
@@ -166,23 +168,23 @@ hipError_t launch_intra_gdn(const ChunkArgs& a, hipStream_t s, int NT, int nslot
   if (a.bf16) {
     if (a.K == 128)
       hipLaunchKernelGGL((gdn_intra_kernel<bf16_t, 128>), grid, dim3(64), 0, s,
-                         (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, a.scale,
+                         (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.g_gamma, a.beta, a.scale,
                          (f16_t*)a.Ainv, (f16_t*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
                          a.T, a.B * a.T, a.N, NT, nslots, a.Hk, a.HV);
     else
       hipLaunchKernelGGL((gdn_intra_kernel<bf16_t, 64>), grid, dim3(64), 0, s,
-                         (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.beta, a.scale,
+                         (const bf16_t*)a.q, (const bf16_t*)a.k, a.g, a.g_gamma, a.beta, a.scale,
                          (f16_t*)a.Ainv, (f16_t*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
                          a.T, a.B * a.T, a.N, NT, nslots, a.Hk, a.HV);
   } else {
     if (a.K == 128)
       hipLaunchKernelGGL((gdn_intra_kernel<float, 128>), grid, dim3(64), 0, s,
-                         (const float*)a.q, (const float*)a.k, a.g, a.beta, a.scale,
+                         (const float*)a.q, (const float*)a.k, a.g, a.g_gamma, a.beta, a.scale,
                          (float*)a.Ainv, (float*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
                          a.T, a.B * a.T, a.N, NT, nslots, a.Hk, a.HV);
     else
       hipLaunchKernelGGL((gdn_intra_kernel<float, 64>), grid, dim3(64), 0, s,
-                         (const float*)a.q, (const float*)a.k, a.g, a.beta, a.scale,
+                         (const float*)a.q, (const float*)a.k, a.g, a.g_gamma, a.beta, a.scale,
                          (float*)a.Ainv, (float*)a.Aqk, (float*)a.GF, a.cu_seqlens, a.chunk_off,
                          a.T, a.B * a.T, a.N, NT, nslots, a.Hk, a.HV);
   }

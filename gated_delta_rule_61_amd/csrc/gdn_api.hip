@@ -287,8 +287,8 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
                                 true).total;
 }
 
-int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                  float scale, const float* h0, float* ht, float* h_snap, int split_size,
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                  const float* g_gamma, const float* beta, float scale, const float* h0, float* ht, float* h_snap, int split_size,
                   const int64_t* cu_seqlens,
                   int num_seqs, int B, int T, int Hk, int HV, int K, int V, int chunk_size,
                   int dtype, void* o, void* workspace, size_t workspace_bytes, void* stream) {
@@ -296,6 +296,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   int st = check_chunk(q, k, v, g, false, beta, h0, ht, h_snap, split_size, cu_seqlens, num_seqs, B, T,
                        Hk, HV, K, V, chunk_size, dtype, o, P);
   if (st != GDN_OK) return st;
+  if (g && g_gamma) return fail(GDN_ERR_INVALID_ARGUMENT, "pass g or g_gamma, not both");
   const int eb = dtype == GDN_DTYPE_BF16 ? 2 : 4;
   const ChunkWorkspace L = chunk_workspace_layout((long long)B * T, HV, K, P.N,
                                                   (T + 63) / 64 * B + P.N, eb, false);
@@ -307,7 +308,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   if (P.N == 0) return ok();
   char* ws = (char*)workspace;
   ChunkArgs a;
-  a.q = q; a.k = k; a.v = v; a.g = g; a.gk = nullptr; a.beta = beta; a.scale = scale;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.g_gamma = g_gamma; a.gk = nullptr; a.beta = beta; a.scale = scale;
   a.h0 = h0; a.ht = ht; a.cu_seqlens = cu_seqlens; a.N = P.N;
   a.hs = h_snap; a.split_chunks = h_snap ? split_size / 64 : 1;
   a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
@@ -347,7 +348,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* gk, 
   if (P.N == 0) return ok();
   char* ws = (char*)workspace;
   ChunkArgs a;
-  a.q = q; a.k = k; a.v = v; a.g = nullptr; a.gk = gk; a.beta = beta; a.scale = scale;
+  a.q = q; a.k = k; a.v = v; a.g = nullptr; a.g_gamma = nullptr; a.gk = gk; a.beta = beta; a.scale = scale;
   a.h0 = h0; a.ht = ht; a.cu_seqlens = cu_seqlens; a.N = P.N;
   a.hs = h_snap; a.split_chunks = h_snap ? split_size / 64 : 1;
   a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;

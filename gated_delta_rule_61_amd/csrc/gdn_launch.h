@@ -32,6 +32,7 @@ hipError_t launch_state_to_pool(const float* ht, const int32_t* idx, void* pool_
 struct ChunkArgs {
   const void *q, *k, *v;
   const float *g, *gk, *beta;
+  const float* g_gamma;  // [HV] fixed per-head log-decay per token (GDN) or nullptr
   float scale;
   const float* h0;
   float* ht;

@@ -88,7 +88,13 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
  *   v           [B, T, HV, V]   io dtype
  *   g           [B, T, HV]      fp32 per-token natural-log gate (the chunk-
  *                               local cumulative sum is taken inside), or
- *                               NULL for no decay
+ *                               NULL
+ *   g_gamma     [HV]            fp32 fixed per-head natural-log decay applied
+ *                               at every token, or NULL ("fla ops/common/
+ *                               chunk_h.py", USE_G_GAMMA: the chunk-local
+ *                               cumulative gate is gamma * (t + 1)); the
+ *                               same as g[b, t, h] = g_gamma[h].  At most one
+ *                               of g and g_gamma; neither means no decay
  *   beta        [B, T, HV]      fp32
  *   scale       output scale (callers usually pass K^-0.5)
  *   h0          [N, HV, V, K]   fp32 initial state, or NULL for zeros
@@ -125,7 +131,7 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
  * T = 0 (or all sequences empty) is valid: ht = h0 (or zeros) is written.
  */
 int gdn_chunk_fwd(const void* q, const void* k, const void* v,
-                  const float* g, const float* beta, float scale,
+                  const float* g, const float* g_gamma, const float* beta, float scale,
                   const float* h0, float* ht, float* h_snap, int split_size,
                   const int64_t* cu_seqlens, int num_seqs,
                   int B, int T, int Hk, int HV, int K, int V,

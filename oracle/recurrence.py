@@ -104,8 +104,17 @@ def delta_rule_recurrent(q, k, v, beta, scale: float, g=None, gk=None, h0=None,
     return o, ht
 
 
-def gdn_recurrent(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, heads=None, split_size=None):
-    """Scalar-gate (GDN) recurrence; ``g`` may be None (no decay)."""
+def gdn_recurrent(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, heads=None, split_size=None,
+                  g_gamma=None):
+    """Scalar-gate (GDN) recurrence; ``g`` may be None (no decay).  ``g_gamma``
+    [HV] is a fixed per-head log-decay applied at every token, in place of g
+    ("fla ops/common/chunk_h.py", USE_G_GAMMA: within a chunk the cumulative
+    gate is gamma * (t + 1), i.e. g_t = gamma at each token)."""
+    if g_gamma is not None:
+        if g is not None:
+            raise ValueError("pass g or g_gamma, not both")
+        B, T = np.shape(q)[:2]
+        g = np.broadcast_to(_f64(g_gamma), (B, T, len(_f64(g_gamma))))
     return delta_rule_recurrent(q, k, v, beta, scale, g=g, h0=h0,
                                 cu_seqlens=cu_seqlens, heads=heads, split_size=split_size)
 

@@ -47,10 +47,10 @@ def test_version_and_status_strings(L):
 
 
 def _chunk(L, **kw):
-    a = dict(q=None, k=None, v=None, g=None, beta=None, scale=1.0, h0=None, ht=None, hs=None, ss=0, cu=None, ns=0,
+    a = dict(q=None, k=None, v=None, g=None, gg=None, beta=None, scale=1.0, h0=None, ht=None, hs=None, ss=0, cu=None, ns=0,
              B=1, T=64, Hk=2, HV=2, K=64, V=64, cs=64, dt=1, o=None, ws=None, wsb=0, st=None)
     a.update(kw)
-    return L.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["h0"], a["ht"],
+    return L.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["gg"], a["beta"], a["scale"], a["h0"], a["ht"],
                            a["hs"], a["ss"], a["cu"], a["ns"], a["B"], a["T"], a["Hk"], a["HV"], a["K"], a["V"], a["cs"],
                            a["dt"], a["o"], a["ws"], a["wsb"], a["st"])
 
@@ -69,6 +69,7 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced (checks
     (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE), 3, b"workspace"),
     (dict(q=FAKE + 4, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, ws=FAKE, wsb=1 << 40), 1, b"aligned"),
     (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE, ss=96), 1, b"split_size"),
+    (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, g=FAKE, gg=FAKE, ws=FAKE, wsb=1 << 40), 1, b"not both"),
     (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE, ss=0), 1, b"split_size"),
     (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE + 8, ss=64, ws=FAKE, wsb=1 << 40), 1, b"aligned"),
 ])

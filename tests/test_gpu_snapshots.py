@@ -75,3 +75,19 @@ def test_snapshot_buffer_untouched_without_snapshots():
     inp = workloads.make_prefill(1, 64, 1, 2, 64, 64, dtype=torch.bfloat16, seed=8, h0=True,
                                  seqlens=[0, 64], name="empty_first")
     _gdn(inp, 64)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gdn_g_gamma(dtype):
+    """Fixed per-head decay in place of g (varlen, h0, GQA)."""
+    inp = workloads.make_prefill(1, 300, 2, 4, 64, 64, dtype=dtype, seed=9, h0=True,
+                                 seqlens=[100, 200], name=f"gamma_{dtype}")
+    gamma = torch.tensor([-0.02, -0.1, -0.5, -2.0], dtype=torch.float32)
+    print(f"g_gamma {dtype}", flush=True)
+    o, ht = binding.gdn_chunk_fwd(dv(inp.q), dv(inp.k), dv(inp.v), None, dv(inp.beta), scale=inp.scale,
+                                  h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens), g_gamma=dv(gamma))
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.gdn_recurrent(inp.q, inp.k, inp.v, None, inp.beta, inp.scale, h0=inp.h0,
+                                         cu_seqlens=inp.cu_seqlens, g_gamma=gamma)
+    check("o", o.cpu(), o_ref, dtype)
+    check("ht", ht.cpu(), ht_ref, dtype)
