@@ -9,7 +9,8 @@ tokens/s (B*T per call).  The same JSON line also carries the decode step
 (B=256, HV=32, K=V=128, bf16 state, T=1 and T=4: tokens/s and state GB/s),
 the varlen GQA prefill (8 packed sequences, Hk=16, HV=32, h0 in), the KDA
 prefill (B=2 T=8192 H=32), the prefill -> decode state handoff (256 states
-into a bf16 pool), the prefill with state snapshots, the per-kernel roofline of the
+into a bf16 pool), the prefill with state snapshots, the backward state-gradient
+scan, the per-kernel roofline of the
 dominant prefill kernel (live HIP-event timing inside the library, on the
 launch stream) and the fp64 CPU oracle timed on a bounded sample.
 
@@ -71,7 +72,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=16384)
     p.add_argument("--skip-extra", action="store_true", help="prefill workload only")
-    p.add_argument("--only", choices=["prefill", "decode", "kda", "varlen", "handoff", "copy"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "kda", "varlen", "handoff", "bwd_dh", "copy"],
+                   default=None,
                    help="run one workload (for profiling) and print its figures")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache prefill timing")
     p.add_argument("--decode-batch", type=int, default=256, help="batch of --only decode")
@@ -260,6 +262,40 @@ def bench_snapshots(args, binding, workloads, torch, base_ms):
     return res
 
 
+def bench_bwd_dh(args, binding, workloads, torch):
+    """Backward state-gradient scan on the headline shape (B=4 T=4096 H=16
+    K=V=128, bf16 q / dout, scalar gate), dh every chunk, dht in, dh0 out."""
+    inp = workloads.gdn_bf16_b4_t4096()
+    dev = "cuda:0"
+    B, T, Hk, HV, K, V = inp.dims
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1006)
+    q, g = inp.q.to(dev), inp.g.to(dev)
+    do = torch.randn((B, T, HV, V), generator=gen, device=dev).to(torch.bfloat16)
+    dht = torch.randn((B, HV, V, K), generator=gen, device=dev) * 0.1
+
+    def step():
+        binding.chunk_bwd_dh(q, do, g=g, scale=inp.scale, dht=dht, split_size=64)
+
+    ms, _ = timed(step, max(args.steps // 2, 1), 1)
+    binding.profile_read()
+    binding.profile_enable(True)
+    for _ in range(max(args.steps // 2, 1)):
+        step()
+    torch.cuda.synchronize()
+    prof = binding.profile_read()
+    binding.profile_enable(False)
+    kms = prof["bwd_dh"][0] / max(prof["bwd_dh"][1], 1)
+    nchunks = B * ((T + 63) // 64)
+    nbytes = (B * T * Hk * K * 2 + B * T * HV * V * 2 + B * T * HV * 4
+              + nchunks * HV * V * K * 4 + 2 * B * HV * V * K * 4)
+    return {"workload": f"gdn_chunk_bwd_dh B={B} T={T} H={HV} K=V={K} bf16, dh every 64 tokens, dht in, dh0 out",
+            "ms_per_call": round(ms, 5), "kernel_ms": round(kms, 5),
+            "GBps": round(nbytes / (kms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes, "measured_bytes": measured_traffic("bwd_dh")}
+
+
 def bench_handoff(args, binding, workloads, torch):
     """Prefill -> decode handoff: 256 sequences' fp32 final states (32 heads,
     K = V = 128) into a shuffled 256-slot bf16 pool."""
@@ -354,6 +390,9 @@ def main():
     if args.only == "kda":
         print(json.dumps({"kda": bench_kda(args, binding, workloads, torch)}), flush=True)
         return
+    if args.only == "bwd_dh":
+        print(json.dumps({"bwd_dh": bench_bwd_dh(args, binding, workloads, torch)}), flush=True)
+        return
     if args.only == "handoff":
         print(json.dumps({"handoff": bench_handoff(args, binding, workloads, torch)}), flush=True)
         return
@@ -418,6 +457,7 @@ def main():
         out["varlen"] = bench_varlen(args, binding, workloads, torch)
         out["handoff"] = bench_handoff(args, binding, workloads, torch)
         out["snapshots"] = bench_snapshots(args, binding, workloads, torch, ms)
+        out["bwd_dh"] = bench_bwd_dh(args, binding, workloads, torch)
         try:
             out["kda"] = bench_kda(args, binding, workloads, torch)
         except Exception as e:  # KDA path reports its own status

@@ -4,9 +4,9 @@ bf16-state decode step, as hand-written HIP kernels behind a C ABI
 into that ABI; nothing is computed in Python.
 """
 
-from .binding import (GDNError, gdn_chunk_fwd, gdn_decode, kda_chunk_fwd, lib, state_to_pool,
-                      workspace_bytes)
+from .binding import (GDNError, chunk_bwd_dh, gdn_chunk_fwd, gdn_decode, kda_chunk_fwd, lib,
+                      state_to_pool, workspace_bytes)
 
-__all__ = ["GDNError", "gdn_chunk_fwd", "gdn_decode", "kda_chunk_fwd", "lib", "state_to_pool",
+__all__ = ["GDNError", "chunk_bwd_dh", "gdn_chunk_fwd", "gdn_decode", "kda_chunk_fwd", "lib", "state_to_pool",
            "workspace_bytes"]
 __version__ = "0.1.0"

@@ -47,6 +47,10 @@ _SIGNATURES = {
                             _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_float, _c_float, _c_float, _c_int, _c_float, _c_void_p]),
+    "gdn_chunk_bwd_dh": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float,
+                                  _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
+                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                  _c_void_p]),
     "gdn_state_to_pool": (_c_int, [_c_void_p, _c_void_p, _c_void_p,
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
 }
@@ -112,7 +116,7 @@ def _need(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype], sh
         raise ValueError(f"{name} must be contiguous")
 
 
-STAGES = ("varlen_tables", "intra", "scan", "decode", "handoff")
+STAGES = ("varlen_tables", "intra", "scan", "decode", "handoff", "bwd_dh")
 
 
 def profile_enable(on: bool = True) -> None:
@@ -303,3 +307,40 @@ def state_to_pool(ht: torch.Tensor, pool_state: torch.Tensor,
     _check(lib().gdn_state_to_pool(_ptr(ht), _ptr(indices), _ptr(pool_state),
                                    N, HV, K, V, pool_state.shape[0], _stream(dev)))
     return pool_state
+
+
+def chunk_bwd_dh(q: torch.Tensor, dout: torch.Tensor, g: Optional[torch.Tensor] = None,
+                 g_gamma: Optional[torch.Tensor] = None, gk: Optional[torch.Tensor] = None,
+                 scale: Optional[float] = None, dht: Optional[torch.Tensor] = None,
+                 cu_seqlens: Optional[torch.Tensor] = None, split_size: Optional[int] = 64,
+                 output_dh0: bool = True, chunk_size: int = 64):
+    """Backward state-gradient scan (bf16 q / dout).  Returns (dh [S,HV,V,K]
+    fp32 or None when ``split_size`` is None, dh0 [N,HV,V,K] fp32 or None)."""
+    if q.dim() != 4 or dout.dim() != 4:
+        raise ValueError("q must be [B, T, Hk, K] and dout [B, T, HV, V]")
+    B, T, Hk, K = q.shape
+    HV, V = dout.shape[2], dout.shape[3]
+    dev = q.device
+    bf = torch.bfloat16
+    _need(q, "q", bf, None, dev)
+    _need(dout, "dout", bf, (B, T, HV, V), dev)
+    _need(g, "g", torch.float32, (B, T, HV), dev)
+    _need(g_gamma, "g_gamma", torch.float32, (HV,), dev)
+    _need(gk, "gk", torch.float32, (B, T, HV, K), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int64, None, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    _need(dht, "dht", torch.float32, (N, HV, V, K), dev)
+    if scale is None:
+        scale = K ** -0.5
+    dh = None
+    if split_size is not None:
+        dh = torch.empty((snapshot_count(B, T, split_size, cu_seqlens), HV, V, K),
+                         dtype=torch.float32, device=dev)
+    dh0 = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if output_dh0 else None
+    _check(lib().gdn_chunk_bwd_dh(_ptr(q), _ptr(dout), _ptr(g), _ptr(g_gamma), _ptr(gk), float(scale),
+                                  _ptr(dht), _ptr(dh), split_size or 0, _ptr(dh0), _ptr(cu_seqlens), N,
+                                  B, T, Hk, HV, K, V, chunk_size, _io_code(bf), _stream(dev)))
+    return dh, dh0

@@ -408,6 +408,47 @@ int gdn_decode(const void* q, const void* k, const void* v, const void* a, const
   return ok();
 }
 
+int gdn_chunk_bwd_dh(const void* q, const void* dout, const float* g, const float* g_gamma,
+                     const float* gk, float scale, const float* dht, float* dh, int split_size,
+                     float* dh0, const int64_t* cu_seqlens, int num_seqs, int B, int T, int Hk, int HV,
+                     int K, int V, int chunk_size, int dtype, void* stream) {
+  if (B < 0 || T < 0 || Hk <= 0 || HV <= 0 || K <= 0 || V <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "sizes must be positive (B, T >= 0): B=%d T=%d Hk=%d HV=%d K=%d V=%d",
+                B, T, Hk, HV, K, V);
+  if (HV % Hk != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "HV (%d) must be a multiple of Hk (%d)", HV, Hk);
+  if (dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_UNSUPPORTED, "the backward dh scan takes bf16 io only");
+  if (chunk_size != 64) return fail(GDN_ERR_UNSUPPORTED, "chunk_size must be 64 (got %d)", chunk_size);
+  if (!((K == 64 && V == 64) || (K == 128 && V == 128)))
+    return fail(GDN_ERR_UNSUPPORTED, "supported head dims are K = V in {64, 128} (got K=%d V=%d)", K, V);
+  if ((g != nullptr) + (g_gamma != nullptr) + (gk != nullptr) > 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "pass at most one of g, g_gamma and gk");
+  if (dh && (split_size <= 0 || split_size % 64 != 0))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "split_size must be a positive multiple of 64 (got %d)", split_size);
+  if ((long long)B * T >= (1LL << 31) / 64)
+    return fail(GDN_ERR_UNSUPPORTED, "B*T too large (got %lld tokens)", (long long)B * T);
+  int N = B;
+  if (cu_seqlens) {
+    if (B != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens requires B == 1 (got B=%d)", B);
+    if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", num_seqs);
+    N = num_seqs;
+  }
+  if ((long long)B * T > 0 && (!q || !dout))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "q and dout are required");
+  const void* ptrs[] = {q, dout, g, g_gamma, gk, dht, dh, dh0};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(GDN_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  if (N == 0 || (!dh && !dh0)) return ok();
+  BwdDhArgs a;
+  a.q = q; a.dout = dout; a.g = g; a.g_gamma = g_gamma; a.gk = gk; a.scale = scale;
+  a.dht = dht; a.dh = dh; a.split_chunks = dh ? split_size / 64 : 1; a.dh0 = dh0;
+  a.cu_seqlens = cu_seqlens; a.N = N; a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
+  prof_begin(GDN_STAGE_BWD_DH, (hipStream_t)stream);
+  const hipError_t e = launch_bwd_dh(a, (hipStream_t)stream);
+  prof_end(GDN_STAGE_BWD_DH, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int gdn_state_to_pool(const float* ht, const int32_t* indices, void* pool_state, int N, int HV,
                       int K, int V, int pool, void* stream) {
   if (N < 0 || HV <= 0 || K <= 0 || V <= 0 || pool < 0)

@@ -24,6 +24,20 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// backward state-gradient scan (bf16 io)
+struct BwdDhArgs {
+  const void *q, *dout;
+  const float *g, *g_gamma, *gk;   // at most one
+  float scale;
+  const float* dht;                // [N, HV, V, K] or nullptr
+  float* dh;                       // [splits, HV, V, K] or nullptr
+  int split_chunks;
+  float* dh0;                      // [N, HV, V, K] or nullptr
+  const int64_t* cu_seqlens;
+  int N, B, T, Hk, HV, K, V;
+};
+hipError_t launch_bwd_dh(const BwdDhArgs& a, hipStream_t s);
+
 // prefill -> decode handoff: fp32 [N, HV, V, K] into bf16 pool slots
 hipError_t launch_state_to_pool(const float* ht, const int32_t* idx, void* pool_state, int N, int HV,
                                 int K, int V, int pool, hipStream_t s);

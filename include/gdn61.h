@@ -204,6 +204,44 @@ int gdn_decode(const void* q, const void* k, const void* v,
                void* stream);
 
 /*
+ * Backward state-gradient scan ("fla ops/common/chunk_h.py",
+ * chunk_bwd_kernel_dh), bf16 io.  Per sequence and v-head, over the chunks of
+ * 64 tokens in reverse order, with dh [V, K] the gradient with respect to the
+ * state at the end of the current chunk:
+ *   start:       dh = dht (or zeros)
+ *   each chunk:  if its index is a multiple of split_size / 64, store dh;
+ *                dh <- decay * dh + scale * sum_t e^{G_t} do_t q_t^T
+ *                (per-channel gate: the key column c of every term and of
+ *                the decay carries e^{G_t,c} / e^{G_last,c} instead)
+ *   end:         dh0 = dh
+ * G = chunk-local cumulative log-gate, decay = e^{G_last}.  This is the
+ * state gradient of the decay-only recurrence h_t = decay_t h_{t-1} +
+ * (terms free of h), o_t = scale q_t . h_t; the delta rule's erase term is
+ * not part of it.
+ *
+ *   q            [B, T, Hk, K]  bf16
+ *   dout         [B, T, HV, V]  bf16 gradient of the output
+ *   g [B,T,HV] | g_gamma [HV] | gk [B,T,HV,K]   fp32 log-gates, at most
+ *                one (none = no decay); as in gdn_chunk_fwd / kda_chunk_fwd
+ *   dht          [N, HV, V, K]  fp32 gradient of the final state, or NULL
+ *   dh           [S, HV, V, K]  fp32 out, or NULL: sequence n of length L_n
+ *                owns ceil(L_n / split_size) entries after those of
+ *                sequences 0..n-1 (entry s = the gradient at the end of
+ *                chunk s * split_size / 64)
+ *   split_size   a positive multiple of 64, read when dh is not NULL
+ *   dh0          [N, HV, V, K]  fp32 out (gradient of the initial state), or NULL
+ *   cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size  as in gdn_chunk_fwd
+ * Supported: dtype = GDN_DTYPE_BF16, K = V in {64, 128}, chunk_size = 64.
+ * Allocates nothing; asynchronous on `stream`.
+ */
+int gdn_chunk_bwd_dh(const void* q, const void* dout,
+                     const float* g, const float* g_gamma, const float* gk,
+                     float scale, const float* dht, float* dh, int split_size,
+                     float* dh0, const int64_t* cu_seqlens, int num_seqs,
+                     int B, int T, int Hk, int HV, int K, int V,
+                     int chunk_size, int dtype, void* stream);
+
+/*
  * Prefill -> decode handoff: write final prefill states into a bf16 decode
  * state pool (the prefill's ht fp32 layout and the decode pool's layout are
  * both [*, HV, V, K], K contiguous: "fla ops/common/chunk_h.py" ht with the
@@ -243,7 +281,8 @@ enum {
   GDN_STAGE_SCAN = 2,          /* chunk-state scan fused with the output       */
   GDN_STAGE_DECODE = 3,        /* decode step                                  */
   GDN_STAGE_HANDOFF = 4,       /* prefill state -> decode pool (bf16)          */
-  GDN_STAGE_COUNT = 5
+  GDN_STAGE_BWD_DH = 5,        /* backward state-gradient scan                 */
+  GDN_STAGE_COUNT = 6
 };
 int gdn_profile_enable(int on);
 int gdn_profile_read(double* ms, int* counts);

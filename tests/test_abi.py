@@ -141,3 +141,22 @@ def test_state_to_pool_rejects(L, kw, status, msg):
 
 def test_state_to_pool_empty_is_a_no_op(L):
     assert _pool(L, N=0, pool=0) == 0
+
+
+def _bwd(L, q=FAKE, do=FAKE, g=None, gg=None, gk=None, dht=None, dh=None, ss=64, dh0=FAKE, cu=None, ns=0,
+         B=1, T=64, Hk=1, HV=1, K=64, V=64, cs=64, dt=1):
+    return L.gdn_chunk_bwd_dh(q, do, g, gg, gk, 1.0, dht, dh, ss, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dt=0), 2, b"bf16 io only"),
+    (dict(g=FAKE, gk=FAKE), 1, b"at most one"),
+    (dict(dh=FAKE, ss=0), 1, b"split_size"),
+    (dict(K=96, V=96), 2, b"head dims"),
+    (dict(q=None), 1, b"required"),
+    (dict(do=FAKE + 2), 1, b"aligned"),
+    (dict(B=2, cu=FAKE, ns=2), 1, b"B == 1"),
+])
+def test_bwd_dh_rejects(L, kw, status, msg):
+    assert _bwd(L, **kw) == status
+    assert msg in L.gdn_last_error()
