@@ -14,12 +14,16 @@
 // gradient of the decay-only recurrence h_t = decay_t h_{t-1} + k_t v_t^T,
 // o_t = scale q_t^T h_t; the delta rule's erase term is not part of it.
 //
-// gfx950 design.  Work-group = 256 threads per (sequence, v-head, 32-column
+// gfx950 design.  Work-group = 256 threads per (sequence, v-head, BVT-column
 // V tile); wave w holds key rows DK/4 * w .. + DK/4 of dh in fp32 MFMA
 // accumulators for the whole scan.  A chunk's q and dO rows are staged in
 // LDS transposed (key channel / value column major, tokens contiguous), so
 // both operands of the 16x16x32 bf16 product read 8 consecutive tokens with
-// one 16-byte LDS read.  The gated operand is split into a bf16 hi + lo pair
+// one 16-byte LDS read: each thread loads an 8 x 8 block (8 tokens x 8
+// channels), transposes it in registers and writes 8 rows of 16 bytes, with
+// the 8-token units XOR-swizzled by row so that writes and reads spread over
+// the banks.  Each chunk's loads are issued two chunks ahead (two register
+// buffers).  The gated operand is split into a bf16 hi + lo pair
 // (dO * scale e^{G_t} for a scalar gate, q * scale e^{G_t,c} for the
 // per-channel gate); the other operand is the raw bf16 input, exact.
 
@@ -32,7 +36,11 @@ namespace gdn {
 namespace {
 
 constexpr int BT = 64;
-constexpr int BVT = 32;        // V columns per work-group
+#ifndef GDN_BWD_BVT
+#define GDN_BWD_BVT 16
+#endif
+constexpr int BVT = GDN_BWD_BVT;   // V columns per work-group
+constexpr int CBN = BVT / 16;      // 16-column blocks per work-group
 constexpr int TP = BT + 8;     // padded token row of the transposed tiles (bf16)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -40,6 +48,27 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mma_bf(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 16-bit element e (0..7) of a 16-byte vector
+__device__ __forceinline__ uint32_t elem16(const uint4& r, int e) {
+  const uint32_t w = e < 2 ? r.x : e < 4 ? r.y : e < 6 ? r.z : r.w;
+  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+__device__ __forceinline__ uint32_t word(const uint4& r, int i) {
+  return i == 0 ? r.x : i == 1 ? r.y : i == 2 ? r.z : r.w;
+}
+// 8 x 8 transpose of 16-bit values: out[e] word p = (row 2p elem e, row 2p + 1 elem e)
+__device__ __forceinline__ void transpose8(const uint4 (&R)[8], uint4 (&O)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      o[p] = __builtin_amdgcn_perm(word(R[2 * p + 1], e >> 1), word(R[2 * p], e >> 1), sel);
+    O[e] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 template <int DK, bool KDA>
@@ -51,13 +80,15 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
   constexpr int DV = DK;
   constexpr int RW = DK / 4;          // key rows per wave
   constexpr int RB = RW / 16;         // 16-row blocks per wave
-  constexpr int QU = BT * DK / 8;     // 16-byte q units of a chunk
-  constexpr int QPT = QU / 256;       // ... per thread
+  constexpr int NQB = BT / 8 * DK / 8;  // 8 x 8 blocks (tokens x channels) of a q tile
+  static_assert(NQB + BT / 8 * BVT / 8 <= 256, "one block per thread");
+  // transposed tiles: row = key channel / value column, 8-token units XOR-swizzled by row / 8
   __shared__ __attribute__((aligned(16))) bf16_t sAh[DK][TP];   // A operand (q side), hi
   __shared__ __attribute__((aligned(16))) bf16_t sAl[KDA ? DK : 1][TP];   //   lo
   __shared__ __attribute__((aligned(16))) bf16_t sBh[BVT][TP];  // B operand (dO side), hi
   __shared__ __attribute__((aligned(16))) bf16_t sBl[KDA ? 1 : BVT][TP];  //   lo
-  __shared__ float sG[KDA ? BT : 1][KDA ? DK + 4 : 1];          // KDA cumulative gates
+  __shared__ __attribute__((aligned(16))) bf16_t sBr[KDA ? 1 : BVT][TP];  // GDN: raw dO, transposed
+  __shared__ float sG[KDA ? BT : 1][KDA ? DK + 4 : 1];          // KDA: scale e^{G_t,c}
   __shared__ float sGam[BT + 1];    // GDN: scale e^{G_t}, and e^{G_last} at [BT]
   __shared__ float sDec[KDA ? DK : 1];  // KDA: e^{G_last, c}
 
@@ -87,11 +118,11 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
   const size_t sbase = dh ? (size_t)snapshot_offset(cu, sq, Tlen, nts * BT) : 0;
 
   // accumulators: block (rb, cb), lane (n, gq): key row RW w + 16 rb + 4 gq + i, column v0 + 16 cb + n
-  f32x4 acc[RB][2];
+  f32x4 acc[RB][CBN];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < CBN; ++cb) {
       if (dht) {
         const float4 x = *reinterpret_cast<const float4*>(
             dht + hbase + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq);
@@ -104,49 +135,65 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < CBN; ++cb)
         *reinterpret_cast<float4*>(dst + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq) =
             make_float4(acc[rb][cb][0], acc[rb][cb][1], acc[rb][cb][2], acc[rb][cb][3]);
   };
 
-  for (int ic = NC - 1; ic >= 0; --ic) {
+  // this thread's 8 x 8 block: q (waves 0 .. NQB / 64 - 1) or dO (the next
+  // wave's first 32 lanes); roles are uniform per wave
+  constexpr int QW = NQB / 64;
+  static_assert(NQB % 64 == 0, "whole q waves");
+  const bool isq = w < QW, isd = w == QW && lane < BT / 8 * BVT / 8;
+  const int bq = isq ? tid : tid - NQB;
+  const int tb = isq ? bq / (DK / 8) : bq / (BVT / 8);     // token block
+  const int cb8 = isq ? bq % (DK / 8) : bq % (BVT / 8);    // channel / column block
+  // raw loads of a chunk: the block's 8 rows, and the gate values; two
+  // buffers, so that the loads of chunk ic - 2 fly during chunks ic and ic - 1
+  uint4 rawA[8], rawB[8];
+  float gvA[KDA ? BT : 1], gvB[KDA ? BT : 1];
+  auto load = [&](int ic, uint4 (&raw)[8], float (&gv)[KDA ? BT : 1]) __attribute__((always_inline)) {
     const int c0 = bos + ic * BT;
     const int nrow = eos - c0 < BT ? eos - c0 : BT;
-
-    // ---- global loads of the chunk (rows past its end repeat the last row; masked below)
-    uint4 qr[QPT];
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int u = tid + 256 * i, t = u / (DK / 8), cu8 = u % (DK / 8);
-      const int tc = t < nrow ? t : nrow - 1;
-      qr[i] = *reinterpret_cast<const uint4*>(q + ((size_t)(c0 + tc) * Hk + jk) * DK + 8 * cu8);
+    for (int r = 0; r < 8; ++r) {
+      const int t = 8 * tb + r, tc = t < nrow ? t : nrow - 1;
+      if (isq) raw[r] = *reinterpret_cast<const uint4*>(q + ((size_t)(c0 + tc) * Hk + jk) * DK + 8 * cb8);
+      else if (isd) raw[r] = *reinterpret_cast<const uint4*>(dout + ((size_t)(c0 + tc) * HV + j) * DV + v0 + 8 * cb8);
     }
-    const int dt_ = tid / (BVT / 8), du = tid % (BVT / 8);   // dO unit: token, 8-column group
-    const int dtc = dt_ < nrow ? dt_ : nrow - 1;
-    const uint4 dr = *reinterpret_cast<const uint4*>(dout + ((size_t)(c0 + dtc) * HV + j) * DV + v0 + 8 * du);
-
-    // ---- chunk-local cumulative gates
     if constexpr (KDA) {
       if (tid < DK) {
-        float gv[BT];
 #pragma unroll
         for (int t = 0; t < BT; ++t) {
           const int tc = t < nrow ? t : nrow - 1;
           gv[t] = gk[((size_t)(c0 + tc) * HV + j) * DK + tid];
         }
+      }
+    } else {
+      if (w == 0) {
+        const int tc = lane < nrow ? lane : nrow - 1;
+        gv[0] = g ? g[(size_t)(c0 + tc) * HV + j] : (gamma ? gamma[j] : 0.f);
+      }
+    }
+  };
+
+  auto step = [&](int ic, uint4 (&raw)[8], float (&gv)[KDA ? BT : 1]) __attribute__((always_inline)) {
+    const int nrow = eos - (bos + ic * BT) < BT ? eos - (bos + ic * BT) : BT;
+
+    // ---- chunk-local cumulative gates
+    if constexpr (KDA) {
+      if (tid < DK) {
         float G = 0.f;
 #pragma unroll
         for (int t = 0; t < BT; ++t) {
           G += t < nrow ? gv[t] : 0.f;
-          sG[t][tid] = G;
+          sG[t][tid] = scale * __expf(G);
         }
         sDec[tid] = __expf(G);
       }
     } else {
       if (w == 0) {
-        const int tc = lane < nrow ? lane : nrow - 1;
-        float gl = g ? g[(size_t)(c0 + tc) * HV + j] : (gamma ? gamma[j] : 0.f);
-        gl = lane < nrow ? gl : 0.f;
+        const float gl = lane < nrow ? gv[0] : 0.f;
         const float G = intra::wave_incl_scan(gl, lane);
         sGam[lane] = lane < nrow ? scale * __expf(G) : 0.f;
         if (lane == nrow - 1) sGam[BT] = __expf(G);
@@ -154,42 +201,72 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
     }
     __syncthreads();
 
-    // ---- transposed operand tiles
+    // ---- the block transposed into its tile: row = channel (column) 8 cb8 + e,
+    // 8-token unit tb at position tb ^ (cb8 & 7); tokens past the chunk end are 0.
+    // The gated operand (KDA: q, GDN: dO) goes in as a bf16 hi + lo pair.
+    const int col = 8 * (tb ^ (cb8 & 7));
+    const bool gated = KDA && isq;   // GDN gates dO in a second pass below
+    if ((isq || isd) && !gated) {
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int u = tid + 256 * i, t = u / (DK / 8), cu8 = u % (DK / 8);
-      const uint32_t wv[4] = {qr[i].x, qr[i].y, qr[i].z, qr[i].w};
+      for (int r = 0; r < 8; ++r)
+        if (8 * tb + r >= nrow) raw[r] = make_uint4(0u, 0u, 0u, 0u);
+      uint4 O[8];
+      transpose8(raw, O);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int c = 8 * cu8 + e;
-        const uint32_t bits = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xFFFFu);
-        if constexpr (KDA) {
-          const float a = t < nrow ? bf2f((bf16_t)bits) * scale * __expf(sG[t][c]) : 0.f;
-          const bf16_t hi = f2bf(a);
-          sAh[c][t] = hi;
-          sAl[c][t] = f2bf(a - bf2f(hi));
-        } else {
-          sAh[c][t] = t < nrow ? (bf16_t)bits : (bf16_t)0;
-        }
+        bf16_t* dst = isq ? &sAh[8 * cb8 + e][col] : (KDA ? &sBh[8 * cb8 + e][col] : &sBr[8 * cb8 + e][col]);
+        *reinterpret_cast<uint4*>(dst) = O[e];
       }
-    }
-    {
-      const uint32_t wv[4] = {dr.x, dr.y, dr.z, dr.w};
+    } else if (isq) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int c = 8 * du + e;
-        const uint32_t bits = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xFFFFu);
-        if constexpr (KDA) {
-          sBh[c][dt_] = dt_ < nrow ? (bf16_t)bits : (bf16_t)0;
-        } else {
-          const float b = bf2f((bf16_t)bits) * sGam[dt_];   // 0 past the chunk end
-          const bf16_t hi = f2bf(b);
-          sBh[c][dt_] = hi;
-          sBl[c][dt_] = f2bf(b - bf2f(hi));
+        const int c = 8 * cb8 + e;
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          float x[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int t = 8 * tb + 2 * p2 + h;
+            // KDA: q * scale e^{G_t,c} (0 past the end); GDN: dO * scale e^{G_t} (0 past the end)
+            const float f = KDA ? (t < nrow ? sG[t][c] : 0.f) : sGam[t];
+            x[h] = bf2f((bf16_t)elem16(raw[2 * p2 + h], e)) * f;
+          }
+          const uint32_t h0 = f2bf(x[0]), h1 = f2bf(x[1]);
+          hw[p2] = h0 | (h1 << 16);
+          lw[p2] = (uint32_t)f2bf(x[0] - bf2f((bf16_t)h0)) | ((uint32_t)f2bf(x[1] - bf2f((bf16_t)h1)) << 16);
         }
+        bf16_t* dh_ = KDA ? &sAh[c][col] : &sBh[c][col];
+        bf16_t* dl_ = KDA ? &sAl[c][col] : &sBl[c][col];
+        *reinterpret_cast<uint4*>(dh_) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(dl_) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
     }
     __syncthreads();
+    if constexpr (!KDA) {
+      // dO * scale e^{G_t} as a bf16 hi + lo pair: one 8-token row piece per
+      // thread (unit u of row c holds tokens 8 (u ^ (c / 8 & 7)) .. + 7)
+      if (tid < BVT * BT / 8) {
+        const int c = tid / (BT / 8), u = tid % (BT / 8);
+        const int t0 = 8 * (u ^ ((c >> 3) & 7));
+        const uint4 r = *reinterpret_cast<const uint4*>(&sBr[c][8 * u]);
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          const uint32_t wv = word(r, p2);
+          const float x0 = __builtin_bit_cast(float, wv << 16) * sGam[t0 + 2 * p2];
+          const float x1 = __builtin_bit_cast(float, wv & 0xFFFF0000u) * sGam[t0 + 2 * p2 + 1];
+          const uint32_t h0 = f2bf(x0), h1 = f2bf(x1);
+          hw[p2] = h0 | (h1 << 16);
+          lw[p2] = (uint32_t)f2bf(x0 - bf2f((bf16_t)h0)) | ((uint32_t)f2bf(x1 - bf2f((bf16_t)h1)) << 16);
+        }
+        *reinterpret_cast<uint4*>(&sBh[c][8 * u]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&sBl[c][8 * u]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      }
+      __syncthreads();
+    }
+    // this buffer is free again: the chunk after next
+    if (ic >= 2) load(ic - 2, raw, gv);
 
     // ---- snapshot, decay, accumulate
     if (dh && ic % nts == 0) store_state(dh + ((sbase + ic / nts) * HV + j) * (size_t)DV * DK);
@@ -199,29 +276,39 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) dec[i] = KDA ? sDec[RW * w + 16 * rb + 4 * gq + i] : sGam[BT];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] *= dec;
+      for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] *= dec;
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const u32x4 ah = *reinterpret_cast<const u32x4*>(&sAh[RW * w + 16 * rb + n][32 * s + 8 * gq]);
+        const int ra = RW * w + 16 * rb + n;
+        const int ca = 8 * ((4 * s + gq) ^ ((ra >> 3) & 7));
+        const u32x4 ah = *reinterpret_cast<const u32x4*>(&sAh[ra][ca]);
         u32x4 al;
-        if constexpr (KDA) al = *reinterpret_cast<const u32x4*>(&sAl[RW * w + 16 * rb + n][32 * s + 8 * gq]);
+        if constexpr (KDA) al = *reinterpret_cast<const u32x4*>(&sAl[ra][ca]);
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const u32x4 bh = *reinterpret_cast<const u32x4*>(&sBh[16 * cb + n][32 * s + 8 * gq]);
+        for (int cb = 0; cb < CBN; ++cb) {
+          const int rbv = 16 * cb + n;
+          const int cbv = 8 * ((4 * s + gq) ^ ((rbv >> 3) & 7));
+          const u32x4 bh = *reinterpret_cast<const u32x4*>(&sBh[rbv][cbv]);
           acc[rb][cb] = mma_bf(ah, bh, acc[rb][cb]);
           if constexpr (KDA) {
             acc[rb][cb] = mma_bf(al, bh, acc[rb][cb]);
           } else {
-            const u32x4 bl = *reinterpret_cast<const u32x4*>(&sBl[16 * cb + n][32 * s + 8 * gq]);
+            const u32x4 bl = *reinterpret_cast<const u32x4*>(&sBl[rbv][cbv]);
             acc[rb][cb] = mma_bf(ah, bl, acc[rb][cb]);
           }
         }
       }
     }
     __syncthreads();
+  };
+  if (NC > 0) load(NC - 1, rawA, gvA);
+  if (NC > 1) load(NC - 2, rawB, gvB);
+  for (int ic = NC - 1; ic >= 0; ic -= 2) {
+    step(ic, rawA, gvA);
+    if (ic >= 1) step(ic - 1, rawB, gvB);
   }
   if (dh0) store_state(dh0 + hbase);
 }
