@@ -37,10 +37,11 @@ namespace {
 
 constexpr int BT = 64;
 #ifndef GDN_BWD_BVT
-#define GDN_BWD_BVT 16
+#define GDN_BWD_BVT 32
 #endif
 constexpr int BVT = GDN_BWD_BVT;   // V columns per work-group
 constexpr int CBN = BVT / 16;      // 16-column blocks per work-group
+static_assert(BVT * 64 / 8 <= 256, "one gating unit per thread");
 constexpr int TP = BT + 8;     // padded token row of the transposed tiles (bf16)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -94,10 +95,14 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, gq = lane >> 4;
+  // work-group -> (sequence, head, V tile): ids are dealt round-robin to the
+  // 8 XCDs; the NVT tiles of a (sequence, head), which read the same q rows,
+  // share an XCD (its L2)
   const int NVT = DV / BVT;
   const int bid = blockIdx.x;
-  const int vt = bid % NVT;
-  const int sh = bid / NVT;
+  const int xcd = bid & 7, pos = bid >> 3;
+  const int vt = pos % NVT;
+  const int sh = (pos / NVT) * 8 + xcd;
   if (sh >= N * HV) return;
   const int sq = sh / HV, j = sh - sq * HV;
   const int jk = j / (HV / Hk);
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
 
 template <int DK, bool KDA>
 hipError_t launch_k(const BwdDhArgs& a, hipStream_t s) {
-  const long long blocks = (long long)a.N * a.HV * (DK / BVT);
+  const long long blocks = ((long long)a.N * a.HV + 7) / 8 * 8 * (DK / BVT);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, KDA>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.dout, a.g, a.g_gamma, a.gk, a.scale, a.dht, a.dh,
