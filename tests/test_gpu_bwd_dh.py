@@ -52,3 +52,22 @@ def test_bwd_dh_kda_k128_varlen():
     inp = workloads.make_prefill(1, 200, 2, 2, 128, 128, dtype=torch.bfloat16, seed=64, gate="kda",
                                  seqlens=[64, 136], name="bwd_kda_K128")
     _case(inp, "kda", 64, seed=65)
+
+
+def test_bwd_dh_b4_t4096_sampled_heads():
+    """The shape bench.py times (B=4 T=4096 H=16 K=V=128, scalar gate, dh every
+    chunk, dht in): two sampled heads, every chunk of every sequence."""
+    inp = workloads.gdn_bf16_b4_t4096()
+    B, T, Hk, HV, K, V = inp.dims
+    rng = np.random.default_rng(66)
+    heads = [0, 9]
+    do = torch.from_numpy(rng.standard_normal((B, T, HV, V)).astype(np.float32)).to(torch.bfloat16)
+    dht = torch.from_numpy((rng.standard_normal((B, HV, V, K)) * 0.1).astype(np.float32))
+    print(f"bwd dh full size heads={heads}", flush=True)
+    dh, dh0 = binding.chunk_bwd_dh(dv(inp.q), dv(do), g=dv(inp.g), scale=inp.scale, dht=dv(dht), split_size=64)
+    torch.cuda.synchronize()
+    # Hk = HV here: v-head h reads q head h
+    dh_ref, dh0_ref = oracle.state_grad_scan(inp.q[:, :, heads], do[:, :, heads], inp.scale,
+                                             g=inp.g[:, :, heads], dht=dht[:, heads], split_size=64)
+    check("dh", dh.cpu()[:, heads], dh_ref, torch.bfloat16)
+    check("dh0", dh0.cpu()[:, heads], dh0_ref, torch.bfloat16)

@@ -65,3 +65,23 @@ def test_prefill_handoff_decode_chain():
     check("o", o.cpu(), o_ref, torch.bfloat16, stores=2)
     check("state", ps.cpu()[slots], s_ref[slots], torch.bfloat16, stores=2)
     assert torch.equal(ps.cpu()[[0, 3, 5]], dec.state[[0, 3, 5]])
+
+
+def test_state_to_pool_full_size_sampled():
+    """256 sequences x 32 heads into a shuffled 256-slot pool, as bench.py
+    times it; eight sampled sequences checked bit for bit, and a pool slot no
+    sequence names stays untouched."""
+    N, HV, K = 256, 32, 128
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1005)
+    ht = torch.randn((N, HV, K, K), generator=gen, device=DEV) * 0.1
+    pool = torch.full((N + 1, HV, K, K), 3.0, dtype=torch.bfloat16, device=DEV)
+    idx = torch.randperm(N, generator=gen, device=DEV).to(torch.int32)
+    print("handoff full size", flush=True)
+    binding.state_to_pool(ht, pool, idx)
+    torch.cuda.synchronize()
+    ids = idx.cpu().tolist()
+    for n in (0, 1, 77, 128, 200, 254, 255, 31):
+        want = oracle.state_to_pool(ht[n:n + 1].cpu().numpy(), np.zeros((1, HV, K, K)), [0])[0]
+        assert np.array_equal(pool[ids[n]].cpu().double().numpy(), want), n
+    assert torch.all(pool[N] == 3.0)

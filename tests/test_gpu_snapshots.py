@@ -91,3 +91,19 @@ def test_gdn_g_gamma(dtype):
                                          cu_seqlens=inp.cu_seqlens, g_gamma=gamma)
     check("o", o.cpu(), o_ref, dtype)
     check("ht", ht.cpu(), ht_ref, dtype)
+
+
+def test_snapshots_b4_t4096_sampled_heads():
+    """The headline workload (B=4 T=4096 H=16 K=V=128) with snapshots every 64
+    tokens, as bench.py times it: two sampled heads of every sequence."""
+    inp = workloads.gdn_bf16_b4_t4096()
+    heads = [3, 12]
+    print(f"snapshots full size heads={heads}", flush=True)
+    o, ht, hs = binding.gdn_chunk_fwd(dv(inp.q), dv(inp.k), dv(inp.v), dv(inp.g), dv(inp.beta),
+                                      scale=inp.scale, split_size=64)
+    torch.cuda.synchronize()
+    _, ht_ref, hs_ref = oracle.gdn_recurrent(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale,
+                                             heads=heads, split_size=64)
+    hs = hs.cpu()
+    print("  h_snap", check("h_snap", hs[:, heads], hs_ref[:, heads], torch.bfloat16), flush=True)
+    check("ht", ht.cpu()[:, heads], ht_ref[:, heads], torch.bfloat16)
