@@ -318,6 +318,201 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
   if (dh0) store_state(dh0 + hbase);
 }
 
+// Scalar gate (g or gamma): two barriers per chunk.  Staging phase: the first
+// DK / 64 waves transpose the q block rows (8 x 8 blocks, v_perm_b32), waves 2 and 3
+// gate dO -- thread (column c, 8-token unit u) reads its 8 values, scales
+// them by scale e^{G_t} and writes the hi and lo rows.  Product phase: the
+// MFMAs of this chunk, while wave 0 forms the next chunk's gate factors into
+// the other buffer and the loads of the chunk after next are issued.
+template <int DK>
+__global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ g,
+    const float* __restrict__ gamma, float scale,
+    const float* __restrict__ dht, float* __restrict__ dh, int nts, float* __restrict__ dh0,
+    const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV) {
+  constexpr int DV = DK;
+  constexpr int RW = DK / 4;
+  constexpr int RB = RW / 16;
+  constexpr int QB = BT / 8 * DK / 8;    // q blocks: one per thread of the first QB / 64 waves
+  constexpr int QPT = 1;
+  constexpr int DCPT = BVT * BT / 8 / 128;   // dO units per thread of waves 2, 3
+  static_assert(QB % 64 == 0 && QB <= 128 && DCPT * 128 == BVT * BT / 8, "thread roles");
+  __shared__ __attribute__((aligned(16))) bf16_t sAh[DK][TP];
+  __shared__ __attribute__((aligned(16))) bf16_t sBh[BVT][TP];
+  __shared__ __attribute__((aligned(16))) bf16_t sBl[BVT][TP];
+  __shared__ float sGam[2][BT + 1];   // scale e^{G_t}; e^{G_last} at [BT]; two chunks
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, gq = lane >> 4;
+  const int NVT = DV / BVT;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, pos = bid >> 3;
+  const int vt = pos % NVT;
+  const int sh = (pos / NVT) * 8 + xcd;
+  if (sh >= N * HV) return;
+  const int sq = sh / HV, j = sh - sq * HV;
+  const int jk = j / (HV / Hk);
+  const int v0 = vt * BVT;
+  int bos, eos;
+  if (cu) {
+    long long b0 = cu[sq], b1 = cu[sq + 1];
+    b0 = b0 < 0 ? 0 : (b0 > Tlen ? Tlen : b0);
+    b1 = b1 < b0 ? b0 : (b1 > Tlen ? Tlen : b1);
+    bos = (int)b0;
+    eos = (int)b1;
+  } else {
+    bos = sq * Tlen;
+    eos = bos + Tlen;
+  }
+  const int NC = (eos - bos + BT - 1) / BT;
+  const size_t hbase = (size_t)sh * DV * DK;
+  const size_t sbase = dh ? (size_t)snapshot_offset(cu, sq, Tlen, nts * BT) : 0;
+
+  f32x4 acc[RB][CBN];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) {
+      if (dht) {
+        const float4 x = *reinterpret_cast<const float4*>(
+            dht + hbase + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq);
+        acc[rb][cb] = f32x4{x.x, x.y, x.z, x.w};
+      } else {
+        acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  auto store_state = [&](float* dst) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CBN; ++cb)
+        *reinterpret_cast<float4*>(dst + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq) =
+            make_float4(acc[rb][cb][0], acc[rb][cb][1], acc[rb][cb][2], acc[rb][cb][3]);
+  };
+
+  // roles: the first QB / 64 waves -> q blocks; waves 2, 3 -> dO (columns
+  // dc + 16 cc, 8-token unit du); with DK = 64 wave 1 stages nothing
+  const bool isq = tid < QB, isd = tid >= 128;
+  const int dc = (tid - 128) / (BT / 8), du = (tid - 128) % (BT / 8);
+  // raw loads of a chunk (two buffers)
+  uint4 rqA[QPT][8], rqB[QPT][8];
+  bf16_t rdA[DCPT][8], rdB[DCPT][8];
+  float gvA, gvB;
+  auto load = [&](int ic, uint4 (&rq)[QPT][8], bf16_t (&rd)[DCPT][8], float& gv) __attribute__((always_inline)) {
+    const int c0 = bos + ic * BT;
+    const int nrow = eos - c0 < BT ? eos - c0 : BT;
+    if (isq) {
+#pragma unroll
+      for (int k2 = 0; k2 < QPT; ++k2) {
+        const int bq = tid + 128 * k2, tb = bq / (DK / 8), cb8 = bq % (DK / 8);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int t = 8 * tb + r, tc = t < nrow ? t : nrow - 1;
+          rq[k2][r] = *reinterpret_cast<const uint4*>(q + ((size_t)(c0 + tc) * Hk + jk) * DK + 8 * cb8);
+        }
+      }
+    } else if (isd) {
+#pragma unroll
+      for (int cc = 0; cc < DCPT; ++cc)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int t = 8 * du + r, tc = t < nrow ? t : nrow - 1;
+          rd[cc][r] = dout[((size_t)(c0 + tc) * HV + j) * DV + v0 + dc + 16 * cc];
+        }
+    }
+    if (w == 0) {
+      const int tc = lane < nrow ? lane : nrow - 1;
+      gv = g ? g[(size_t)(c0 + tc) * HV + j] : (gamma ? gamma[j] : 0.f);
+    }
+  };
+  // wave 0: gate factors of chunk ic into buffer b
+  auto gates = [&](int ic, float gv, int b) __attribute__((always_inline)) {
+    const int nrow = eos - (bos + ic * BT) < BT ? eos - (bos + ic * BT) : BT;
+    const float gl = lane < nrow ? gv : 0.f;
+    const float G = intra::wave_incl_scan(gl, lane);
+    sGam[b][lane] = lane < nrow ? scale * __expf(G) : 0.f;
+    if (lane == nrow - 1) sGam[b][BT] = __expf(G);
+  };
+
+  auto step = [&](int ic, int b, uint4 (&rq)[QPT][8], bf16_t (&rd)[DCPT][8], float& gv,
+                  uint4 (&rqN)[QPT][8], bf16_t (&rdN)[DCPT][8], float& gvN) __attribute__((always_inline)) {
+    const int nrow = eos - (bos + ic * BT) < BT ? eos - (bos + ic * BT) : BT;
+    // ---- staging
+    if (isq) {
+#pragma unroll
+      for (int k2 = 0; k2 < QPT; ++k2) {
+        const int bq = tid + 128 * k2, tb = bq / (DK / 8), cb8 = bq % (DK / 8);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          if (8 * tb + r >= nrow) rq[k2][r] = make_uint4(0u, 0u, 0u, 0u);
+        uint4 O[8];
+        transpose8(rq[k2], O);
+        const int col = 8 * (tb ^ (cb8 & 7));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(&sAh[8 * cb8 + e][col]) = O[e];
+      }
+    } else if (isd) {
+      const int t0 = 8 * du;
+#pragma unroll
+      for (int cc = 0; cc < DCPT; ++cc) {
+        const int c = dc + 16 * cc;
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          const float x0 = bf2f(rd[cc][2 * p2]) * sGam[b][t0 + 2 * p2];       // 0 past the chunk end
+          const float x1 = bf2f(rd[cc][2 * p2 + 1]) * sGam[b][t0 + 2 * p2 + 1];
+          const uint32_t h0 = f2bf(x0), h1 = f2bf(x1);
+          hw[p2] = h0 | (h1 << 16);
+          lw[p2] = (uint32_t)f2bf(x0 - bf2f((bf16_t)h0)) | ((uint32_t)f2bf(x1 - bf2f((bf16_t)h1)) << 16);
+        }
+        const int col = 8 * (du ^ ((c >> 3) & 7));
+        *reinterpret_cast<uint4*>(&sBh[c][col]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&sBl[c][col]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      }
+    }
+    __syncthreads();
+    // ---- products; the next chunk's gate factors; the loads of the chunk after next
+    if (w == 0 && ic >= 1) gates(ic - 1, gvN, b ^ 1);
+    if (ic >= 2) load(ic - 2, rq, rd, gv);
+    if (dh && ic % nts == 0) store_state(dh + ((sbase + ic / nts) * HV + j) * (size_t)DV * DK);
+    const float dec = sGam[b][BT];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] *= dec;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int ra = RW * w + 16 * rb + n;
+        const u32x4 ah = *reinterpret_cast<const u32x4*>(&sAh[ra][8 * ((4 * s2 + gq) ^ ((ra >> 3) & 7))]);
+#pragma unroll
+        for (int cb = 0; cb < CBN; ++cb) {
+          const int rbv = 16 * cb + n;
+          const int cbv = 8 * ((4 * s2 + gq) ^ ((rbv >> 3) & 7));
+          acc[rb][cb] = mma_bf(ah, *reinterpret_cast<const u32x4*>(&sBh[rbv][cbv]), acc[rb][cb]);
+          acc[rb][cb] = mma_bf(ah, *reinterpret_cast<const u32x4*>(&sBl[rbv][cbv]), acc[rb][cb]);
+        }
+      }
+    }
+    __syncthreads();
+    (void)rqN; (void)rdN;
+  };
+
+  if (NC > 0) load(NC - 1, rqA, rdA, gvA);
+  if (NC > 1) load(NC - 2, rqB, rdB, gvB);
+  if (NC > 0) {
+    if (w == 0) gates(NC - 1, gvA, 0);
+    __syncthreads();
+  }
+  // chunk NC - 1 - 2i uses buffer A and gate slot 0, NC - 2 - 2i buffer B and slot 1
+  for (int ic = NC - 1; ic >= 0; ic -= 2) {
+    step(ic, 0, rqA, rdA, gvA, rqB, rdB, gvB);
+    if (ic >= 1) step(ic - 1, 1, rqB, rdB, gvB, rqA, rdA, gvA);
+  }
+  if (dh0) store_state(dh0 + hbase);
+}
+
 template <int DK, bool KDA>
 hipError_t launch_k(const BwdDhArgs& a, hipStream_t s) {
   const long long blocks = ((long long)a.N * a.HV + 7) / 8 * 8 * (DK / BVT);
@@ -330,9 +525,19 @@ hipError_t launch_k(const BwdDhArgs& a, hipStream_t s) {
 
 }  // namespace
 
+template <int DK>
+hipError_t launch_gdn(const BwdDhArgs& a, hipStream_t s) {
+  const long long blocks = ((long long)a.N * a.HV + 7) / 8 * 8 * (DK / BVT);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((chunk_bwd_dh_gdn_kernel<DK>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const bf16_t*)a.q, (const bf16_t*)a.dout, a.g, a.g_gamma, a.scale, a.dht, a.dh,
+                     a.split_chunks, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dh(const BwdDhArgs& a, hipStream_t s) {
   if (a.gk) return a.K == 128 ? launch_k<128, true>(a, s) : launch_k<64, true>(a, s);
-  return a.K == 128 ? launch_k<128, false>(a, s) : launch_k<64, false>(a, s);
+  return a.K == 128 ? launch_gdn<128>(a, s) : launch_gdn<64>(a, s);
 }
 
 }  // namespace gdn
