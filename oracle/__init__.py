@@ -13,8 +13,9 @@ Sources (cited by page and function in each module):
 
 * "sglang srt/layers/attention/fla/chunk_fwd.py" -- GDN fused beta*K K^T +
   solve_tril kernel and its host wrapper;
-* "fla ops/common/chunk_h.py" -- chunked state recurrence (``chunk_fwd_kernel_h``)
-  and the backward state-gradient scan (``chunk_bwd_kernel_dh``);
+* "fla ops/common/chunk_h.py" -- chunked state recurrence (``chunk_fwd_kernel_h``,
+  also as the standalone decay-only state scan) and the backward
+  state-gradient scan (``chunk_bwd_kernel_dh``);
 * "vLLM kimi_k3 amd ops kda/chunk_intra" -- KDA inter-sub-chunk Aqk/Akk +
   solve_tril fused kernel;
 * "flashinfer gdn_kernels/gdn_decode_bf16_state.py" -- GDN decode with a bf16
@@ -34,10 +35,11 @@ from .decode import decode_gate, decode_normalize, gdn_decode
 from .bf16 import round_to_bf16
 from .handoff import state_to_pool
 from .backward import state_grad_scan
+from .state_scan import state_scan
 
 __all__ = [
     "delta_rule_recurrent", "gdn_recurrent", "kda_recurrent",
     "chunk_intra_matrices",
     "decode_gate", "decode_normalize", "gdn_decode",
-    "round_to_bf16", "state_to_pool", "state_grad_scan",
+    "round_to_bf16", "state_to_pool", "state_grad_scan", "state_scan",
 ]

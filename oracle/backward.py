@@ -9,7 +9,8 @@ start of the sequence.
 
 That is the gradient of the decay-only recurrence
     h_t = D_t h_{t-1} + (terms free of h),   o_t = scale * h_t q_t
-(D_t = e^{g_t}, or diag(e^{gk_t}) on the key channels), taken token by token
+(D_t = e^{g_t}, diag(e^{gk_t}) on the key channels and / or diag(e^{gv_t}) on
+the value channels, as in the forward state scan), taken token by token
 here: at token t (last to first) the output's term scale * do_t q_t^T joins the
 gradient of h_t, then the gradient passes to h_{t-1} through D_t.  States are
 [V, K] (value rows, key columns), like the forward oracle.
@@ -22,7 +23,7 @@ import numpy as np
 from .recurrence import _f64, sequences
 
 
-def state_grad_scan(q, dout, scale: float, g=None, g_gamma=None, gk=None, dht=None,
+def state_grad_scan(q, dout, scale: float, g=None, g_gamma=None, gk=None, gv=None, dht=None,
                     cu_seqlens=None, split_size=None, chunk_size: int = 64):
     """Return (dh [S, HV, V, K] or None, dh0 [N, HV, V, K]), float64.
 
@@ -30,7 +31,7 @@ def state_grad_scan(q, dout, scale: float, g=None, g_gamma=None, gk=None, dht=No
     0, r, 2r, ... (r = split_size / chunk_size): ceil(length / split_size)
     entries per sequence."""
     q, dout = _f64(q), _f64(dout)
-    g, gk, dht = _f64(g), _f64(gk), _f64(dht)
+    g, gk, gv, dht = _f64(g), _f64(gk), _f64(gv), _f64(dht)
     B, T, Hk, K = q.shape
     HV, V = dout.shape[2], dout.shape[3]
     if g_gamma is not None:
@@ -56,6 +57,8 @@ def state_grad_scan(q, dout, scale: float, g=None, g_gamma=None, gk=None, dht=No
                         D = D * np.exp(g[b, t, j])
                     if gk is not None:
                         D = D * np.exp(gk[b, t, j])[None, :]
+                    if gv is not None:
+                        D = D * np.exp(gv[b, t, j])[:, None]
             dh0[n, j] = D
         snaps += seq_snaps
     dh = None

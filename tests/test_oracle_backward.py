@@ -21,17 +21,19 @@ import oracle.backward as bwd
 def _problem(rng, B, T, Hk, HV, K, V, gate):
     q = rng.standard_normal((B, T, Hk, K))
     do = rng.standard_normal((B, T, HV, V))
-    g = gk = gamma = None
-    if gate == "gdn":
+    g = gk = gamma = gv = None
+    if gate in ("gdn", "gdn+gv"):
         g = -np.logaddexp(0, rng.standard_normal((B, T, HV))) * 0.3
-    elif gate == "kda":
+    if gate in ("gv", "gdn+gv"):
+        gv = -np.logaddexp(0, rng.standard_normal((B, T, HV, V))) * 0.3
+    if gate == "kda":
         gk = -np.logaddexp(0, rng.standard_normal((B, T, HV, K))) * 0.3
     elif gate == "gamma":
         gamma = -np.abs(rng.standard_normal(HV)) * 0.2
-    return q, do, g, gk, gamma
+    return q, do, g, gk, gamma, gv
 
 
-def _autograd_grad(q, do, g, gk, gamma, dht, scale, b, bos, eos, start, j, kh, rng):
+def _autograd_grad(q, do, g, gk, gamma, dht, scale, b, bos, eos, start, j, kh, rng, gv=None):
     """d loss / d state after token start - 1 (the state before token `start`)."""
     V, K = do.shape[3], q.shape[3]
     S0 = torch.zeros((V, K), dtype=torch.float64, requires_grad=True)
@@ -44,6 +46,8 @@ def _autograd_grad(q, do, g, gk, gamma, dht, scale, b, bos, eos, start, j, kh, r
             S = S * float(np.exp(gamma[j]))
         if gk is not None:
             S = S * torch.from_numpy(np.exp(gk[b, t, j]))[None, :]
+        if gv is not None:
+            S = S * torch.from_numpy(np.exp(gv[b, t, j]))[:, None]
         kv = torch.from_numpy(np.outer(rng.standard_normal(V), rng.standard_normal(K)))
         S = S + kv
         o = scale * (S @ torch.from_numpy(q[b, t, kh]))
@@ -54,27 +58,27 @@ def _autograd_grad(q, do, g, gk, gamma, dht, scale, b, bos, eos, start, j, kh, r
     return S0.grad.numpy()
 
 
-@pytest.mark.parametrize("gate", ["gdn", "kda", "gamma", None])
+@pytest.mark.parametrize("gate", ["gdn", "kda", "gamma", "gv", "gdn+gv", None])
 def test_state_grad_matches_autograd(gate):
     rng = np.random.default_rng(50)
     B, T, Hk, HV, K, V, C = 1, 11, 1, 2, 4, 3, 4
     lens = [7, 0, 4]
     cu = np.concatenate([[0], np.cumsum(lens)])
-    q, do, g, gk, gamma = _problem(rng, B, T, Hk, HV, K, V, gate)
+    q, do, g, gk, gamma, gv = _problem(rng, B, T, Hk, HV, K, V, gate)
     dht = rng.standard_normal((len(lens), HV, V, K))
-    dh, dh0 = oracle.state_grad_scan(q, do, 0.7, g=g, g_gamma=gamma, gk=gk, dht=dht, cu_seqlens=cu,
+    dh, dh0 = oracle.state_grad_scan(q, do, 0.7, g=g, g_gamma=gamma, gk=gk, gv=gv, dht=dht, cu_seqlens=cu,
                                      split_size=2 * C, chunk_size=C)
     i = 0
     for n, L in enumerate(lens):
         bos, eos = cu[n], cu[n + 1]
         for j in range(HV):
-            got = _autograd_grad(q, do, g, gk, gamma, dht[n, j], 0.7, 0, bos, eos, bos, j, 0, rng)
+            got = _autograd_grad(q, do, g, gk, gamma, dht[n, j], 0.7, 0, bos, eos, bos, j, 0, rng, gv=gv)
             np.testing.assert_allclose(dh0[n, j], got, atol=1e-12)
         nsnap = -(-L // (2 * C))
         for s in range(nsnap):
             end = min(bos + (2 * s + 1) * C, eos)   # end of chunk 2 s
             for j in range(HV):
-                got = _autograd_grad(q, do, g, gk, gamma, dht[n, j], 0.7, 0, bos, eos, end, j, 0, rng)
+                got = _autograd_grad(q, do, g, gk, gamma, dht[n, j], 0.7, 0, bos, eos, end, j, 0, rng, gv=gv)
                 np.testing.assert_allclose(dh[i + s, j], got, atol=1e-12)
         i += nsnap
     assert dh.shape[0] == i
@@ -88,6 +92,7 @@ MUTATIONS = [
                     D = D + scale * np.outer(dout[b, t, j], q[b, t, kh])"""),   # decay before the output term
     ("D = D + scale * np.outer(dout[b, t, j], q[b, t, kh])", "D = D + np.outer(dout[b, t, j], q[b, t, kh])"),  # scale dropped
     ("seq_snaps[ic // r][j] = D", "seq_snaps[ic // r][j] = D * 0 + dh0[n, j]"),  # snapshot of the wrong state
+    ("D = D * np.exp(gv[b, t, j])[:, None]", "D = D * np.exp(gv[b, t, j])[None, :]"),     # gv on the key axis
 ]
 
 
@@ -99,10 +104,11 @@ def test_state_grad_mutant_is_caught(old, new):
     m = types.ModuleType("bwd_mutant")
     exec(compile(src, "<mutant>", "exec"), m.__dict__)
     rng = np.random.default_rng(51)
-    q, do, g, gk, gamma = _problem(rng, 1, 6, 1, 1, 3, 2, "gdn")
-    dh, dh0 = m.state_grad_scan(q, do, 0.7, g=g, split_size=2, chunk_size=2)
-    ok = np.allclose(dh0[0, 0], _autograd_grad(q, do, g, None, None, None, 0.7, 0, 0, 6, 0, 0, 0, rng), atol=1e-12)
+    q, do, g, gk, gamma, gv = _problem(rng, 1, 6, 1, 1, 3, 3, "gdn+gv")   # K = V: a wrong axis still runs
+    dh, dh0 = m.state_grad_scan(q, do, 0.7, g=g, gv=gv, split_size=2, chunk_size=2)
+    ok = np.allclose(dh0[0, 0], _autograd_grad(q, do, g, None, None, None, 0.7, 0, 0, 6, 0, 0, 0, rng, gv=gv),
+                     atol=1e-12)
     ok = ok and all(np.allclose(dh[s, 0], _autograd_grad(q, do, g, None, None, None, 0.7, 0, 0, 6,
-                                                           min(2 * s + 2, 6), 0, 0, rng), atol=1e-12)
+                                                           min(2 * s + 2, 6), 0, 0, rng, gv=gv), atol=1e-12)
                     for s in range(3))
     assert not ok
