@@ -47,10 +47,14 @@ _SIGNATURES = {
                             _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_float, _c_float, _c_float, _c_int, _c_float, _c_void_p]),
-    "gdn_chunk_bwd_dh": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float,
-                                  _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
+    "gdn_chunk_bwd_dh": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_float, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                   _c_void_p]),
+    "gdn_chunk_fwd_h": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
+                                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                 _c_void_p]),
     "gdn_state_to_pool": (_c_int, [_c_void_p, _c_void_p, _c_void_p,
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
 }
@@ -116,7 +120,7 @@ def _need(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype], sh
         raise ValueError(f"{name} must be contiguous")
 
 
-STAGES = ("varlen_tables", "intra", "scan", "decode", "handoff", "bwd_dh")
+STAGES = ("varlen_tables", "intra", "scan", "decode", "handoff", "bwd_dh", "fwd_h")
 
 
 def profile_enable(on: bool = True) -> None:
@@ -309,38 +313,67 @@ def state_to_pool(ht: torch.Tensor, pool_state: torch.Tensor,
     return pool_state
 
 
-def chunk_bwd_dh(q: torch.Tensor, dout: torch.Tensor, g: Optional[torch.Tensor] = None,
-                 g_gamma: Optional[torch.Tensor] = None, gk: Optional[torch.Tensor] = None,
-                 scale: Optional[float] = None, dht: Optional[torch.Tensor] = None,
-                 cu_seqlens: Optional[torch.Tensor] = None, split_size: Optional[int] = 64,
-                 output_dh0: bool = True, chunk_size: int = 64):
-    """Backward state-gradient scan (bf16 q / dout).  Returns (dh [S,HV,V,K]
-    fp32 or None when ``split_size`` is None, dh0 [N,HV,V,K] fp32 or None)."""
-    if q.dim() != 4 or dout.dim() != 4:
-        raise ValueError("q must be [B, T, Hk, K] and dout [B, T, HV, V]")
-    B, T, Hk, K = q.shape
-    HV, V = dout.shape[2], dout.shape[3]
-    dev = q.device
+def _state_scan_args(a, b, an, bn, g, g_gamma, gk, gv, init, init_name, cu_seqlens):
+    if a.dim() != 4 or b.dim() != 4:
+        raise ValueError(f"{an} must be [B, T, Hk, K] and {bn} [B, T, HV, V]")
+    B, T, Hk, K = a.shape
+    HV, V = b.shape[2], b.shape[3]
+    dev = a.device
     bf = torch.bfloat16
-    _need(q, "q", bf, None, dev)
-    _need(dout, "dout", bf, (B, T, HV, V), dev)
+    _need(a, an, bf, None, dev)
+    _need(b, bn, bf, (B, T, HV, V), dev)
     _need(g, "g", torch.float32, (B, T, HV), dev)
     _need(g_gamma, "g_gamma", torch.float32, (HV,), dev)
     _need(gk, "gk", torch.float32, (B, T, HV, K), dev)
+    _need(gv, "gv", torch.float32, (B, T, HV, V), dev)
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int64, None, dev)
         N = cu_seqlens.numel() - 1
     else:
         N = B
-    _need(dht, "dht", torch.float32, (N, HV, V, K), dev)
+    _need(init, init_name, torch.float32, (N, HV, V, K), dev)
+    return B, T, Hk, HV, K, V, N, dev
+
+
+def _state_buffers(B, T, HV, V, K, N, dev, split_size, cu_seqlens, final):
+    snaps = None
+    if split_size is not None:
+        snaps = torch.empty((snapshot_count(B, T, split_size, cu_seqlens), HV, V, K),
+                            dtype=torch.float32, device=dev)
+    fin = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if final else None
+    return snaps, fin
+
+
+def chunk_bwd_dh(q: torch.Tensor, dout: torch.Tensor, g: Optional[torch.Tensor] = None,
+                 g_gamma: Optional[torch.Tensor] = None, gk: Optional[torch.Tensor] = None,
+                 scale: Optional[float] = None, dht: Optional[torch.Tensor] = None,
+                 cu_seqlens: Optional[torch.Tensor] = None, split_size: Optional[int] = 64,
+                 output_dh0: bool = True, chunk_size: int = 64, gv: Optional[torch.Tensor] = None):
+    """Backward state-gradient scan (bf16 q / dout).  Returns (dh [S,HV,V,K]
+    fp32 or None when ``split_size`` is None, dh0 [N,HV,V,K] fp32 or None)."""
+    B, T, Hk, HV, K, V, N, dev = _state_scan_args(q, dout, "q", "dout", g, g_gamma, gk, gv, dht, "dht",
+                                                  cu_seqlens)
     if scale is None:
         scale = K ** -0.5
-    dh = None
-    if split_size is not None:
-        dh = torch.empty((snapshot_count(B, T, split_size, cu_seqlens), HV, V, K),
-                         dtype=torch.float32, device=dev)
-    dh0 = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if output_dh0 else None
-    _check(lib().gdn_chunk_bwd_dh(_ptr(q), _ptr(dout), _ptr(g), _ptr(g_gamma), _ptr(gk), float(scale),
-                                  _ptr(dht), _ptr(dh), split_size or 0, _ptr(dh0), _ptr(cu_seqlens), N,
-                                  B, T, Hk, HV, K, V, chunk_size, _io_code(bf), _stream(dev)))
+    dh, dh0 = _state_buffers(B, T, HV, V, K, N, dev, split_size, cu_seqlens, output_dh0)
+    _check(lib().gdn_chunk_bwd_dh(_ptr(q), _ptr(dout), _ptr(g), _ptr(g_gamma), _ptr(gk), _ptr(gv),
+                                  float(scale), _ptr(dht), _ptr(dh), split_size or 0, _ptr(dh0),
+                                  _ptr(cu_seqlens), N, B, T, Hk, HV, K, V, chunk_size,
+                                  _io_code(torch.bfloat16), _stream(dev)))
     return dh, dh0
+
+
+def chunk_fwd_h(k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor] = None,
+                g_gamma: Optional[torch.Tensor] = None, gk: Optional[torch.Tensor] = None,
+                gv: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None,
+                cu_seqlens: Optional[torch.Tensor] = None, split_size: Optional[int] = 64,
+                output_final_state: bool = True, chunk_size: int = 64):
+    """Forward decay-only chunk-state scan (bf16 k / v).  Returns (h [S,HV,V,K]
+    fp32, the state at the start of every split, or None when ``split_size`` is
+    None; ht [N,HV,V,K] fp32 or None)."""
+    B, T, Hk, HV, K, V, N, dev = _state_scan_args(k, v, "k", "v", g, g_gamma, gk, gv, h0, "h0", cu_seqlens)
+    h, ht = _state_buffers(B, T, HV, V, K, N, dev, split_size, cu_seqlens, output_final_state)
+    _check(lib().gdn_chunk_fwd_h(_ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma), _ptr(gk), _ptr(gv),
+                                 _ptr(h0), _ptr(h), split_size or 0, _ptr(ht), _ptr(cu_seqlens), N,
+                                 B, T, Hk, HV, K, V, chunk_size, _io_code(torch.bfloat16), _stream(dev)))
+    return h, ht

@@ -1,18 +1,26 @@
-// Backward state-gradient scan, gfx950: "fla ops/common/chunk_h.py",
-// chunk_bwd_kernel_dh.  Per (sequence, v-head), over the chunks in reverse
-// order, with dh (K x V, fp32) the gradient with respect to the state at the
-// end of the current chunk:
+// The state scans of "fla ops/common/chunk_h.py", gfx950: the backward
+// state-gradient scan (chunk_bwd_kernel_dh) and, run forward over (k, v), the
+// decay-only state scan (chunk_fwd_kernel_h).  Both keep a K x V fp32
+// accumulator per (sequence, v-head, V tile) and apply one chunk per step:
 //
-//   start:        dh = dht (or 0)
-//   every chunk:  if its index is a multiple of split_size / 64, store dh;
-//                 dh <- decay * dh + scale * (Q o e^G)^T dO
-//   end:          dh0 = dh
+//   backward (chunks in reverse order; A = q, B = dO):
+//     start dh = dht (or 0); per chunk: if its index is a multiple of
+//     split_size / 64, store dh; dh <- decay o dh + scale (A o e^{G_t})^T B;
+//     end: dh0 = dh
+//   forward (chunks in order; A = k, B = v):
+//     start h = h0 (or 0); per chunk: if its index is a multiple of
+//     split_size / 64, store h; h <- decay o h + (A o e^{G_last - G_t})^T B;
+//     end: ht = h
 //
-// with G the chunk-local cumulative log-gate (scalar per token, the fixed
-// per-head gamma, or per key channel), decay = e^{G_last} (per channel for
-// the per-channel gate, applied to the key rows).  This is the state
-// gradient of the decay-only recurrence h_t = decay_t h_{t-1} + k_t v_t^T,
-// o_t = scale q_t^T h_t; the delta rule's erase term is not part of it.
+// with G the chunk-local cumulative log-gate: scalar per token (g), the
+// fixed per-head gamma, per key channel (gk: a factor of the A rows) or per
+// value channel (gv: a factor of the B columns; it may come with g or
+// gamma), and decay = e^{G_last} on the matching rows / columns.  The
+// backward one is the state gradient of the decay-only recurrence
+// h_t = decay_t h_{t-1} + k_t v_t^T, o_t = scale q_t^T h_t; the delta rule's
+// erase term is part of neither.  In the code below the buffers keep the
+// backward's names: dht = the initial state, dh = the stored states, dh0 =
+// the final state.
 //
 // gfx950 design.  Work-group = 256 threads per (sequence, v-head, BVT-column
 // V tile); wave w holds key rows DK/4 * w .. + DK/4 of dh in fp32 MFMA
@@ -25,7 +33,8 @@
 // the banks.  Each chunk's loads are issued two chunks ahead (two register
 // buffers).  The gated operand is split into a bf16 hi + lo pair
 // (dO * scale e^{G_t} for a scalar gate, q * scale e^{G_t,c} for the
-// per-channel gate); the other operand is the raw bf16 input, exact.
+// per-channel gate; forward: the e^{G_last - G_t} factors); the other
+// operand is the raw bf16 input, exact.
 
 #include "chunk_common.h"
 #include "gdn_device.h"
@@ -72,12 +81,13 @@ __device__ __forceinline__ void transpose8(const uint4 (&R)[8], uint4 (&O)[8]) {
   }
 }
 
-template <int DK, bool KDA>
+template <int DK, bool KDA, bool FWD>
 __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ g,
     const float* __restrict__ gamma, const float* __restrict__ gk, float scale,
     const float* __restrict__ dht, float* __restrict__ dh, int nts, float* __restrict__ dh0,
     const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV) {
+  static_assert(KDA, "the scalar gates take chunk_bwd_dh_gdn_kernel");
   constexpr int DV = DK;
   constexpr int RW = DK / 4;          // key rows per wave
   constexpr int RB = RW / 16;         // 16-row blocks per wave
@@ -182,19 +192,34 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
     }
   };
 
-  auto step = [&](int ic, uint4 (&raw)[8], float (&gv)[KDA ? BT : 1]) __attribute__((always_inline)) {
+  // chunk of scan position i (forward: in order, backward: in reverse)
+  auto chunk_at = [&](int i) { return FWD ? i : NC - 1 - i; };
+  auto step = [&](int ic, int i, uint4 (&raw)[8], float (&gv)[KDA ? BT : 1]) __attribute__((always_inline)) {
     const int nrow = eos - (bos + ic * BT) < BT ? eos - (bos + ic * BT) : BT;
 
     // ---- chunk-local cumulative gates
     if constexpr (KDA) {
       if (tid < DK) {
-        float G = 0.f;
+        if constexpr (FWD) {
+          float GL = 0.f;
 #pragma unroll
-        for (int t = 0; t < BT; ++t) {
-          G += t < nrow ? gv[t] : 0.f;
-          sG[t][tid] = scale * __expf(G);
+          for (int t = 0; t < BT; ++t) GL += t < nrow ? gv[t] : 0.f;
+          float G = 0.f;
+#pragma unroll
+          for (int t = 0; t < BT; ++t) {
+            G += t < nrow ? gv[t] : 0.f;
+            sG[t][tid] = __expf(GL - G);
+          }
+          sDec[tid] = __expf(GL);
+        } else {
+          float G = 0.f;
+#pragma unroll
+          for (int t = 0; t < BT; ++t) {
+            G += t < nrow ? gv[t] : 0.f;
+            sG[t][tid] = scale * __expf(G);
+          }
+          sDec[tid] = __expf(G);
         }
-        sDec[tid] = __expf(G);
       }
     } else {
       if (w == 0) {
@@ -271,7 +296,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
       __syncthreads();
     }
     // this buffer is free again: the chunk after next
-    if (ic >= 2) load(ic - 2, raw, gv);
+    if (i + 2 < NC) load(chunk_at(i + 2), raw, gv);
 
     // ---- snapshot, decay, accumulate
     if (dh && ic % nts == 0) store_state(dh + ((sbase + ic / nts) * HV + j) * (size_t)DV * DK);
@@ -309,25 +334,29 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
     }
     __syncthreads();
   };
-  if (NC > 0) load(NC - 1, rawA, gvA);
-  if (NC > 1) load(NC - 2, rawB, gvB);
-  for (int ic = NC - 1; ic >= 0; ic -= 2) {
-    step(ic, rawA, gvA);
-    if (ic >= 1) step(ic - 1, rawB, gvB);
+  if (NC > 0) load(chunk_at(0), rawA, gvA);
+  if (NC > 1) load(chunk_at(1), rawB, gvB);
+  for (int i = 0; i < NC; i += 2) {
+    step(chunk_at(i), i, rawA, gvA);
+    if (i + 1 < NC) step(chunk_at(i + 1), i + 1, rawB, gvB);
   }
   if (dh0) store_state(dh0 + hbase);
 }
 
-// Scalar gate (g or gamma): two barriers per chunk.  Staging phase: the first
-// DK / 64 waves transpose the q block rows (8 x 8 blocks, v_perm_b32), waves 2 and 3
-// gate dO -- thread (column c, 8-token unit u) reads its 8 values, scales
-// them by scale e^{G_t} and writes the hi and lo rows.  Product phase: the
-// MFMAs of this chunk, while wave 0 forms the next chunk's gate factors into
-// the other buffer and the loads of the chunk after next are issued.
-template <int DK>
+// Scalar gate (g or gamma) and / or the per-value-channel gate (gv): two
+// barriers per chunk.  Staging phase: the first DK / 64 waves transpose the
+// q (k) block rows (8 x 8 blocks, v_perm_b32), waves 2 and 3 gate dO (v) --
+// thread (column c, 8-token unit u) reads its 8 values, scales them by the
+// token's factor (and, with gv, by its column's factor: the 8 threads of a
+// column are adjacent lanes, so the column's chunk-local cumulative gate is
+// a sum over the thread's 8 tokens plus a prefix over the 8 lanes) and
+// writes the hi and lo rows.  Product phase: the MFMAs of this chunk, while
+// wave 0 forms the next chunk's token factors into the other buffer and the
+// loads of the chunk after next are issued.
+template <int DK, bool FWD, bool GV>
 __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ g,
-    const float* __restrict__ gamma, float scale,
+    const float* __restrict__ gamma, const float* __restrict__ gvp, float scale,
     const float* __restrict__ dht, float* __restrict__ dh, int nts, float* __restrict__ dh0,
     const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV) {
   constexpr int DV = DK;
@@ -340,7 +369,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t sAh[DK][TP];
   __shared__ __attribute__((aligned(16))) bf16_t sBh[BVT][TP];
   __shared__ __attribute__((aligned(16))) bf16_t sBl[BVT][TP];
-  __shared__ float sGam[2][BT + 1];   // scale e^{G_t}; e^{G_last} at [BT]; two chunks
+  __shared__ float sGam[2][BT + 1];   // token factors; e^{G_last} at [BT]; two chunks
+  __shared__ float sGvL[GV ? BVT : 1];  // gv: e^{Gv_last} of each column of the tile
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, gq = lane >> 4;
@@ -394,11 +424,14 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
   // dc + 16 cc, 8-token unit du); with DK = 64 wave 1 stages nothing
   const bool isq = tid < QB, isd = tid >= 128;
   const int dc = (tid - 128) / (BT / 8), du = (tid - 128) % (BT / 8);
-  // raw loads of a chunk (two buffers)
+  // raw loads of a chunk (two buffers); gv: the thread's 8 tokens of its columns (0 past the end)
+  constexpr int GVC = GV ? DCPT : 1, GVT = GV ? 8 : 1;
   uint4 rqA[QPT][8], rqB[QPT][8];
   bf16_t rdA[DCPT][8], rdB[DCPT][8];
+  float gwA[GVC][GVT], gwB[GVC][GVT];
   float gvA, gvB;
-  auto load = [&](int ic, uint4 (&rq)[QPT][8], bf16_t (&rd)[DCPT][8], float& gv) __attribute__((always_inline)) {
+  auto load = [&](int ic, uint4 (&rq)[QPT][8], bf16_t (&rd)[DCPT][8], float (&gw)[GVC][GVT], float& gv)
+      __attribute__((always_inline)) {
     const int c0 = bos + ic * BT;
     const int nrow = eos - c0 < BT ? eos - c0 : BT;
     if (isq) {
@@ -418,6 +451,10 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
         for (int r = 0; r < 8; ++r) {
           const int t = 8 * du + r, tc = t < nrow ? t : nrow - 1;
           rd[cc][r] = dout[((size_t)(c0 + tc) * HV + j) * DV + v0 + dc + 16 * cc];
+          if constexpr (GV) {
+            const float x = gvp[((size_t)(c0 + tc) * HV + j) * DV + v0 + dc + 16 * cc];
+            gw[cc][r] = t < nrow ? x : 0.f;
+          }
         }
     }
     if (w == 0) {
@@ -425,17 +462,26 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
       gv = g ? g[(size_t)(c0 + tc) * HV + j] : (gamma ? gamma[j] : 0.f);
     }
   };
-  // wave 0: gate factors of chunk ic into buffer b
+  // wave 0: token factors of chunk ic into buffer b (backward scale e^{G_t},
+  // forward e^{G_last - G_t}; 0 past the end)
   auto gates = [&](int ic, float gv, int b) __attribute__((always_inline)) {
     const int nrow = eos - (bos + ic * BT) < BT ? eos - (bos + ic * BT) : BT;
     const float gl = lane < nrow ? gv : 0.f;
     const float G = intra::wave_incl_scan(gl, lane);
-    sGam[b][lane] = lane < nrow ? scale * __expf(G) : 0.f;
-    if (lane == nrow - 1) sGam[b][BT] = __expf(G);
+    if constexpr (FWD) {
+      const float GL = __shfl(G, nrow - 1);
+      sGam[b][lane] = lane < nrow ? __expf(GL - G) : 0.f;
+      if (lane == 0) sGam[b][BT] = __expf(GL);
+    } else {
+      sGam[b][lane] = lane < nrow ? scale * __expf(G) : 0.f;
+      if (lane == nrow - 1) sGam[b][BT] = __expf(G);
+    }
   };
+  // chunk of scan position i (forward: in order, backward: in reverse)
+  auto chunk_at = [&](int i) { return FWD ? i : NC - 1 - i; };
 
-  auto step = [&](int ic, int b, uint4 (&rq)[QPT][8], bf16_t (&rd)[DCPT][8], float& gv,
-                  uint4 (&rqN)[QPT][8], bf16_t (&rdN)[DCPT][8], float& gvN) __attribute__((always_inline)) {
+  auto step = [&](int ic, int i, int b, uint4 (&rq)[QPT][8], bf16_t (&rd)[DCPT][8], float (&gw)[GVC][GVT],
+                  float& gv, float& gvN) __attribute__((always_inline)) {
     const int nrow = eos - (bos + ic * BT) < BT ? eos - (bos + ic * BT) : BT;
     // ---- staging
     if (isq) {
@@ -456,11 +502,34 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
 #pragma unroll
       for (int cc = 0; cc < DCPT; ++cc) {
         const int c = dc + 16 * cc;
+        // gv: the column's factors at the thread's 8 tokens
+        float fv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) fv[r] = 1.f;
+        if constexpr (GV) {
+          float P[8], run = 0.f;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            run += gw[cc][r];
+            P[r] = run;
+          }
+          // inclusive prefix of the 8 units' sums over the column's lanes (du = lane % 8)
+          float inc = run;
+#pragma unroll
+          for (int d = 1; d < 8; d <<= 1) {
+            const float y = __shfl_up(inc, d, 8);
+            if (du >= d) inc += y;
+          }
+          const float base = inc - run, GL = __shfl(inc, 7, 8);
+#pragma unroll
+          for (int r = 0; r < 8; ++r) fv[r] = FWD ? __expf(GL - (base + P[r])) : __expf(base + P[r]);
+          if (du == 0) sGvL[c] = __expf(GL);
+        }
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int p2 = 0; p2 < 4; ++p2) {
-          const float x0 = bf2f(rd[cc][2 * p2]) * sGam[b][t0 + 2 * p2];       // 0 past the chunk end
-          const float x1 = bf2f(rd[cc][2 * p2 + 1]) * sGam[b][t0 + 2 * p2 + 1];
+          const float x0 = bf2f(rd[cc][2 * p2]) * (sGam[b][t0 + 2 * p2] * fv[2 * p2]);   // 0 past the chunk end
+          const float x1 = bf2f(rd[cc][2 * p2 + 1]) * (sGam[b][t0 + 2 * p2 + 1] * fv[2 * p2 + 1]);
           const uint32_t h0 = f2bf(x0), h1 = f2bf(x1);
           hw[p2] = h0 | (h1 << 16);
           lw[p2] = (uint32_t)f2bf(x0 - bf2f((bf16_t)h0)) | ((uint32_t)f2bf(x1 - bf2f((bf16_t)h1)) << 16);
@@ -472,14 +541,16 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
     }
     __syncthreads();
     // ---- products; the next chunk's gate factors; the loads of the chunk after next
-    if (w == 0 && ic >= 1) gates(ic - 1, gvN, b ^ 1);
-    if (ic >= 2) load(ic - 2, rq, rd, gv);
+    if (w == 0 && i + 1 < NC) gates(chunk_at(i + 1), gvN, b ^ 1);
+    if (i + 2 < NC) load(chunk_at(i + 2), rq, rd, gw, gv);
     if (dh && ic % nts == 0) store_state(dh + ((sbase + ic / nts) * HV + j) * (size_t)DV * DK);
     const float dec = sGam[b][BT];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int cb = 0; cb < CBN; ++cb) {
+      const float decy = GV ? dec * sGvL[16 * cb + n] : dec;   // the lane's column 16 cb + n
 #pragma unroll
-      for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] *= dec;
+      for (int rb = 0; rb < RB; ++rb) acc[rb][cb] *= decy;
+    }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
@@ -496,28 +567,27 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
       }
     }
     __syncthreads();
-    (void)rqN; (void)rdN;
   };
 
-  if (NC > 0) load(NC - 1, rqA, rdA, gvA);
-  if (NC > 1) load(NC - 2, rqB, rdB, gvB);
+  if (NC > 0) load(chunk_at(0), rqA, rdA, gwA, gvA);
+  if (NC > 1) load(chunk_at(1), rqB, rdB, gwB, gvB);
   if (NC > 0) {
-    if (w == 0) gates(NC - 1, gvA, 0);
+    if (w == 0) gates(chunk_at(0), gvA, 0);
     __syncthreads();
   }
-  // chunk NC - 1 - 2i uses buffer A and gate slot 0, NC - 2 - 2i buffer B and slot 1
-  for (int ic = NC - 1; ic >= 0; ic -= 2) {
-    step(ic, 0, rqA, rdA, gvA, rqB, rdB, gvB);
-    if (ic >= 1) step(ic - 1, 1, rqB, rdB, gvB, rqA, rdA, gvA);
+  // scan position 2 m uses buffer A and gate slot 0, 2 m + 1 buffer B and slot 1
+  for (int i = 0; i < NC; i += 2) {
+    step(chunk_at(i), i, 0, rqA, rdA, gwA, gvA, gvB);
+    if (i + 1 < NC) step(chunk_at(i + 1), i + 1, 1, rqB, rdB, gwB, gvB, gvA);
   }
   if (dh0) store_state(dh0 + hbase);
 }
 
-template <int DK, bool KDA>
+template <int DK, bool KDA, bool FWD>
 hipError_t launch_k(const BwdDhArgs& a, hipStream_t s) {
   const long long blocks = ((long long)a.N * a.HV + 7) / 8 * 8 * (DK / BVT);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, KDA>), dim3((unsigned)blocks), dim3(256), 0, s,
+  hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, KDA, FWD>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.dout, a.g, a.g_gamma, a.gk, a.scale, a.dht, a.dh,
                      a.split_chunks, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV);
   return hipGetLastError();
@@ -525,19 +595,25 @@ hipError_t launch_k(const BwdDhArgs& a, hipStream_t s) {
 
 }  // namespace
 
-template <int DK>
+template <int DK, bool FWD, bool GV>
 hipError_t launch_gdn(const BwdDhArgs& a, hipStream_t s) {
   const long long blocks = ((long long)a.N * a.HV + 7) / 8 * 8 * (DK / BVT);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_bwd_dh_gdn_kernel<DK>), dim3((unsigned)blocks), dim3(256), 0, s,
-                     (const bf16_t*)a.q, (const bf16_t*)a.dout, a.g, a.g_gamma, a.scale, a.dht, a.dh,
+  hipLaunchKernelGGL((chunk_bwd_dh_gdn_kernel<DK, FWD, GV>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const bf16_t*)a.q, (const bf16_t*)a.dout, a.g, a.g_gamma, a.gv, a.scale, a.dht, a.dh,
                      a.split_chunks, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV);
   return hipGetLastError();
 }
 
+template <bool FWD>
+hipError_t launch_dir(const BwdDhArgs& a, hipStream_t s) {
+  if (a.gk) return a.K == 128 ? launch_k<128, true, FWD>(a, s) : launch_k<64, true, FWD>(a, s);
+  if (a.gv) return a.K == 128 ? launch_gdn<128, FWD, true>(a, s) : launch_gdn<64, FWD, true>(a, s);
+  return a.K == 128 ? launch_gdn<128, FWD, false>(a, s) : launch_gdn<64, FWD, false>(a, s);
+}
+
 hipError_t launch_bwd_dh(const BwdDhArgs& a, hipStream_t s) {
-  if (a.gk) return a.K == 128 ? launch_k<128, true>(a, s) : launch_k<64, true>(a, s);
-  return a.K == 128 ? launch_gdn<128>(a, s) : launch_gdn<64>(a, s);
+  return a.fwd ? launch_dir<true>(a, s) : launch_dir<false>(a, s);
 }
 
 }  // namespace gdn

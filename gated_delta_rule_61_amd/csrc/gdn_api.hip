@@ -408,21 +408,27 @@ int gdn_decode(const void* q, const void* k, const void* v, const void* a, const
   return ok();
 }
 
-int gdn_chunk_bwd_dh(const void* q, const void* dout, const float* g, const float* g_gamma,
-                     const float* gk, float scale, const float* dht, float* dh, int split_size,
-                     float* dh0, const int64_t* cu_seqlens, int num_seqs, int B, int T, int Hk, int HV,
-                     int K, int V, int chunk_size, int dtype, void* stream) {
+// checks and launch shared by the two state scans; a = A operand (q / k),
+// b = B operand (dout / v), init / snaps / fin = dht, dh, dh0 (h0, h, ht)
+static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, const float* g,
+                      const float* g_gamma, const float* gk, const float* gv, float scale,
+                      const float* init, float* snaps, int split_size, float* fin,
+                      const int64_t* cu_seqlens, int num_seqs, int B, int T, int Hk, int HV, int K, int V,
+                      int chunk_size, int dtype, void* stream) {
+  const char* an = fwd ? "k" : "q";
+  const char* bn = fwd ? "v" : "dout";
   if (B < 0 || T < 0 || Hk <= 0 || HV <= 0 || K <= 0 || V <= 0)
     return fail(GDN_ERR_INVALID_ARGUMENT, "sizes must be positive (B, T >= 0): B=%d T=%d Hk=%d HV=%d K=%d V=%d",
                 B, T, Hk, HV, K, V);
   if (HV % Hk != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "HV (%d) must be a multiple of Hk (%d)", HV, Hk);
-  if (dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_UNSUPPORTED, "the backward dh scan takes bf16 io only");
+  if (dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_UNSUPPORTED, "the state scans take bf16 io only");
   if (chunk_size != 64) return fail(GDN_ERR_UNSUPPORTED, "chunk_size must be 64 (got %d)", chunk_size);
   if (!((K == 64 && V == 64) || (K == 128 && V == 128)))
     return fail(GDN_ERR_UNSUPPORTED, "supported head dims are K = V in {64, 128} (got K=%d V=%d)", K, V);
   if ((g != nullptr) + (g_gamma != nullptr) + (gk != nullptr) > 1)
     return fail(GDN_ERR_INVALID_ARGUMENT, "pass at most one of g, g_gamma and gk");
-  if (dh && (split_size <= 0 || split_size % 64 != 0))
+  if (gk && gv) return fail(GDN_ERR_UNSUPPORTED, "gk together with gv is not supported");
+  if (snaps && (split_size <= 0 || split_size % 64 != 0))
     return fail(GDN_ERR_INVALID_ARGUMENT, "split_size must be a positive multiple of 64 (got %d)", split_size);
   if ((long long)B * T >= (1LL << 31) / 64)
     return fail(GDN_ERR_UNSUPPORTED, "B*T too large (got %lld tokens)", (long long)B * T);
@@ -432,21 +438,37 @@ int gdn_chunk_bwd_dh(const void* q, const void* dout, const float* g, const floa
     if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", num_seqs);
     N = num_seqs;
   }
-  if ((long long)B * T > 0 && (!q || !dout))
-    return fail(GDN_ERR_INVALID_ARGUMENT, "q and dout are required");
-  const void* ptrs[] = {q, dout, g, g_gamma, gk, dht, dh, dh0};
+  if ((long long)B * T > 0 && (!a_op || !b_op))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s and %s are required", an, bn);
+  const void* ptrs[] = {a_op, b_op, g, g_gamma, gk, gv, init, snaps, fin};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(GDN_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
-  if (N == 0 || (!dh && !dh0)) return ok();
+  if (N == 0 || (!snaps && !fin)) return ok();
   BwdDhArgs a;
-  a.q = q; a.dout = dout; a.g = g; a.g_gamma = g_gamma; a.gk = gk; a.scale = scale;
-  a.dht = dht; a.dh = dh; a.split_chunks = dh ? split_size / 64 : 1; a.dh0 = dh0;
+  a.q = a_op; a.dout = b_op; a.g = g; a.g_gamma = g_gamma; a.gk = gk; a.gv = gv; a.fwd = fwd;
+  a.scale = scale; a.dht = init; a.dh = snaps; a.split_chunks = snaps ? split_size / 64 : 1; a.dh0 = fin;
   a.cu_seqlens = cu_seqlens; a.N = N; a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
-  prof_begin(GDN_STAGE_BWD_DH, (hipStream_t)stream);
+  prof_begin(stage, (hipStream_t)stream);
   const hipError_t e = launch_bwd_dh(a, (hipStream_t)stream);
-  prof_end(GDN_STAGE_BWD_DH, (hipStream_t)stream);
+  prof_end(stage, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int gdn_chunk_bwd_dh(const void* q, const void* dout, const float* g, const float* g_gamma,
+                     const float* gk, const float* gv, float scale, const float* dht, float* dh,
+                     int split_size, float* dh0, const int64_t* cu_seqlens, int num_seqs, int B, int T,
+                     int Hk, int HV, int K, int V, int chunk_size, int dtype, void* stream) {
+  return state_scan(false, GDN_STAGE_BWD_DH, q, dout, g, g_gamma, gk, gv, scale, dht, dh, split_size, dh0,
+                    cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size, dtype, stream);
+}
+
+int gdn_chunk_fwd_h(const void* k, const void* v, const float* g, const float* g_gamma,
+                    const float* gk, const float* gv, const float* h0, float* h, int split_size,
+                    float* ht, const int64_t* cu_seqlens, int num_seqs, int B, int T, int Hk, int HV,
+                    int K, int V, int chunk_size, int dtype, void* stream) {
+  return state_scan(true, GDN_STAGE_FWD_H, k, v, g, g_gamma, gk, gv, 1.f, h0, h, split_size, ht,
+                    cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size, dtype, stream);
 }
 
 int gdn_state_to_pool(const float* ht, const int32_t* indices, void* pool_state, int N, int HV,

@@ -24,10 +24,14 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
-// backward state-gradient scan (bf16 io)
+// the state scans (bf16 io): backward state gradient (fwd = false; q, dout)
+// or the forward decay-only state scan (fwd = true; k in q, v in dout, h0 in
+// dht, the stored states in dh, ht in dh0)
 struct BwdDhArgs {
   const void *q, *dout;
   const float *g, *g_gamma, *gk;   // at most one
+  const float* gv;                 // [B*T, HV, V] or nullptr; not with gk
+  bool fwd;
   float scale;
   const float* dht;                // [N, HV, V, K] or nullptr
   float* dh;                       // [splits, HV, V, K] or nullptr

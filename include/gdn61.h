@@ -211,8 +211,10 @@ int gdn_decode(const void* q, const void* k, const void* v,
  *   start:       dh = dht (or zeros)
  *   each chunk:  if its index is a multiple of split_size / 64, store dh;
  *                dh <- decay * dh + scale * sum_t e^{G_t} do_t q_t^T
- *                (per-channel gate: the key column c of every term and of
- *                the decay carries e^{G_t,c} / e^{G_last,c} instead)
+ *                (per-key-channel gate gk: the key column c of every term
+ *                and of the decay carries e^{G_t,c} / e^{G_last,c} instead;
+ *                per-value-channel gate gv: the value row i carries in
+ *                addition e^{Gv_t,i} / e^{Gv_last,i})
  *   end:         dh0 = dh
  * G = chunk-local cumulative log-gate, decay = e^{G_last}.  This is the
  * state gradient of the decay-only recurrence h_t = decay_t h_{t-1} +
@@ -223,6 +225,8 @@ int gdn_decode(const void* q, const void* k, const void* v,
  *   dout         [B, T, HV, V]  bf16 gradient of the output
  *   g [B,T,HV] | g_gamma [HV] | gk [B,T,HV,K]   fp32 log-gates, at most
  *                one (none = no decay); as in gdn_chunk_fwd / kda_chunk_fwd
+ *   gv           [B, T, HV, V]  fp32 per-value-channel log-gates, or NULL;
+ *                may come with g or g_gamma, not with gk (GDN_ERR_UNSUPPORTED)
  *   dht          [N, HV, V, K]  fp32 gradient of the final state, or NULL
  *   dh           [S, HV, V, K]  fp32 out, or NULL: sequence n of length L_n
  *                owns ceil(L_n / split_size) entries after those of
@@ -236,10 +240,48 @@ int gdn_decode(const void* q, const void* k, const void* v,
  */
 int gdn_chunk_bwd_dh(const void* q, const void* dout,
                      const float* g, const float* g_gamma, const float* gk,
-                     float scale, const float* dht, float* dh, int split_size,
-                     float* dh0, const int64_t* cu_seqlens, int num_seqs,
-                     int B, int T, int Hk, int HV, int K, int V,
+                     const float* gv, float scale, const float* dht, float* dh,
+                     int split_size, float* dh0, const int64_t* cu_seqlens,
+                     int num_seqs, int B, int T, int Hk, int HV, int K, int V,
                      int chunk_size, int dtype, void* stream);
+
+/*
+ * Forward decay-only chunk-state scan ("fla ops/common/chunk_h.py",
+ * chunk_fwd_kernel_h, with the state-V-first layout), bf16 io.  Per sequence
+ * and v-head, over the chunks of 64 tokens in order, with h [V, K] the state
+ * at the start of the current chunk:
+ *   start:       h = h0 (or zeros)
+ *   each chunk:  if its index is a multiple of split_size / 64, store h;
+ *                h <- e^{G_last} h + sum_t e^{G_last - G_t} v_t k_t^T
+ *                (gk: key column c carries e^{G_last,c} and
+ *                e^{G_last,c - G_t,c}; gv: value row i carries in addition
+ *                e^{Gv_last,i} and e^{Gv_last,i - Gv_t,i})
+ *   end:         ht = h
+ * G = chunk-local cumulative log-gate.  Token by token this is
+ * S_t = diag(e^{gv_t}) S_{t-1} diag(e^{gk_t}) e^{g_t} + v_t k_t^T: the
+ * linear-attention state without the delta rule's erase term.
+ *
+ *   k            [B, T, Hk, K]  bf16 (key head of v-head j: j / (HV / Hk))
+ *   v            [B, T, HV, V]  bf16
+ *   g, g_gamma, gk, gv          as in gdn_chunk_bwd_dh
+ *   h0           [N, HV, V, K]  fp32 initial state, or NULL (zeros)
+ *   h            [S, HV, V, K]  fp32 out, or NULL: sequence n of length L_n
+ *                owns ceil(L_n / split_size) entries after those of
+ *                sequences 0..n-1 (entry s = the state at the start of chunk
+ *                s * split_size / 64)
+ *   split_size   a positive multiple of 64, read when h is not NULL
+ *   ht           [N, HV, V, K]  fp32 out (final state), or NULL
+ *   cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size  as in gdn_chunk_fwd
+ * Supported: dtype = GDN_DTYPE_BF16, K = V in {64, 128}, chunk_size = 64.
+ * Errors and pointer rules as in gdn_chunk_bwd_dh.  Allocates nothing;
+ * asynchronous on `stream`.
+ */
+int gdn_chunk_fwd_h(const void* k, const void* v,
+                    const float* g, const float* g_gamma, const float* gk,
+                    const float* gv, const float* h0, float* h, int split_size,
+                    float* ht, const int64_t* cu_seqlens, int num_seqs,
+                    int B, int T, int Hk, int HV, int K, int V,
+                    int chunk_size, int dtype, void* stream);
 
 /*
  * Prefill -> decode handoff: write final prefill states into a bf16 decode
@@ -282,7 +324,8 @@ enum {
   GDN_STAGE_DECODE = 3,        /* decode step                                  */
   GDN_STAGE_HANDOFF = 4,       /* prefill state -> decode pool (bf16)          */
   GDN_STAGE_BWD_DH = 5,        /* backward state-gradient scan                 */
-  GDN_STAGE_COUNT = 6
+  GDN_STAGE_FWD_H = 6,         /* forward decay-only state scan                */
+  GDN_STAGE_COUNT = 7
 };
 int gdn_profile_enable(int on);
 int gdn_profile_read(double* ms, int* counts);

@@ -143,20 +143,33 @@ def test_state_to_pool_empty_is_a_no_op(L):
     assert _pool(L, N=0, pool=0) == 0
 
 
-def _bwd(L, q=FAKE, do=FAKE, g=None, gg=None, gk=None, dht=None, dh=None, ss=64, dh0=FAKE, cu=None, ns=0,
-         B=1, T=64, Hk=1, HV=1, K=64, V=64, cs=64, dt=1):
-    return L.gdn_chunk_bwd_dh(q, do, g, gg, gk, 1.0, dht, dh, ss, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
+def _bwd(L, q=FAKE, do=FAKE, g=None, gg=None, gk=None, gv=None, dht=None, dh=None, ss=64, dh0=FAKE, cu=None,
+         ns=0, B=1, T=64, Hk=1, HV=1, K=64, V=64, cs=64, dt=1, fwd=False):
+    f = L.gdn_chunk_fwd_h if fwd else L.gdn_chunk_bwd_dh
+    if fwd:
+        return f(q, do, g, gg, gk, gv, dht, dh, ss, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
+    return f(q, do, g, gg, gk, gv, 1.0, dht, dh, ss, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
 
 
+@pytest.mark.parametrize("fwd", [False, True])
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(dt=0), 2, b"bf16 io only"),
     (dict(g=FAKE, gk=FAKE), 1, b"at most one"),
+    (dict(gk=FAKE, gv=FAKE), 2, b"gk together with gv"),
     (dict(dh=FAKE, ss=0), 1, b"split_size"),
     (dict(K=96, V=96), 2, b"head dims"),
     (dict(q=None), 1, b"required"),
     (dict(do=FAKE + 2), 1, b"aligned"),
+    (dict(gv=FAKE + 4), 1, b"aligned"),
     (dict(B=2, cu=FAKE, ns=2), 1, b"B == 1"),
 ])
-def test_bwd_dh_rejects(L, kw, status, msg):
-    assert _bwd(L, **kw) == status
+def test_state_scans_reject(L, kw, status, msg, fwd):
+    assert _bwd(L, fwd=fwd, **kw) == status
     assert msg in L.gdn_last_error()
+
+
+@pytest.mark.parametrize("fwd", [False, True])
+def test_state_scans_nothing_to_do(L, fwd):
+    # no sequences, or no output requested: returns before any HIP call
+    assert _bwd(L, fwd=fwd, B=0) == 0
+    assert _bwd(L, fwd=fwd, dh0=None) == 0

@@ -1,6 +1,7 @@
 """GPU parity of the backward state-gradient scan (gdn_chunk_bwd_dh, C ABI)
 against the fp64 oracle: dh every split_size tokens and dh0, for the scalar
-gate, the fixed per-head decay, the per-channel gate and no gate."""
+gate, the fixed per-head decay, the per-key-channel gate, the per-value-channel
+gate (alone and with a scalar gate) and no gate."""
 
 import numpy as np
 import pytest
@@ -21,25 +22,35 @@ def _case(inp, gate, S, dht_std=0.1, seed=0):
     do = torch.from_numpy(rng.standard_normal((B, T, HV, V)).astype(np.float32)).to(torch.bfloat16)
     N = inp.num_seqs
     dht = torch.from_numpy((rng.standard_normal((N, HV, V, K)) * dht_std).astype(np.float32))
-    g = inp.g if gate == "gdn" else None
-    gk = inp.gk if gate == "kda" else None
-    gamma = torch.from_numpy(-np.abs(rng.standard_normal(HV)).astype(np.float32) * 0.05) if gate == "gamma" else None
+    forms = (gate or "").split("+")
+    g = inp.g if "gdn" in forms else None
+    gk = inp.gk if "kda" in forms else None
+    gamma = torch.from_numpy(-np.abs(rng.standard_normal(HV)).astype(np.float32) * 0.05) if "gamma" in forms else None
+    gv = None
+    if "gv" in forms:   # per-value-channel log-gates, -softplus(N(0, 1)) * 0.05
+        gv = torch.from_numpy((-np.logaddexp(0, rng.standard_normal((B, T, HV, V))) * 0.05).astype(np.float32))
     print(f"bwd dh {inp.name} gate={gate} split={S} dims={inp.dims}", flush=True)
-    dh, dh0 = binding.chunk_bwd_dh(dv(inp.q), dv(do), g=dv(g), g_gamma=dv(gamma), gk=dv(gk),
+    dh, dh0 = binding.chunk_bwd_dh(dv(inp.q), dv(do), g=dv(g), g_gamma=dv(gamma), gk=dv(gk), gv=dv(gv),
                                    scale=inp.scale, dht=dv(dht), cu_seqlens=dv(inp.cu_seqlens), split_size=S)
     torch.cuda.synchronize()
-    dh_ref, dh0_ref = oracle.state_grad_scan(inp.q, do, inp.scale, g=g, g_gamma=gamma, gk=gk, dht=dht,
+    dh_ref, dh0_ref = oracle.state_grad_scan(inp.q, do, inp.scale, g=g, g_gamma=gamma, gk=gk, gv=gv, dht=dht,
                                              cu_seqlens=inp.cu_seqlens, split_size=S)
     assert dh.shape == dh_ref.shape
     print("  dh", check("dh", dh.cpu(), dh_ref, torch.bfloat16),
           " dh0", check("dh0", dh0.cpu(), dh0_ref, torch.bfloat16), flush=True)
 
 
-@pytest.mark.parametrize("gate", ["gdn", "gamma", None])
+@pytest.mark.parametrize("gate", ["gdn", "gamma", None, "gv", "gdn+gv", "gamma+gv"])
 def test_bwd_dh_scalar_gate_varlen(gate):
     inp = workloads.make_prefill(1, 330, 2, 4, 128, 128, dtype=torch.bfloat16, seed=60, h0=True,
                                  seqlens=[200, 1, 129], name="bwd_varlen")
     _case(inp, gate, 64, seed=61)
+
+
+@pytest.mark.parametrize("gate", ["gv", "gdn+gv"])
+def test_bwd_dh_gv_k64(gate):
+    inp = workloads.make_prefill(2, 150, 1, 2, 64, 64, dtype=torch.bfloat16, seed=67, name="bwd_gv_K64")
+    _case(inp, gate, 128, seed=68)
 
 
 def test_bwd_dh_kda():

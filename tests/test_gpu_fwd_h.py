@@ -1,0 +1,86 @@
+"""GPU parity of the forward decay-only state scan (gdn_chunk_fwd_h, C ABI)
+against the fp64 oracle: the state at the start of every split and the final
+state, for every gate form (scalar, fixed per-head, per key channel, per
+value channel, scalar with per value channel, none), ragged and empty
+sequences, GQA heads, an initial state, K = V = 64 and 128."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_61_amd import binding, workloads
+from tests.tolerance import check
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+dv = lambda t: None if t is None else t.to(DEV)
+
+
+def _gates(inp, gate, rng):
+    B, T, Hk, HV, K, V = inp.dims
+    forms = (gate or "").split("+")
+    g = inp.g if "gdn" in forms else None
+    gk = inp.gk if "kda" in forms else None
+    gamma = torch.from_numpy(-np.abs(rng.standard_normal(HV)).astype(np.float32) * 0.05) if "gamma" in forms else None
+    gv = None
+    if "gv" in forms:   # per-value-channel log-gates, -softplus(N(0, 1)) * 0.05
+        gv = torch.from_numpy((-np.logaddexp(0, rng.standard_normal((B, T, HV, V))) * 0.05).astype(np.float32))
+    return g, gamma, gk, gv
+
+
+def _case(inp, gate, S, seed=0):
+    rng = np.random.default_rng(seed)
+    g, gamma, gk, gv = _gates(inp, gate, rng)
+    print(f"fwd h {inp.name} gate={gate} split={S} dims={inp.dims} h0={inp.h0 is not None}", flush=True)
+    h, ht = binding.chunk_fwd_h(dv(inp.k), dv(inp.v), g=dv(g), g_gamma=dv(gamma), gk=dv(gk), gv=dv(gv),
+                                h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens), split_size=S)
+    torch.cuda.synchronize()
+    h_ref, ht_ref = oracle.state_scan(inp.k, inp.v, g=g, g_gamma=gamma, gk=gk, gv=gv, h0=inp.h0,
+                                      cu_seqlens=inp.cu_seqlens, split_size=S)
+    assert h.shape == h_ref.shape
+    print("  h", check("h", h.cpu(), h_ref, torch.bfloat16),
+          " ht", check("ht", ht.cpu(), ht_ref, torch.bfloat16), flush=True)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "gamma", None, "gv", "gdn+gv", "gamma+gv"])
+def test_fwd_h_varlen_gqa(gate):
+    inp = workloads.make_prefill(1, 331, 2, 4, 128, 128, dtype=torch.bfloat16, seed=70, h0=True,
+                                 seqlens=[200, 1, 0, 130], name="fwd_h_varlen")
+    _case(inp, gate, 64, seed=71)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "gv", "gdn+gv", "kda"])
+def test_fwd_h_k64(gate):
+    inp = workloads.make_prefill(2, 150, 1, 2, 64, 64, dtype=torch.bfloat16, seed=72,
+                                 gate="kda" if gate == "kda" else "gdn", name="fwd_h_K64")
+    _case(inp, gate, 128, seed=73)
+
+
+def test_fwd_h_kda_k128_varlen():
+    inp = workloads.make_prefill(1, 200, 2, 2, 128, 128, dtype=torch.bfloat16, seed=74, gate="kda", h0=True,
+                                 seqlens=[64, 136], name="fwd_h_kda_K128")
+    _case(inp, "kda", 64, seed=75)
+
+
+def test_fwd_h_final_state_only():
+    inp = workloads.make_prefill(2, 100, 2, 2, 128, 128, dtype=torch.bfloat16, seed=76, h0=True, name="fwd_h_ht")
+    h, ht = binding.chunk_fwd_h(dv(inp.k), dv(inp.v), g=dv(inp.g), h0=dv(inp.h0), split_size=None)
+    torch.cuda.synchronize()
+    assert h is None
+    _, ht_ref = oracle.state_scan(inp.k, inp.v, g=inp.g, h0=inp.h0)
+    check("ht", ht.cpu(), ht_ref, torch.bfloat16)
+
+
+def test_fwd_h_b4_t4096_sampled_heads():
+    """The shape bench.py times (B=4 T=4096 H=16 K=V=128, scalar gate, h at
+    every chunk, ht out): two sampled heads, every chunk of every sequence."""
+    inp = workloads.gdn_bf16_b4_t4096()
+    heads = [0, 13]
+    print(f"fwd h full size heads={heads}", flush=True)
+    h, ht = binding.chunk_fwd_h(dv(inp.k), dv(inp.v), g=dv(inp.g), split_size=64)
+    torch.cuda.synchronize()
+    # Hk = HV here: v-head h reads k head h
+    h_ref, ht_ref = oracle.state_scan(inp.k[:, :, heads], inp.v[:, :, heads], g=inp.g[:, :, heads], split_size=64)
+    check("h", h.cpu()[:, heads], h_ref, torch.bfloat16)
+    check("ht", ht.cpu()[:, heads], ht_ref, torch.bfloat16)
