@@ -72,7 +72,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=16384)
     p.add_argument("--skip-extra", action="store_true", help="prefill workload only")
-    p.add_argument("--only", choices=["prefill", "decode", "kda", "varlen", "handoff", "bwd_dh", "copy"],
+    p.add_argument("--only", choices=["prefill", "decode", "kda", "varlen", "handoff", "bwd_dh", "fwd_h", "copy"],
                    default=None,
                    help="run one workload (for profiling) and print its figures")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache prefill timing")
@@ -277,6 +277,32 @@ def bench_bwd_dh(args, binding, workloads, torch):
     def step():
         binding.chunk_bwd_dh(q, do, g=g, scale=inp.scale, dht=dht, split_size=64)
 
+    nchunks = B * ((T + 63) // 64)
+    nbytes = (B * T * Hk * K * 2 + B * T * HV * V * 2 + B * T * HV * 4
+              + nchunks * HV * V * K * 4 + 2 * B * HV * V * K * 4)
+    return _bench_state_scan(args, binding, torch, step, "bwd_dh", nbytes,
+                             f"gdn_chunk_bwd_dh B={B} T={T} H={HV} K=V={K} bf16, dh every 64 tokens, dht in, dh0 out")
+
+
+def bench_fwd_h(args, binding, workloads, torch):
+    """Forward decay-only state scan on the headline shape (B=4 T=4096 H=16
+    K=V=128, bf16 k / v, scalar gate), h at every chunk, ht out."""
+    inp = workloads.gdn_bf16_b4_t4096()
+    dev = "cuda:0"
+    B, T, Hk, HV, K, V = inp.dims
+    k, v, g = inp.k.to(dev), inp.v.to(dev), inp.g.to(dev)
+
+    def step():
+        binding.chunk_fwd_h(k, v, g=g, split_size=64)
+
+    nchunks = B * ((T + 63) // 64)
+    nbytes = (B * T * Hk * K * 2 + B * T * HV * V * 2 + B * T * HV * 4
+              + nchunks * HV * V * K * 4 + B * HV * V * K * 4)
+    return _bench_state_scan(args, binding, torch, step, "fwd_h", nbytes,
+                             f"gdn_chunk_fwd_h B={B} T={T} H={HV} K=V={K} bf16, h every 64 tokens, ht out")
+
+
+def _bench_state_scan(args, binding, torch, step, stage, nbytes, desc):
     ms, _ = timed(step, max(args.steps // 2, 1), 1)
     binding.profile_read()
     binding.profile_enable(True)
@@ -285,15 +311,12 @@ def bench_bwd_dh(args, binding, workloads, torch):
     torch.cuda.synchronize()
     prof = binding.profile_read()
     binding.profile_enable(False)
-    kms = prof["bwd_dh"][0] / max(prof["bwd_dh"][1], 1)
-    nchunks = B * ((T + 63) // 64)
-    nbytes = (B * T * Hk * K * 2 + B * T * HV * V * 2 + B * T * HV * 4
-              + nchunks * HV * V * K * 4 + 2 * B * HV * V * K * 4)
-    return {"workload": f"gdn_chunk_bwd_dh B={B} T={T} H={HV} K=V={K} bf16, dh every 64 tokens, dht in, dh0 out",
+    kms = prof[stage][0] / max(prof[stage][1], 1)
+    return {"workload": desc,
             "ms_per_call": round(ms, 5), "kernel_ms": round(kms, 5),
             "GBps": round(nbytes / (kms * 1e-3) / 1e9, 1),
             "hbm_frac": round(nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": nbytes, "measured_bytes": measured_traffic("bwd_dh")}
+            "algorithmic_bytes": nbytes, "measured_bytes": measured_traffic(stage)}
 
 
 def bench_handoff(args, binding, workloads, torch):
@@ -393,6 +416,9 @@ def main():
     if args.only == "bwd_dh":
         print(json.dumps({"bwd_dh": bench_bwd_dh(args, binding, workloads, torch)}), flush=True)
         return
+    if args.only == "fwd_h":
+        print(json.dumps({"fwd_h": bench_fwd_h(args, binding, workloads, torch)}), flush=True)
+        return
     if args.only == "handoff":
         print(json.dumps({"handoff": bench_handoff(args, binding, workloads, torch)}), flush=True)
         return
@@ -458,6 +484,7 @@ def main():
         out["handoff"] = bench_handoff(args, binding, workloads, torch)
         out["snapshots"] = bench_snapshots(args, binding, workloads, torch, ms)
         out["bwd_dh"] = bench_bwd_dh(args, binding, workloads, torch)
+        out["fwd_h"] = bench_fwd_h(args, binding, workloads, torch)
         try:
             out["kda"] = bench_kda(args, binding, workloads, torch)
         except Exception as e:  # KDA path reports its own status

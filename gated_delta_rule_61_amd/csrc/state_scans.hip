@@ -55,6 +55,8 @@ constexpr int TP = BT + 8;     // padded token row of the transposed tiles (bf16
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+__device__ const float kNoGate[1] = {0.f};   // the log-gate of "no gate"
+
 __device__ __forceinline__ f32x4 mma_bf(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -82,12 +84,12 @@ __device__ __forceinline__ void transpose8(const uint4 (&R)[8], uint4 (&O)[8]) {
 }
 
 template <int DK, bool KDA, bool FWD>
-__global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
+__global__ __launch_bounds__(256) void state_scan_gk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ g,
     const float* __restrict__ gamma, const float* __restrict__ gk, float scale,
     const float* __restrict__ dht, float* __restrict__ dh, int nts, float* __restrict__ dh0,
     const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV) {
-  static_assert(KDA, "the scalar gates take chunk_bwd_dh_gdn_kernel");
+  static_assert(KDA, "the scalar gates take state_scan_kernel");
   constexpr int DV = DK;
   constexpr int RW = DK / 4;          // key rows per wave
   constexpr int RB = RW / 16;         // 16-row blocks per wave
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
 // wave 0 forms the next chunk's token factors into the other buffer and the
 // loads of the chunk after next are issued.
 template <int DK, bool FWD, bool GV>
-__global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
+__global__ __launch_bounds__(256) void state_scan_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ g,
     const float* __restrict__ gamma, const float* __restrict__ gvp, float scale,
     const float* __restrict__ dht, float* __restrict__ dh, int nts, float* __restrict__ dh0,
@@ -364,8 +366,9 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
   constexpr int RB = RW / 16;
   constexpr int QB = BT / 8 * DK / 8;    // q blocks: one per thread of the first QB / 64 waves
   constexpr int QPT = 1;
-  constexpr int DCPT = BVT * BT / 8 / 128;   // dO units per thread of waves 2, 3
-  static_assert(QB % 64 == 0 && QB <= 128 && DCPT * 128 == BVT * BT / 8, "thread roles");
+  // threads 128 .. 128 + ND - 1: one 8-token unit of two adjacent dO columns each
+  constexpr int ND = BVT * BT / 16;
+  static_assert(QB % 64 == 0 && QB <= 128 && ND % 64 == 0 && ND <= 128, "thread roles");
   __shared__ __attribute__((aligned(16))) bf16_t sAh[DK][TP];
   __shared__ __attribute__((aligned(16))) bf16_t sBh[BVT][TP];
   __shared__ __attribute__((aligned(16))) bf16_t sBl[BVT][TP];
@@ -421,16 +424,18 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
   };
 
   // roles: the first QB / 64 waves -> q blocks; waves 2, 3 -> dO (columns
-  // dc + 16 cc, 8-token unit du); with DK = 64 wave 1 stages nothing
-  const bool isq = tid < QB, isd = tid >= 128;
-  const int dc = (tid - 128) / (BT / 8), du = (tid - 128) % (BT / 8);
-  // raw loads of a chunk (two buffers); gv: the thread's 8 tokens of its columns (0 past the end)
-  constexpr int GVC = GV ? DCPT : 1, GVT = GV ? 8 : 1;
+  // 2 dp and 2 dp + 1, 8-token unit du: one 32-bit word per token, so the
+  // loads land in whole registers and stay in flight); with DK = 64 wave 1
+  // stages nothing
+  const bool isq = tid < QB, isd = tid >= 128 && tid < 128 + ND;
+  const int dp = (tid - 128) / (BT / 8), du = (tid - 128) % (BT / 8);
+  // raw loads of a chunk (two buffers); gv: the thread's 8 tokens of its two columns (0 past the end)
+  constexpr int GVT = GV ? 8 : 1;
   uint4 rqA[QPT][8], rqB[QPT][8];
-  bf16_t rdA[DCPT][8], rdB[DCPT][8];
-  float gwA[GVC][GVT], gwB[GVC][GVT];
+  uint32_t rdA[8], rdB[8];
+  float gwA[2][GVT], gwB[2][GVT];
   float gvA, gvB;
-  auto load = [&](int ic, uint4 (&rq)[QPT][8], bf16_t (&rd)[DCPT][8], float (&gw)[GVC][GVT], float& gv)
+  auto load = [&](int ic, uint4 (&rq)[QPT][8], uint32_t (&rd)[8], float (&gw)[2][GVT], float& gv)
       __attribute__((always_inline)) {
     const int c0 = bos + ic * BT;
     const int nrow = eos - c0 < BT ? eos - c0 : BT;
@@ -446,20 +451,24 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
       }
     } else if (isd) {
 #pragma unroll
-      for (int cc = 0; cc < DCPT; ++cc)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int t = 8 * du + r, tc = t < nrow ? t : nrow - 1;
-          rd[cc][r] = dout[((size_t)(c0 + tc) * HV + j) * DV + v0 + dc + 16 * cc];
-          if constexpr (GV) {
-            const float x = gvp[((size_t)(c0 + tc) * HV + j) * DV + v0 + dc + 16 * cc];
-            gw[cc][r] = t < nrow ? x : 0.f;
-          }
+      for (int r = 0; r < 8; ++r) {
+        const int t = 8 * du + r, tc = t < nrow ? t : nrow - 1;
+        const size_t off = ((size_t)(c0 + tc) * HV + j) * DV + v0 + 2 * dp;
+        rd[r] = *reinterpret_cast<const uint32_t*>(dout + off);
+        if constexpr (GV) {
+          const float2 x = *reinterpret_cast<const float2*>(gvp + off);
+          gw[0][r] = t < nrow ? x.x : 0.f;
+          gw[1][r] = t < nrow ? x.y : 0.f;
         }
+      }
     }
     if (w == 0) {
+      // one vector load from whichever source applies (a zero for no gate):
+      // a branch between a vector and a scalar load would make the compiler
+      // wait for every load in flight where the two meet
       const int tc = lane < nrow ? lane : nrow - 1;
-      gv = g ? g[(size_t)(c0 + tc) * HV + j] : (gamma ? gamma[j] : 0.f);
+      const float* gp = g ? g + (size_t)(c0 + tc) * HV + j : (gamma ? gamma + j : kNoGate);
+      gv = *gp;
     }
   };
   // wave 0: token factors of chunk ic into buffer b (backward scale e^{G_t},
@@ -480,7 +489,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
   // chunk of scan position i (forward: in order, backward: in reverse)
   auto chunk_at = [&](int i) { return FWD ? i : NC - 1 - i; };
 
-  auto step = [&](int ic, int i, int b, uint4 (&rq)[QPT][8], bf16_t (&rd)[DCPT][8], float (&gw)[GVC][GVT],
+  auto step = [&](int ic, int i, int b, uint4 (&rq)[QPT][8], uint32_t (&rd)[8], float (&gw)[2][GVT],
                   float& gv, float& gvN) __attribute__((always_inline)) {
     const int nrow = eos - (bos + ic * BT) < BT ? eos - (bos + ic * BT) : BT;
     // ---- staging
@@ -500,8 +509,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
     } else if (isd) {
       const int t0 = 8 * du;
 #pragma unroll
-      for (int cc = 0; cc < DCPT; ++cc) {
-        const int c = dc + 16 * cc;
+      for (int cc = 0; cc < 2; ++cc) {
+        const int c = 2 * dp + cc;
         // gv: the column's factors at the thread's 8 tokens
         float fv[8];
 #pragma unroll
@@ -528,8 +537,12 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_gdn_kernel(
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int p2 = 0; p2 < 4; ++p2) {
-          const float x0 = bf2f(rd[cc][2 * p2]) * (sGam[b][t0 + 2 * p2] * fv[2 * p2]);   // 0 past the chunk end
-          const float x1 = bf2f(rd[cc][2 * p2 + 1]) * (sGam[b][t0 + 2 * p2 + 1] * fv[2 * p2 + 1]);
+          // column cc of tokens t0 + 2 p2 (+ 1): the low / high half of the word
+          const uint32_t w0 = rd[2 * p2], w1 = rd[2 * p2 + 1];
+          const float d0 = __builtin_bit_cast(float, cc ? (w0 & 0xFFFF0000u) : (w0 << 16));
+          const float d1 = __builtin_bit_cast(float, cc ? (w1 & 0xFFFF0000u) : (w1 << 16));
+          const float x0 = d0 * (sGam[b][t0 + 2 * p2] * fv[2 * p2]);   // 0 past the chunk end
+          const float x1 = d1 * (sGam[b][t0 + 2 * p2 + 1] * fv[2 * p2 + 1]);
           const uint32_t h0 = f2bf(x0), h1 = f2bf(x1);
           hw[p2] = h0 | (h1 << 16);
           lw[p2] = (uint32_t)f2bf(x0 - bf2f((bf16_t)h0)) | ((uint32_t)f2bf(x1 - bf2f((bf16_t)h1)) << 16);
@@ -587,7 +600,7 @@ template <int DK, bool KDA, bool FWD>
 hipError_t launch_k(const BwdDhArgs& a, hipStream_t s) {
   const long long blocks = ((long long)a.N * a.HV + 7) / 8 * 8 * (DK / BVT);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_bwd_dh_kernel<DK, KDA, FWD>), dim3((unsigned)blocks), dim3(256), 0, s,
+  hipLaunchKernelGGL((state_scan_gk_kernel<DK, KDA, FWD>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.dout, a.g, a.g_gamma, a.gk, a.scale, a.dht, a.dh,
                      a.split_chunks, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV);
   return hipGetLastError();
@@ -599,7 +612,7 @@ template <int DK, bool FWD, bool GV>
 hipError_t launch_gdn(const BwdDhArgs& a, hipStream_t s) {
   const long long blocks = ((long long)a.N * a.HV + 7) / 8 * 8 * (DK / BVT);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_bwd_dh_gdn_kernel<DK, FWD, GV>), dim3((unsigned)blocks), dim3(256), 0, s,
+  hipLaunchKernelGGL((state_scan_kernel<DK, FWD, GV>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.dout, a.g, a.g_gamma, a.gv, a.scale, a.dht, a.dh,
                      a.split_chunks, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV);
   return hipGetLastError();
