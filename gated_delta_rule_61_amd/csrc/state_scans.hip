@@ -55,7 +55,9 @@ constexpr int TP = BT + 8;     // padded token row of the transposed tiles (bf16
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ const float kNoGate[1] = {0.f};   // the log-gate of "no gate"
+// the log-gate of "no gate" (not const: a const array would sit in the constant
+// address space, and a pointer that may point to either would load through flat)
+__device__ float kNoGate[1] = {0.f};
 
 __device__ __forceinline__ f32x4 mma_bf(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
