@@ -393,8 +393,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         float* hp = hs + ((sbase + c / nts) * HV + j) * (size_t)V * DK;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-          *reinterpret_cast<float4*>(hp + (size_t)(v0 + 16 * cb + n) * DK + perm_row(kb, 4 * g)) =
-              make_float4(St[kb][0], St[kb][1], St[kb][2], St[kb][3]);
+          store_nt16(hp + (size_t)(v0 + 16 * cb + n) * DK + perm_row(kb, 4 * g), St[kb]);
       }
       const char* sAi = S1 ? sAi1 : sAi0;
       const char* sV = S1 ? sV1 : sV0;
@@ -533,8 +532,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     if (ht) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        *reinterpret_cast<float4*>(ht + hbase + (size_t)(v0 + 16 * cb + n) * DK + perm_row(kb, 4 * g)) =
-            make_float4(St[kb][0], St[kb][1], St[kb][2], St[kb][3]);
+        store_nt16(ht + hbase + (size_t)(v0 + 16 * cb + n) * DK + perm_row(kb, 4 * g), St[kb]);
     }
   } else if (role == 1) {
     // =================== helper wave: the output of 16 columns
@@ -708,8 +706,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       const int qq = mv * 64 + lane;
       const int row = qq / (BV / 8), u = qq % (BV / 8);
       if (row < nr)
-        *reinterpret_cast<uint4*>(o + ((size_t)(c0 + row) * HV + j) * V + v0 + 8 * u) =
-            *reinterpret_cast<const uint4*>(sO + row * L::OROW + 16 * u);
+        store_nt16(o + ((size_t)(c0 + row) * HV + j) * V + v0 + 8 * u,
+                   *reinterpret_cast<const uint4*>(sO + row * L::OROW + 16 * u));
     };
 
     if (NC > 0) {

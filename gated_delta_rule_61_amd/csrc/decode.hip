@@ -164,7 +164,7 @@ __global__ __launch_bounds__(TPB) void gdn_decode_kernel(
       w.y = pack_bf2(out[2], out[3]);
       w.z = pack_bf2(out[4], out[5]);
       w.w = pack_bf2(out[6], out[7]);
-      *reinterpret_cast<uint4*>(o + (tok * HV + hv) * DV + 8 * rg) = w;
+      store_nt16(o + (tok * HV + hv) * DV + 8 * rg, w);
     }
   }
 
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(TPB) void gdn_decode_kernel(
     w.y = pack_bf2(S[i][2], S[i][3]);
     w.z = pack_bf2(S[i][4], S[i][5]);
     w.w = pack_bf2(S[i][6], S[i][7]);
-    *reinterpret_cast<uint4*>(sp + (size_t)i * DK) = w;
+    store_nt16(sp + (size_t)i * DK, w);
   }
 }
 
@@ -467,8 +467,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(4))) v
     for (int i = 0; i < 4; ++i) {
       const int rl = 4 * i + (lane >> 4);   // row within the block
       const int u = lane & 15;
-      *reinterpret_cast<uint4*>(sp + (size_t)(row0 + 16 * rb + rl) * DK + 8 * u) =
-          sb[(16 * lw + rl) * 16 + (u ^ rl)];
+      store_nt16(sp + (size_t)(row0 + 16 * rb + rl) * DK + 8 * u, sb[(16 * lw + rl) * 16 + (u ^ rl)]);
     }
     if (g == 1) {
 #pragma unroll

@@ -27,6 +27,17 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t bf16_t;  // raw bf16 bits in memory
 
 // ---------------------------------------------------------------- bf16 bits
+// A 16-byte store marked nontemporal (streaming): for results that this
+// kernel writes once and does not read back.  On gfx950 such stores were
+// seen to complete much sooner under heavy write traffic, and every
+// vmcnt wait of the storing wave covers its stores as well as its loads.
+template <typename V>
+__device__ __forceinline__ void store_nt16(void* p, const V& v) {
+  static_assert(sizeof(V) == 16, "16-byte stores");
+  typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, v), reinterpret_cast<u32x4_nt*>(p));
+}
+
 __device__ __forceinline__ float bf2f(bf16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
 }

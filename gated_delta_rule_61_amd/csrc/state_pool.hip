@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void state_to_pool_kernel(
       w.y = pack_bf2(a[i].z, a[i].w);
       w.z = pack_bf2(b[i].x, b[i].y);
       w.w = pack_bf2(b[i].z, b[i].w);
-      *reinterpret_cast<uint4*>(dst + e0) = w;
+      store_nt16(dst + e0, w);
     }
   }
 }

@@ -155,8 +155,7 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < CBN; ++cb)
-        *reinterpret_cast<float4*>(dst + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq) =
-            make_float4(acc[rb][cb][0], acc[rb][cb][1], acc[rb][cb][2], acc[rb][cb][3]);
+        store_nt16(dst + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq, acc[rb][cb]);
   };
 
   // this thread's 8 x 8 block: q (waves 0 .. NQB / 64 - 1) or dO (the next
@@ -421,8 +420,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < CBN; ++cb)
-        *reinterpret_cast<float4*>(dst + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq) =
-            make_float4(acc[rb][cb][0], acc[rb][cb][1], acc[rb][cb][2], acc[rb][cb][3]);
+        store_nt16(dst + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq, acc[rb][cb]);
   };
 
   // roles: the first QB / 64 waves -> q blocks; waves 2, 3 -> dO (columns
