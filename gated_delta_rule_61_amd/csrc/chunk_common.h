@@ -85,7 +85,7 @@ __device__ __forceinline__ void store_tile(const float (*sA)[AP], T* __restrict_
         w.y = pack2<T>(s[2], s[3]);
         w.z = pack2<T>(s[4], s[5]);
         w.w = pack2<T>(s[6], s[7]);
-        *reinterpret_cast<uint4*>(p) = w;
+        store_nt16(p, w);   // streaming: the scan reads these rows once, from memory anyway
       } else {
         const float* s = &sA[r][sg * 4];
         *reinterpret_cast<float4*>(p) = make_float4(s[0], s[1], s[2], s[3]);
