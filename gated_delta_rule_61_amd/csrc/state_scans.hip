@@ -85,13 +85,14 @@ __device__ __forceinline__ void transpose8(const uint4 (&R)[8], uint4 (&O)[8]) {
   }
 }
 
-template <int DK, bool KDA, bool FWD>
+// Per-key-channel gate (gk): the gated operand is the A side (q / k), one
+// thread per key channel forms the chunk-local cumulative gates in LDS, the
+// value side transposes raw; three barriers per chunk.
+template <int DK, bool FWD>
 __global__ __launch_bounds__(256) void state_scan_gk_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ g,
-    const float* __restrict__ gamma, const float* __restrict__ gk, float scale,
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ gk, float scale,
     const float* __restrict__ dht, float* __restrict__ dh, int nts, float* __restrict__ dh0,
     const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV) {
-  static_assert(KDA, "the scalar gates take state_scan_kernel");
   constexpr int DV = DK;
   constexpr int RW = DK / 4;          // key rows per wave
   constexpr int RB = RW / 16;         // 16-row blocks per wave
@@ -99,13 +100,10 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
   static_assert(NQB + BT / 8 * BVT / 8 <= 256, "one block per thread");
   // transposed tiles: row = key channel / value column, 8-token units XOR-swizzled by row / 8
   __shared__ __attribute__((aligned(16))) bf16_t sAh[DK][TP];   // A operand (q side), hi
-  __shared__ __attribute__((aligned(16))) bf16_t sAl[KDA ? DK : 1][TP];   //   lo
-  __shared__ __attribute__((aligned(16))) bf16_t sBh[BVT][TP];  // B operand (dO side), hi
-  __shared__ __attribute__((aligned(16))) bf16_t sBl[KDA ? 1 : BVT][TP];  //   lo
-  __shared__ __attribute__((aligned(16))) bf16_t sBr[KDA ? 1 : BVT][TP];  // GDN: raw dO, transposed
-  __shared__ float sG[KDA ? BT : 1][KDA ? DK + 4 : 1];          // KDA: scale e^{G_t,c}
-  __shared__ float sGam[BT + 1];    // GDN: scale e^{G_t}, and e^{G_last} at [BT]
-  __shared__ float sDec[KDA ? DK : 1];  // KDA: e^{G_last, c}
+  __shared__ __attribute__((aligned(16))) bf16_t sAl[DK][TP];   //   lo
+  __shared__ __attribute__((aligned(16))) bf16_t sBh[BVT][TP];  // B operand (dO side), raw
+  __shared__ float sG[BT][DK + 4];   // token x channel factors (backward scale e^{G_t,c}, forward e^{G_last,c - G_t,c})
+  __shared__ float sDec[DK];         // e^{G_last,c}
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, gq = lane >> 4;
@@ -169,8 +167,8 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
   // raw loads of a chunk: the block's 8 rows, and the gate values; two
   // buffers, so that the loads of chunk ic - 2 fly during chunks ic and ic - 1
   uint4 rawA[8], rawB[8];
-  float gvA[KDA ? BT : 1], gvB[KDA ? BT : 1];
-  auto load = [&](int ic, uint4 (&raw)[8], float (&gv)[KDA ? BT : 1]) __attribute__((always_inline)) {
+  float gvA[BT], gvB[BT];
+  auto load = [&](int ic, uint4 (&raw)[8], float (&gv)[BT]) __attribute__((always_inline)) {
     const int c0 = bos + ic * BT;
     const int nrow = eos - c0 < BT ? eos - c0 : BT;
 #pragma unroll
@@ -179,67 +177,50 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
       if (isq) raw[r] = *reinterpret_cast<const uint4*>(q + ((size_t)(c0 + tc) * Hk + jk) * DK + 8 * cb8);
       else if (isd) raw[r] = *reinterpret_cast<const uint4*>(dout + ((size_t)(c0 + tc) * HV + j) * DV + v0 + 8 * cb8);
     }
-    if constexpr (KDA) {
-      if (tid < DK) {
+    if (tid < DK) {
 #pragma unroll
-        for (int t = 0; t < BT; ++t) {
-          const int tc = t < nrow ? t : nrow - 1;
-          gv[t] = gk[((size_t)(c0 + tc) * HV + j) * DK + tid];
-        }
-      }
-    } else {
-      if (w == 0) {
-        const int tc = lane < nrow ? lane : nrow - 1;
-        gv[0] = g ? g[(size_t)(c0 + tc) * HV + j] : (gamma ? gamma[j] : 0.f);
+      for (int t = 0; t < BT; ++t) {
+        const int tc = t < nrow ? t : nrow - 1;
+        gv[t] = gk[((size_t)(c0 + tc) * HV + j) * DK + tid];
       }
     }
   };
 
   // chunk of scan position i (forward: in order, backward: in reverse)
   auto chunk_at = [&](int i) { return FWD ? i : NC - 1 - i; };
-  auto step = [&](int ic, int i, uint4 (&raw)[8], float (&gv)[KDA ? BT : 1]) __attribute__((always_inline)) {
+  auto step = [&](int ic, int i, uint4 (&raw)[8], float (&gv)[BT]) __attribute__((always_inline)) {
     const int nrow = eos - (bos + ic * BT) < BT ? eos - (bos + ic * BT) : BT;
 
-    // ---- chunk-local cumulative gates
-    if constexpr (KDA) {
-      if (tid < DK) {
-        if constexpr (FWD) {
-          float GL = 0.f;
+    // ---- chunk-local cumulative gates, one thread per key channel
+    if (tid < DK) {
+      if constexpr (FWD) {
+        float GL = 0.f;
 #pragma unroll
-          for (int t = 0; t < BT; ++t) GL += t < nrow ? gv[t] : 0.f;
-          float G = 0.f;
+        for (int t = 0; t < BT; ++t) GL += t < nrow ? gv[t] : 0.f;
+        float G = 0.f;
 #pragma unroll
-          for (int t = 0; t < BT; ++t) {
-            G += t < nrow ? gv[t] : 0.f;
-            sG[t][tid] = __expf(GL - G);
-          }
-          sDec[tid] = __expf(GL);
-        } else {
-          float G = 0.f;
-#pragma unroll
-          for (int t = 0; t < BT; ++t) {
-            G += t < nrow ? gv[t] : 0.f;
-            sG[t][tid] = scale * __expf(G);
-          }
-          sDec[tid] = __expf(G);
+        for (int t = 0; t < BT; ++t) {
+          G += t < nrow ? gv[t] : 0.f;
+          sG[t][tid] = __expf(GL - G);
         }
-      }
-    } else {
-      if (w == 0) {
-        const float gl = lane < nrow ? gv[0] : 0.f;
-        const float G = intra::wave_incl_scan(gl, lane);
-        sGam[lane] = lane < nrow ? scale * __expf(G) : 0.f;
-        if (lane == nrow - 1) sGam[BT] = __expf(G);
+        sDec[tid] = __expf(GL);
+      } else {
+        float G = 0.f;
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+          G += t < nrow ? gv[t] : 0.f;
+          sG[t][tid] = scale * __expf(G);
+        }
+        sDec[tid] = __expf(G);
       }
     }
     __syncthreads();
 
     // ---- the block transposed into its tile: row = channel (column) 8 cb8 + e,
     // 8-token unit tb at position tb ^ (cb8 & 7); tokens past the chunk end are 0.
-    // The gated operand (KDA: q, GDN: dO) goes in as a bf16 hi + lo pair.
+    // The gated operand (q / k) goes in as a bf16 hi + lo pair, dO / v raw.
     const int col = 8 * (tb ^ (cb8 & 7));
-    const bool gated = KDA && isq;   // GDN gates dO in a second pass below
-    if ((isq || isd) && !gated) {
+    if (isd) {
 #pragma unroll
       for (int r = 0; r < 8; ++r)
         if (8 * tb + r >= nrow) raw[r] = make_uint4(0u, 0u, 0u, 0u);
@@ -247,8 +228,7 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
       transpose8(raw, O);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bf16_t* dst = isq ? &sAh[8 * cb8 + e][col] : (KDA ? &sBh[8 * cb8 + e][col] : &sBr[8 * cb8 + e][col]);
-        *reinterpret_cast<uint4*>(dst) = O[e];
+        *reinterpret_cast<uint4*>(&sBh[8 * cb8 + e][col]) = O[e];
       }
     } else if (isq) {
 #pragma unroll
@@ -261,43 +241,19 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int t = 8 * tb + 2 * p2 + h;
-            // KDA: q * scale e^{G_t,c} (0 past the end); GDN: dO * scale e^{G_t} (0 past the end)
-            const float f = KDA ? (t < nrow ? sG[t][c] : 0.f) : sGam[t];
+            // q * scale e^{G_t,c} (forward: k * e^{G_last,c - G_t,c}); 0 past the end
+            const float f = t < nrow ? sG[t][c] : 0.f;
             x[h] = bf2f((bf16_t)elem16(raw[2 * p2 + h], e)) * f;
           }
           const uint32_t h0 = f2bf(x[0]), h1 = f2bf(x[1]);
           hw[p2] = h0 | (h1 << 16);
           lw[p2] = (uint32_t)f2bf(x[0] - bf2f((bf16_t)h0)) | ((uint32_t)f2bf(x[1] - bf2f((bf16_t)h1)) << 16);
         }
-        bf16_t* dh_ = KDA ? &sAh[c][col] : &sBh[c][col];
-        bf16_t* dl_ = KDA ? &sAl[c][col] : &sBl[c][col];
-        *reinterpret_cast<uint4*>(dh_) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(dl_) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        *reinterpret_cast<uint4*>(&sAh[c][col]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&sAl[c][col]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
     }
     __syncthreads();
-    if constexpr (!KDA) {
-      // dO * scale e^{G_t} as a bf16 hi + lo pair: one 8-token row piece per
-      // thread (unit u of row c holds tokens 8 (u ^ (c / 8 & 7)) .. + 7)
-      if (tid < BVT * BT / 8) {
-        const int c = tid / (BT / 8), u = tid % (BT / 8);
-        const int t0 = 8 * (u ^ ((c >> 3) & 7));
-        const uint4 r = *reinterpret_cast<const uint4*>(&sBr[c][8 * u]);
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int p2 = 0; p2 < 4; ++p2) {
-          const uint32_t wv = word(r, p2);
-          const float x0 = __builtin_bit_cast(float, wv << 16) * sGam[t0 + 2 * p2];
-          const float x1 = __builtin_bit_cast(float, wv & 0xFFFF0000u) * sGam[t0 + 2 * p2 + 1];
-          const uint32_t h0 = f2bf(x0), h1 = f2bf(x1);
-          hw[p2] = h0 | (h1 << 16);
-          lw[p2] = (uint32_t)f2bf(x0 - bf2f((bf16_t)h0)) | ((uint32_t)f2bf(x1 - bf2f((bf16_t)h1)) << 16);
-        }
-        *reinterpret_cast<uint4*>(&sBh[c][8 * u]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(&sBl[c][8 * u]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      }
-      __syncthreads();
-    }
     // this buffer is free again: the chunk after next
     if (i + 2 < NC) load(chunk_at(i + 2), raw, gv);
 
@@ -307,7 +263,7 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
     for (int rb = 0; rb < RB; ++rb) {
       f32x4 dec;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dec[i] = KDA ? sDec[RW * w + 16 * rb + 4 * gq + i] : sGam[BT];
+      for (int e = 0; e < 4; ++e) dec[e] = sDec[RW * w + 16 * rb + 4 * gq + e];
 #pragma unroll
       for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] *= dec;
     }
@@ -318,20 +274,14 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
         const int ra = RW * w + 16 * rb + n;
         const int ca = 8 * ((4 * s + gq) ^ ((ra >> 3) & 7));
         const u32x4 ah = *reinterpret_cast<const u32x4*>(&sAh[ra][ca]);
-        u32x4 al;
-        if constexpr (KDA) al = *reinterpret_cast<const u32x4*>(&sAl[ra][ca]);
+        const u32x4 al = *reinterpret_cast<const u32x4*>(&sAl[ra][ca]);
 #pragma unroll
         for (int cb = 0; cb < CBN; ++cb) {
           const int rbv = 16 * cb + n;
           const int cbv = 8 * ((4 * s + gq) ^ ((rbv >> 3) & 7));
           const u32x4 bh = *reinterpret_cast<const u32x4*>(&sBh[rbv][cbv]);
           acc[rb][cb] = mma_bf(ah, bh, acc[rb][cb]);
-          if constexpr (KDA) {
-            acc[rb][cb] = mma_bf(al, bh, acc[rb][cb]);
-          } else {
-            const u32x4 bl = *reinterpret_cast<const u32x4*>(&sBl[rbv][cbv]);
-            acc[rb][cb] = mma_bf(ah, bl, acc[rb][cb]);
-          }
+          acc[rb][cb] = mma_bf(al, bh, acc[rb][cb]);
         }
       }
     }
@@ -596,12 +546,12 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
   if (dh0) store_state(dh0 + hbase);
 }
 
-template <int DK, bool KDA, bool FWD>
+template <int DK, bool FWD>
 hipError_t launch_k(const BwdDhArgs& a, hipStream_t s) {
   const long long blocks = ((long long)a.N * a.HV + 7) / 8 * 8 * (DK / BVT);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((state_scan_gk_kernel<DK, KDA, FWD>), dim3((unsigned)blocks), dim3(256), 0, s,
-                     (const bf16_t*)a.q, (const bf16_t*)a.dout, a.g, a.g_gamma, a.gk, a.scale, a.dht, a.dh,
+  hipLaunchKernelGGL((state_scan_gk_kernel<DK, FWD>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const bf16_t*)a.q, (const bf16_t*)a.dout, a.gk, a.scale, a.dht, a.dh,
                      a.split_chunks, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV);
   return hipGetLastError();
 }
@@ -620,7 +570,7 @@ hipError_t launch_gdn(const BwdDhArgs& a, hipStream_t s) {
 
 template <bool FWD>
 hipError_t launch_dir(const BwdDhArgs& a, hipStream_t s) {
-  if (a.gk) return a.K == 128 ? launch_k<128, true, FWD>(a, s) : launch_k<64, true, FWD>(a, s);
+  if (a.gk) return a.K == 128 ? launch_k<128, FWD>(a, s) : launch_k<64, FWD>(a, s);
   if (a.gv) return a.K == 128 ? launch_gdn<128, FWD, true>(a, s) : launch_gdn<64, FWD, true>(a, s);
   return a.K == 128 ? launch_gdn<128, FWD, false>(a, s) : launch_gdn<64, FWD, false>(a, s);
 }
