@@ -82,3 +82,11 @@ def test_bwd_dh_b4_t4096_sampled_heads():
                                              g=inp.g[:, :, heads], dht=dht[:, heads], split_size=64)
     check("dh", dh.cpu()[:, heads], dh_ref, torch.bfloat16)
     check("dh0", dh0.cpu()[:, heads], dh0_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("gate", ["gamma+gv", "kda"])
+def test_bwd_dh_split_of_three_chunks(gate):
+    """split_size = 192 (a stored gradient every third chunk), odd lengths, GQA."""
+    inp = workloads.make_prefill(1, 455, 1, 2, 64, 64, dtype=torch.bfloat16, seed=79, h0=True,
+                                 gate="kda" if gate == "kda" else "gdn", seqlens=[390, 0, 65], name="bwd_split192")
+    _case(inp, gate, 192, seed=80)

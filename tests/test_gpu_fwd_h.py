@@ -84,3 +84,11 @@ def test_fwd_h_b4_t4096_sampled_heads():
     h_ref, ht_ref = oracle.state_scan(inp.k[:, :, heads], inp.v[:, :, heads], g=inp.g[:, :, heads], split_size=64)
     check("h", h.cpu()[:, heads], h_ref, torch.bfloat16)
     check("ht", ht.cpu()[:, heads], ht_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("gate", ["gamma+gv", "kda"])
+def test_fwd_h_split_of_three_chunks(gate):
+    """split_size = 192 (a stored state every third chunk), odd lengths, GQA."""
+    inp = workloads.make_prefill(1, 455, 1, 2, 64, 64, dtype=torch.bfloat16, seed=77, h0=True,
+                                 gate="kda" if gate == "kda" else "gdn", seqlens=[390, 0, 65], name="fwd_h_split192")
+    _case(inp, gate, 192, seed=78)
