@@ -253,7 +253,7 @@ def bench_snapshots(args, binding, workloads, torch, base_ms):
 
         def step():
             binding.gdn_chunk_fwd(q, k, v, g, beta, scale=inp.scale, out=o, workspace=ws,
-                                  split_size=S, h_snap=hs)
+                                  split_size=S, h_snap=hs, states_in_fp32=True)
 
         ms, _ = timed(step, max(args.steps // 2, 1), 1)
         res[f"split{S}"] = {"ms_per_call": round(ms, 5), "overhead_vs_no_snapshots": round(ms / base_ms - 1, 4),
@@ -275,7 +275,7 @@ def bench_bwd_dh(args, binding, workloads, torch):
     dht = torch.randn((B, HV, V, K), generator=gen, device=dev) * 0.1
 
     def step():
-        binding.chunk_bwd_dh(q, do, g=g, scale=inp.scale, dht=dht, split_size=64)
+        binding.chunk_bwd_dh(q, do, g=g, scale=inp.scale, dht=dht, split_size=64, states_in_fp32=True)
 
     nchunks = B * ((T + 63) // 64)
     nbytes = (B * T * Hk * K * 2 + B * T * HV * V * 2 + B * T * HV * 4
@@ -293,7 +293,7 @@ def bench_fwd_h(args, binding, workloads, torch):
     k, v, g = inp.k.to(dev), inp.v.to(dev), inp.g.to(dev)
 
     def step():
-        binding.chunk_fwd_h(k, v, g=g, split_size=64)
+        binding.chunk_fwd_h(k, v, g=g, split_size=64, states_in_fp32=True)
 
     nchunks = B * ((T + 63) // 64)
     nbytes = (B * T * Hk * K * 2 + B * T * HV * V * 2 + B * T * HV * 4

@@ -26,6 +26,7 @@ _c_void_p = ctypes.c_void_p
 _c_int = ctypes.c_int
 _c_float = ctypes.c_float
 _c_size_t = ctypes.c_size_t
+_c_ll = ctypes.c_longlong
 
 _SIGNATURES = {
     "gdn_status_string": (ctypes.c_char_p, [_c_int]),
@@ -34,11 +35,11 @@ _SIGNATURES = {
     "gdn_chunk_fwd_workspace_bytes": (_c_size_t, [_c_int] * 8),
     "kda_chunk_fwd_workspace_bytes": (_c_size_t, [_c_int] * 8),
     "gdn_chunk_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float,
-                               _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_int,
+                               _c_void_p, _c_void_p, _c_void_p, _c_int, _c_ll, _c_int, _c_void_p, _c_int,
                                _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "kda_chunk_fwd": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float,
-                               _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_int,
+                               _c_void_p, _c_void_p, _c_void_p, _c_int, _c_ll, _c_int, _c_void_p, _c_int,
                                _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "gdn_profile_enable": (_c_int, [_c_int]),
@@ -47,12 +48,13 @@ _SIGNATURES = {
                             _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_float, _c_float, _c_float, _c_int, _c_float, _c_void_p]),
-    "gdn_chunk_bwd_dh": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                                  _c_float, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
+    "gdn_chunk_bwd_dh": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                  _c_float, _c_void_p, _c_void_p, _c_int, _c_ll, _c_int, _c_void_p,
+                                  _c_void_p, _c_int,
                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                   _c_void_p]),
-    "gdn_chunk_fwd_h": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                                 _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
+    "gdn_chunk_fwd_h": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                 _c_void_p, _c_void_p, _c_int, _c_ll, _c_int, _c_void_p, _c_void_p, _c_int,
                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_void_p]),
     "gdn_state_to_pool": (_c_int, [_c_void_p, _c_void_p, _c_void_p,
@@ -164,27 +166,50 @@ def _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, gate, gate_shape_ta
     return B, T, Hk, HV, K, V, N, dev, io
 
 
-def snapshot_count(B: int, T: int, split_size: int, cu_seqlens: Optional[torch.Tensor] = None) -> int:
-    """Number of state snapshots of a call: sum over sequences of
-    ceil(length / split_size).  With ``cu_seqlens`` this reads the (device)
-    boundaries back to the host."""
-    if cu_seqlens is None:
+def snapshot_count(B: int, T: int, split_size: int, cu_seqlens_host=None) -> int:
+    """Number of stored states of a call: sum over sequences of
+    ceil(length / split_size).  Varlen batches need the boundaries on the
+    HOST (a list or a CPU tensor): nothing here reads device memory, so no
+    call synchronises the host."""
+    if cu_seqlens_host is None:
         return B * ((T + split_size - 1) // split_size)
-    cu = cu_seqlens.cpu().clamp(0, T)
-    lens = (cu[1:] - cu[:-1]).clamp(min=0)
-    return int(((lens + split_size - 1) // split_size).sum())
+    if isinstance(cu_seqlens_host, torch.Tensor):
+        if cu_seqlens_host.device.type != "cpu":
+            raise ValueError("snapshot_count needs the boundaries in host memory (a list or CPU tensor)")
+        cu_seqlens_host = cu_seqlens_host.tolist()
+    cu = [min(max(int(c), 0), T) for c in cu_seqlens_host]
+    return sum((max(b - a, 0) + split_size - 1) // split_size for a, b in zip(cu[:-1], cu[1:]))
 
 
-def _snapshots(B, T, HV, V, K, N, dev, split_size, h_snap, cu_seqlens):
+def _state_dtype(io: torch.dtype, states_in_fp32: bool) -> torch.dtype:
+    """Stored states in the input dtype unless ``states_in_fp32``."""
+    return torch.float32 if states_in_fp32 else io
+
+
+def _states(B, T, HV, V, K, N, dev, split_size, buf, name, varlen, cu_seqlens_cpu, dtype):
+    """The stored-state buffer of a call: the caller's (any capacity; the
+    library writes no entry past it) or a new one.  A varlen call allocates
+    only with the host copy of its boundaries."""
     if split_size is None:
+        if buf is not None:
+            raise ValueError(f"{name} given without split_size")
         return None
     if split_size <= 0 or split_size % 64:
         raise ValueError("split_size must be a positive multiple of 64")
-    if h_snap is None:
-        h_snap = torch.empty((snapshot_count(B, T, split_size, cu_seqlens), HV, V, K),
-                             dtype=torch.float32, device=dev)
-    _need(h_snap, "h_snap", torch.float32, (h_snap.shape[0], HV, V, K), dev)
-    return h_snap
+    if buf is None:
+        if varlen and cu_seqlens_cpu is None:
+            raise ValueError(f"a varlen call with split_size needs a preallocated {name} or cu_seqlens_cpu "
+                             f"(the host copy of cu_seqlens); at most ceil(T / split_size) + N entries are used")
+        n = snapshot_count(B, T, split_size, cu_seqlens_cpu if varlen else None)
+        buf = torch.empty((n, HV, V, K), dtype=dtype, device=dev)
+    if buf.dim() != 4:
+        raise ValueError(f"{name} must be [S, HV, V, K]")
+    _need(buf, name, dtype, (buf.shape[0], HV, V, K), dev)
+    return buf
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    return GDN_DTYPE_BF16 if dt == torch.bfloat16 else GDN_DTYPE_F32
 
 
 def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
@@ -193,18 +218,22 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
                   cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   split_size: Optional[int] = None, h_snap: Optional[torch.Tensor] = None,
-                  g_gamma: Optional[torch.Tensor] = None):
+                  g_gamma: Optional[torch.Tensor] = None, states_in_fp32: bool = False,
+                  cu_seqlens_cpu=None):
     """GDN chunked prefill.  Returns (o [B,T,HV,V], ht [N,HV,V,K] fp32 or None),
-    and the state snapshots [S,HV,V,K] fp32 as a third element when
-    ``split_size`` is given (``h_snap`` may be passed preallocated).
-    ``g_gamma`` [HV] (fp32) is a fixed per-head log-decay at every token, in
-    place of ``g``."""
+    and the state snapshots [S,HV,V,K] as a third element when
+    ``split_size`` is given: in the io dtype, or fp32 with
+    ``states_in_fp32``.  ``h_snap`` may be passed preallocated (with
+    ``cu_seqlens``, either it or ``cu_seqlens_cpu``, the host copy of the
+    boundaries, is required).  ``g_gamma`` [HV] (fp32) is a fixed per-head
+    log-decay at every token, in place of ``g``."""
     B, T, Hk, HV, K, V, N, dev, io = _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, g, (), "g")
     if g_gamma is not None:
         if g is not None:
             raise ValueError("pass g or g_gamma, not both")
         _need(g_gamma, "g_gamma", torch.float32, (HV,), dev)
-    hs = _snapshots(B, T, HV, V, K, N, dev, split_size, h_snap, cu_seqlens)
+    sdt = _state_dtype(io, states_in_fp32)
+    hs = _states(B, T, HV, V, K, N, dev, split_size, h_snap, "h_snap", cu_seqlens is not None, cu_seqlens_cpu, sdt)
     if scale is None:
         scale = K ** -0.5
     o = torch.empty((B, T, HV, V), dtype=io, device=dev) if out is None else out
@@ -214,7 +243,8 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _check(lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma), _ptr(beta), float(scale),
-                               _ptr(h0), _ptr(ht), _ptr(hs), split_size or 0, _ptr(cu_seqlens), N,
+                               _ptr(h0), _ptr(ht), _ptr(hs), split_size or 0,
+                               0 if hs is None else hs.shape[0], _dtype_code(sdt), _ptr(cu_seqlens), N,
                                B, T, Hk, HV, K, V, chunk_size, _io_code(io),
                                _ptr(o), _ptr(workspace), workspace.numel(), _stream(dev)))
     return (o, ht) if hs is None else (o, ht, hs)
@@ -225,15 +255,18 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.T
                   h0: Optional[torch.Tensor] = None, output_final_state: bool = True,
                   cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
                   return_intra: bool = True, workspace: Optional[torch.Tensor] = None,
-                  split_size: Optional[int] = None, h_snap: Optional[torch.Tensor] = None):
+                  split_size: Optional[int] = None, h_snap: Optional[torch.Tensor] = None,
+                  states_in_fp32: bool = False, cu_seqlens_cpu=None):
     """KDA chunked prefill.  Returns (o, ht, Aqk, Akk_inv); the last two are
     [B,T,HV,64] in the io dtype (None when ``return_intra`` is False).  With
-    ``split_size`` the state snapshots follow as a fifth element."""
+    ``split_size`` the state snapshots follow as a fifth element (dtype and
+    buffer rules as in ``gdn_chunk_fwd``)."""
     if gk is None:
         raise ValueError("gk is required")
     B, T, Hk, HV, K, V, N, dev, io = _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, gk,
                                                    (q.shape[-1],), "gk")
-    hs = _snapshots(B, T, HV, V, K, N, dev, split_size, h_snap, cu_seqlens)
+    sdt = _state_dtype(io, states_in_fp32)
+    hs = _states(B, T, HV, V, K, N, dev, split_size, h_snap, "h_snap", cu_seqlens is not None, cu_seqlens_cpu, sdt)
     if scale is None:
         scale = K ** -0.5
     o = torch.empty((B, T, HV, V), dtype=io, device=dev)
@@ -246,7 +279,8 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.T
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _check(lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(gk), _ptr(beta), float(scale),
-                               _ptr(h0), _ptr(ht), _ptr(hs), split_size or 0, _ptr(cu_seqlens), N,
+                               _ptr(h0), _ptr(ht), _ptr(hs), split_size or 0,
+                               0 if hs is None else hs.shape[0], _dtype_code(sdt), _ptr(cu_seqlens), N,
                                B, T, Hk, HV, K, V, chunk_size, _io_code(io),
                                _ptr(o), _ptr(Aqk), _ptr(Akk), _ptr(workspace), workspace.numel(),
                                _stream(dev)))
@@ -322,42 +356,51 @@ def _state_scan_args(a, b, an, bn, g, g_gamma, gk, gv, init, init_name, cu_seqle
     bf = torch.bfloat16
     _need(a, an, bf, None, dev)
     _need(b, bn, bf, (B, T, HV, V), dev)
-    _need(g, "g", torch.float32, (B, T, HV), dev)
-    _need(g_gamma, "g_gamma", torch.float32, (HV,), dev)
-    _need(gk, "gk", torch.float32, (B, T, HV, K), dev)
-    _need(gv, "gv", torch.float32, (B, T, HV, V), dev)
+    # gate heads: taken from whichever gate is given (all must agree)
+    heads = {t.shape[2] for t in (g, gk, gv) if t is not None and t.dim() >= 3}
+    if g_gamma is not None:
+        heads.add(g_gamma.shape[0])
+    if len(heads) > 1:
+        raise ValueError(f"the gates disagree on their head count: {sorted(heads)}")
+    Hg = heads.pop() if heads else HV
+    if Hg <= 0 or HV % Hg:
+        raise ValueError(f"HV ({HV}) must be a multiple of the gate heads ({Hg})")
+    _need(g, "g", torch.float32, (B, T, Hg), dev)
+    _need(g_gamma, "g_gamma", torch.float32, (Hg,), dev)
+    _need(gk, "gk", torch.float32, (B, T, Hg, K), dev)
+    _need(gv, "gv", torch.float32, (B, T, Hg, V), dev)
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int64, None, dev)
         N = cu_seqlens.numel() - 1
     else:
         N = B
     _need(init, init_name, torch.float32, (N, HV, V, K), dev)
-    return B, T, Hk, HV, K, V, N, dev
-
-
-def _state_buffers(B, T, HV, V, K, N, dev, split_size, cu_seqlens, final):
-    snaps = None
-    if split_size is not None:
-        snaps = torch.empty((snapshot_count(B, T, split_size, cu_seqlens), HV, V, K),
-                            dtype=torch.float32, device=dev)
-    fin = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if final else None
-    return snaps, fin
+    return B, T, Hk, HV, K, V, N, dev, Hg
 
 
 def chunk_bwd_dh(q: torch.Tensor, dout: torch.Tensor, g: Optional[torch.Tensor] = None,
                  g_gamma: Optional[torch.Tensor] = None, gk: Optional[torch.Tensor] = None,
                  scale: Optional[float] = None, dht: Optional[torch.Tensor] = None,
                  cu_seqlens: Optional[torch.Tensor] = None, split_size: Optional[int] = 64,
-                 output_dh0: bool = True, chunk_size: int = 64, gv: Optional[torch.Tensor] = None):
+                 output_dh0: bool = True, chunk_size: int = 64, gv: Optional[torch.Tensor] = None,
+                 states_in_fp32: bool = False, dh: Optional[torch.Tensor] = None,
+                 cu_seqlens_cpu=None):
     """Backward state-gradient scan (bf16 q / dout).  Returns (dh [S,HV,V,K]
-    fp32 or None when ``split_size`` is None, dh0 [N,HV,V,K] fp32 or None)."""
-    B, T, Hk, HV, K, V, N, dev = _state_scan_args(q, dout, "q", "dout", g, g_gamma, gk, gv, dht, "dht",
-                                                  cu_seqlens)
+    -- bf16, or fp32 with ``states_in_fp32``; None when ``split_size`` is
+    None -- and dh0 [N,HV,V,K] fp32 or None).  The gates may have fewer heads
+    than dout (Hg, a divisor of HV: v-head j takes gate head j / (HV / Hg)).
+    ``dh`` may be passed preallocated (any capacity; entries past it are not
+    written); a varlen call without it needs ``cu_seqlens_cpu``."""
+    B, T, Hk, HV, K, V, N, dev, Hg = _state_scan_args(q, dout, "q", "dout", g, g_gamma, gk, gv, dht, "dht",
+                                                      cu_seqlens)
     if scale is None:
         scale = K ** -0.5
-    dh, dh0 = _state_buffers(B, T, HV, V, K, N, dev, split_size, cu_seqlens, output_dh0)
-    _check(lib().gdn_chunk_bwd_dh(_ptr(q), _ptr(dout), _ptr(g), _ptr(g_gamma), _ptr(gk), _ptr(gv),
-                                  float(scale), _ptr(dht), _ptr(dh), split_size or 0, _ptr(dh0),
+    sdt = _state_dtype(torch.bfloat16, states_in_fp32)
+    dh = _states(B, T, HV, V, K, N, dev, split_size, dh, "dh", cu_seqlens is not None, cu_seqlens_cpu, sdt)
+    dh0 = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if output_dh0 else None
+    _check(lib().gdn_chunk_bwd_dh(_ptr(q), _ptr(dout), _ptr(g), _ptr(g_gamma), _ptr(gk), _ptr(gv), Hg,
+                                  float(scale), _ptr(dht), _ptr(dh), split_size or 0,
+                                  0 if dh is None else dh.shape[0], _dtype_code(sdt), _ptr(dh0),
                                   _ptr(cu_seqlens), N, B, T, Hk, HV, K, V, chunk_size,
                                   _io_code(torch.bfloat16), _stream(dev)))
     return dh, dh0
@@ -367,13 +410,18 @@ def chunk_fwd_h(k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor] = No
                 g_gamma: Optional[torch.Tensor] = None, gk: Optional[torch.Tensor] = None,
                 gv: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None,
                 cu_seqlens: Optional[torch.Tensor] = None, split_size: Optional[int] = 64,
-                output_final_state: bool = True, chunk_size: int = 64):
-    """Forward decay-only chunk-state scan (bf16 k / v).  Returns (h [S,HV,V,K]
-    fp32, the state at the start of every split, or None when ``split_size`` is
-    None; ht [N,HV,V,K] fp32 or None)."""
-    B, T, Hk, HV, K, V, N, dev = _state_scan_args(k, v, "k", "v", g, g_gamma, gk, gv, h0, "h0", cu_seqlens)
-    h, ht = _state_buffers(B, T, HV, V, K, N, dev, split_size, cu_seqlens, output_final_state)
-    _check(lib().gdn_chunk_fwd_h(_ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma), _ptr(gk), _ptr(gv),
-                                 _ptr(h0), _ptr(h), split_size or 0, _ptr(ht), _ptr(cu_seqlens), N,
+                output_final_state: bool = True, chunk_size: int = 64, states_in_fp32: bool = False,
+                h: Optional[torch.Tensor] = None, cu_seqlens_cpu=None):
+    """Forward decay-only chunk-state scan (bf16 k / v).  Returns (h
+    [S,HV,V,K], the state at the start of every split -- bf16, or fp32 with
+    ``states_in_fp32``; None when ``split_size`` is None -- and ht [N,HV,V,K]
+    fp32 or None).  Gate heads and the ``h`` buffer as in ``chunk_bwd_dh``."""
+    B, T, Hk, HV, K, V, N, dev, Hg = _state_scan_args(k, v, "k", "v", g, g_gamma, gk, gv, h0, "h0", cu_seqlens)
+    sdt = _state_dtype(torch.bfloat16, states_in_fp32)
+    h = _states(B, T, HV, V, K, N, dev, split_size, h, "h", cu_seqlens is not None, cu_seqlens_cpu, sdt)
+    ht = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if output_final_state else None
+    _check(lib().gdn_chunk_fwd_h(_ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma), _ptr(gk), _ptr(gv), Hg,
+                                 _ptr(h0), _ptr(h), split_size or 0, 0 if h is None else h.shape[0],
+                                 _dtype_code(sdt), _ptr(ht), _ptr(cu_seqlens), N,
                                  B, T, Hk, HV, K, V, chunk_size, _io_code(torch.bfloat16), _stream(dev)))
     return h, ht

@@ -233,10 +233,11 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     const typename C::OPT* __restrict__ top, int op_rows, int op_head_div,
     const typename C::IOT* __restrict__ v, const float* __restrict__ GF,
     const float* __restrict__ DG, float scale, const float* __restrict__ h0,
-    float* __restrict__ ht, float* __restrict__ hs, int nts, const typename C::P* __restrict__ Ainv,
+    float* __restrict__ ht, void* __restrict__ hs, int nts, int sbf16, long long scap,
+    const typename C::P* __restrict__ Ainv,
     const typename C::P* __restrict__ Aqk, typename C::IOT* __restrict__ o,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ coff,
-    const int32_t* __restrict__ order, int Tlen, int ttot, int NT, int N, int HV, int V) {
+    const int32_t* __restrict__ order, int Tlen, int ttot, int NT, int N, int HV, int V, int dg_rows) {
   typedef ScanRegs<C> RT;
   typedef typename C::OPT OPT;
   typedef typename C::P P;
@@ -332,7 +333,10 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
   const size_t cQK = (size_t)BT * sQK, cA = (size_t)BT * sA, cV = (size_t)BT * sV,
                cG = (size_t)BT * sG, cD = (size_t)HV * DK;
 
-  const int NC = (eos - bos + BT - 1) / BT;
+  int NC = (eos - bos + BT - 1) / BT;
+  // KDA: the decay rows of the sequence's chunks are rows chunk0 .. chunk0 + NC - 1
+  // of DG; only non-monotone (invalid) varlen boundaries can reach past its end
+  if (C::KDA && chunk0 + NC > dg_rows) NC = dg_rows - chunk0 > 0 ? dg_rows - chunk0 : 0;
   // state snapshots: the state at the start of every nts-th chunk
   const size_t sbase = hs ? (size_t)snapshot_offset(cu, n, Tlen, nts * BT) : 0;
 
@@ -340,14 +344,16 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
   auto step = [&](RT& cur, RT& nxt, int ic) {
     const int c0 = bos + ic * BT;
     const int nrow = eos - c0 < BT ? eos - c0 : BT;
-    if (hs && ic % nts == 0) {
-      float* hp = hs + ((sbase + ic / nts) * HV + j) * (size_t)V * DK;
+    // (entries past the buffer's capacity are not written)
+    if (hs && ic % nts == 0 && (long long)(sbase + ic / nts) < scap) {
+      const size_t hp = ((sbase + ic / nts) * HV + j) * (size_t)V * DK;
 #pragma unroll
       for (int rb2 = 0; rb2 < RB; ++rb2)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          *reinterpret_cast<float4*>(hp + (size_t)(v0 + 16 * cb + row) * DK + WR * w + 16 * rb2 + 4 * grp) =
-              make_float4(St[rb2][cb][0], St[rb2][cb][1], St[rb2][cb][2], St[rb2][cb][3]);
+        for (int cb = 0; cb < CB; ++cb) {
+          const float x[4] = {St[rb2][cb][0], St[rb2][cb][1], St[rb2][cb][2], St[rb2][cb][3]};
+          store_state4(hs, hp + (size_t)(v0 + 16 * cb + row) * DK + WR * w + 16 * rb2 + 4 * grp, x, sbf16 != 0);
+        }
     }
     // update operand^T into LDS from the loader registers
 #pragma unroll
@@ -493,8 +499,9 @@ hipError_t launch_scan_c(const ChunkArgs& a, const ScanArgs& sa, hipStream_t s) 
   hipLaunchKernelGGL((chunk_scan_kernel<C>), dim3((unsigned)nblk), dim3(256), 0, s,
                      (const OPT*)sa.x, (const OPT*)sa.op, (const OPT*)sa.t, sa.op_rows,
                      sa.op_head_div, (const IOT*)a.v, (const float*)a.GF, sa.dg, a.scale, a.h0,
-                     a.ht, a.hs, a.split_chunks, (const P*)a.Ainv, (const P*)a.Aqk, (IOT*)a.o, a.cu_seqlens, sa.coff,
-                     a.seq_order, a.T, a.B * a.T, sa.NT, a.N, a.HV, a.V);
+                     a.ht, a.hs, a.split_chunks, a.hs_bf16 ? 1 : 0, a.hs_cap, (const P*)a.Ainv, (const P*)a.Aqk,
+                     (IOT*)a.o, a.cu_seqlens, sa.coff, a.seq_order, a.T, a.B * a.T, sa.NT, a.N, a.HV, a.V,
+                     a.max_chunks);
   return hipGetLastError();
 }
 

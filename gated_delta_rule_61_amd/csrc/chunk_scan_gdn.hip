@@ -266,10 +266,10 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     const void* __restrict__ qop, const void* __restrict__ kop, const f16_t* __restrict__ ktop,
     const bf16_t* __restrict__ v, const float* __restrict__ GF, const float* __restrict__ DG,
     const f16_t* __restrict__ Ainv, const f16_t* __restrict__ Aqk, float scale,
-    const float* __restrict__ h0, float* __restrict__ ht, float* __restrict__ hs, int nts,
-    bf16_t* __restrict__ o,
+    const float* __restrict__ h0, float* __restrict__ ht, void* __restrict__ hs, int nts, int sbf16,
+    long long scap, bf16_t* __restrict__ o,
     const int64_t* __restrict__ cu, const int32_t* __restrict__ order, const int32_t* __restrict__ coff,
-    int Tlen, int ttot, int NT, int N, int Hk, int HV, int V) {
+    int Tlen, int ttot, int NT, int N, int Hk, int HV, int V, int dg_rows) {
   typedef Lds<DK> L;
   constexpr int KS = L::KS, KB = L::KB, NQK = L::NQK;
   // q / k tile sources (GDN: the raw bf16 inputs, one row per q / k head;
@@ -326,7 +326,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   }
   const int jo = KDA ? j : j / (HV / Hk);   // row of the q / k tile sources
   const int v0 = vt * BV;
-  const int NC = (eos - bos + BT - 1) / BT;
+  int NC = (eos - bos + BT - 1) / BT;
+  // KDA: global index of the sequence's first chunk (row of the decay rows);
+  // only non-monotone (invalid) varlen boundaries can reach past their end
+  const int chunk0 = KDA ? (coff ? coff[ns] : ns * NT) : 0;
+  if (KDA && chunk0 + NC > dg_rows) NC = dg_rows - chunk0 > 0 ? dg_rows - chunk0 : 0;
   const size_t hbase = ((size_t)ns * HV + j) * (size_t)V * DK;
   const size_t gs = (size_t)gf_stride(ttot);   // gate-factor plane stride
   const uint32_t qk_row = (uint32_t)(KDA ? HV : Hk) * DK * 2, a_row = (uint32_t)HV * BT * 2,
@@ -389,11 +393,14 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       constexpr bool S1 = decltype(stg)::value;
       const char* sK = S1 ? sK1 : sK0;
       const char* sKt = KDA ? (S1 ? sT1 : sT0) : sK;   // source of the update's K^T
-      if (hs && c % nts == 0) {
-        float* hp = hs + ((sbase + c / nts) * HV + j) * (size_t)V * DK;
+      // (entries past the buffer's capacity are not written)
+      if (hs && c % nts == 0 && (long long)(sbase + c / nts) < scap) {
+        const size_t hp = ((sbase + c / nts) * HV + j) * (size_t)V * DK + (size_t)(v0 + 16 * cb + n) * DK;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          store_nt16(hp + (size_t)(v0 + 16 * cb + n) * DK + perm_row(kb, 4 * g), St[kb]);
+        for (int kb = 0; kb < KB; ++kb) {
+          const float x[4] = {St[kb][0], St[kb][1], St[kb][2], St[kb][3]};
+          store_state4(hs, hp + perm_row(kb, 4 * g), x, sbf16 != 0);
+        }
       }
       const char* sAi = S1 ? sAi1 : sAi0;
       const char* sV = S1 ? sV1 : sV0;
@@ -625,8 +632,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) o_v[i] = (uint32_t)(16 * i + lane / 4) * v_row + 16 * (lane % 4);
-    // KDA: global index of the sequence's first chunk (row of the decay rows)
-    const int chunk0 = KDA ? (coff ? coff[ns] : ns * NT) : 0;
 
     // loads of the chunk at token c0 into the given stage
     auto dma_chunk = [&](int c0, lchar* dK, lchar* dQ, lchar* dT, lchar* dAi, lchar* dAq, lchar* dV,
@@ -759,9 +764,9 @@ hipError_t launch_dk(const ChunkArgs& a, const void* qop, const void* kop, const
   hipLaunchKernelGGL((gdn_scan_bf16_kernel<DK, KDA>), dim3((unsigned)nblk), dim3(NTHR), 0, s, qop, kop,
                      (const f16_t*)ktop, (const bf16_t*)a.v, (const float*)a.GF, dg,
                      (const f16_t*)a.Ainv, (const f16_t*)a.Aqk, a.scale, a.h0, a.ht, a.hs, a.split_chunks,
-                     (bf16_t*)a.o,
+                     a.hs_bf16 ? 1 : 0, a.hs_cap, (bf16_t*)a.o,
                      a.cu_seqlens, a.seq_order, a.chunk_off, a.T, a.B * a.T, (a.T + BT - 1) / BT, a.N,
-                     a.Hk, a.HV, a.V);
+                     a.Hk, a.HV, a.V, a.max_chunks);
   return hipGetLastError();
 }
 

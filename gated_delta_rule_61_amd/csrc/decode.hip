@@ -498,15 +498,13 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(4))) v
 // With fewer (batch row, v-head) pairs than the 256 CUs, each pair is split
 // over four 64-thread work-groups (measured: -5 % at B = 1, T = 1 and -12 %
 // at B = 1, T = 4 with 32 v-heads; no gain from 16 rows of 32 v-heads on).
-#ifndef GDN_DECODE_SPLIT_BELOW
-#define GDN_DECODE_SPLIT_BELOW 256
-#endif
+constexpr long long kSplitBelow = 256;   // (batch row, v-head) pairs
 
 // T = 1 runs the per-token kernel (the rank-1 step has no products worth
 // MFMA work and its loads / stores cover whole rows); T = 2 .. 4 the MFMA form.
 template <int NTOK>
 hipError_t launch_n(const DecodeArgs& a, hipStream_t s) {
-  const bool split = (long long)a.B * a.HV < GDN_DECODE_SPLIT_BELOW;
+  const bool split = (long long)a.B * a.HV < kSplitBelow;
   const dim3 grid((unsigned)(a.B * a.HV * (split ? 4 : 1)));
   void (*kern)(const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*,
                const float*, const float*, bf16_t*, const int32_t*, bf16_t*, int, int, int,

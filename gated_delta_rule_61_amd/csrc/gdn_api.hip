@@ -99,9 +99,25 @@ struct Problem {
   int B, T, Hk, HV, K, V, N;
 };
 
+// Checks of the stored-state arguments shared by the prefill and the state
+// scans: split size, dtype, capacity (dense batches: every entry must fit).
+int check_states(const void* snaps, int split_size, long long entries, int state_dtype, bool varlen,
+                 int B, int T, const char* name) {
+  if (!snaps) return GDN_OK;
+  if (split_size <= 0 || split_size % 64 != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "split_size must be a positive multiple of 64 (got %d)", split_size);
+  if (state_dtype != GDN_DTYPE_F32 && state_dtype != GDN_DTYPE_BF16)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "unknown state dtype code %d", state_dtype);
+  if (entries < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "%s entries must be >= 0", name);
+  const long long need = (long long)B * ((T + split_size - 1) / split_size);
+  if (!varlen && entries < need)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "%s holds %lld entries, %lld needed", name, entries, need);
+  return GDN_OK;
+}
+
 int check_chunk(const void* q, const void* k, const void* v, const float* gate,
                 bool gate_required, const float* beta, const float* h0, float* ht,
-                const float* h_snap, int split_size,
+                const void* h_snap, int split_size, long long snap_entries, int state_dtype,
                 const int64_t* cu, int num_seqs, int B, int T, int Hk, int HV, int K, int V,
                 int chunk_size, int dtype, const void* o, Problem& P) {
   if (B < 0 || T < 0 || Hk <= 0 || HV <= 0 || K <= 0 || V <= 0)
@@ -128,8 +144,10 @@ int check_chunk(const void* q, const void* k, const void* v, const float* gate,
   if (work && (!q || !k || !v || !beta || !o))
     return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, beta and o are required");
   if (work && gate_required && !gate) return fail(GDN_ERR_INVALID_ARGUMENT, "gk is required");
-  if (h_snap && (split_size <= 0 || split_size % 64 != 0))
-    return fail(GDN_ERR_INVALID_ARGUMENT, "split_size must be a positive multiple of 64 (got %d)", split_size);
+  {
+    const int st = check_states(h_snap, split_size, snap_entries, state_dtype, cu != nullptr, B, T, "h_snap");
+    if (st != GDN_OK) return st;
+  }
   const void* ptrs[] = {q, k, v, gate, beta, h0, ht, h_snap, o};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(GDN_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
@@ -257,8 +275,8 @@ const char* gdn_status_string(int status) {
     case GDN_OK: return "ok";
     case GDN_ERR_INVALID_ARGUMENT: return "invalid argument";
     case GDN_ERR_UNSUPPORTED: return "unsupported";
-    case GDN_ERR_WORKSPACE: return "workspace too small";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
+    case GDN_ERR_WORKSPACE: return "workspace too small";
     default: return "unknown status";
   }
 }
@@ -288,13 +306,14 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
 }
 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
-                  const float* g_gamma, const float* beta, float scale, const float* h0, float* ht, float* h_snap, int split_size,
+                  const float* g_gamma, const float* beta, float scale, const float* h0, float* ht,
+                  void* h_snap, int split_size, long long snap_entries, int state_dtype,
                   const int64_t* cu_seqlens,
                   int num_seqs, int B, int T, int Hk, int HV, int K, int V, int chunk_size,
                   int dtype, void* o, void* workspace, size_t workspace_bytes, void* stream) {
   Problem P;
-  int st = check_chunk(q, k, v, g, false, beta, h0, ht, h_snap, split_size, cu_seqlens, num_seqs, B, T,
-                       Hk, HV, K, V, chunk_size, dtype, o, P);
+  int st = check_chunk(q, k, v, g, false, beta, h0, ht, h_snap, split_size, snap_entries, state_dtype,
+                       cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size, dtype, o, P);
   if (st != GDN_OK) return st;
   if (g && g_gamma) return fail(GDN_ERR_INVALID_ARGUMENT, "pass g or g_gamma, not both");
   const int eb = dtype == GDN_DTYPE_BF16 ? 2 : 4;
@@ -311,6 +330,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   a.q = q; a.k = k; a.v = v; a.g = g; a.g_gamma = g_gamma; a.gk = nullptr; a.beta = beta; a.scale = scale;
   a.h0 = h0; a.ht = ht; a.cu_seqlens = cu_seqlens; a.N = P.N;
   a.hs = h_snap; a.split_chunks = h_snap ? split_size / 64 : 1;
+  a.hs_bf16 = h_snap && state_dtype == GDN_DTYPE_BF16;
+  a.hs_cap = h_snap ? snap_entries : 0;
   a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
   a.bf16 = dtype == GDN_DTYPE_BF16;
   a.o = o;
@@ -326,14 +347,15 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* gk, const float* beta,
-                  float scale, const float* h0, float* ht, float* h_snap, int split_size,
+                  float scale, const float* h0, float* ht,
+                  void* h_snap, int split_size, long long snap_entries, int state_dtype,
                   const int64_t* cu_seqlens,
                   int num_seqs, int B, int T, int Hk, int HV, int K, int V, int chunk_size,
                   int dtype, void* o, void* Aqk, void* Akk_inv, void* workspace,
                   size_t workspace_bytes, void* stream) {
   Problem P;
-  int st = check_chunk(q, k, v, gk, true, beta, h0, ht, h_snap, split_size, cu_seqlens, num_seqs, B, T,
-                       Hk, HV, K, V, chunk_size, dtype, o, P);
+  int st = check_chunk(q, k, v, gk, true, beta, h0, ht, h_snap, split_size, snap_entries, state_dtype,
+                       cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size, dtype, o, P);
   if (st != GDN_OK) return st;
   if ((Aqk && !aligned16(Aqk)) || (Akk_inv && !aligned16(Akk_inv)))
     return fail(GDN_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
@@ -351,6 +373,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* gk, 
   a.q = q; a.k = k; a.v = v; a.g = nullptr; a.g_gamma = nullptr; a.gk = gk; a.beta = beta; a.scale = scale;
   a.h0 = h0; a.ht = ht; a.cu_seqlens = cu_seqlens; a.N = P.N;
   a.hs = h_snap; a.split_chunks = h_snap ? split_size / 64 : 1;
+  a.hs_bf16 = h_snap && state_dtype == GDN_DTYPE_BF16;
+  a.hs_cap = h_snap ? snap_entries : 0;
   a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
   a.bf16 = dtype == GDN_DTYPE_BF16;
   a.o = o;
@@ -411,8 +435,9 @@ int gdn_decode(const void* q, const void* k, const void* v, const void* a, const
 // checks and launch shared by the two state scans; a = A operand (q / k),
 // b = B operand (dout / v), init / snaps / fin = dht, dh, dh0 (h0, h, ht)
 static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, const float* g,
-                      const float* g_gamma, const float* gk, const float* gv, float scale,
-                      const float* init, float* snaps, int split_size, float* fin,
+                      const float* g_gamma, const float* gk, const float* gv, int num_gate_heads,
+                      float scale, const float* init, void* snaps, int split_size, long long entries,
+                      int state_dtype, float* fin,
                       const int64_t* cu_seqlens, int num_seqs, int B, int T, int Hk, int HV, int K, int V,
                       int chunk_size, int dtype, void* stream) {
   const char* an = fwd ? "k" : "q";
@@ -421,6 +446,9 @@ static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, c
     return fail(GDN_ERR_INVALID_ARGUMENT, "sizes must be positive (B, T >= 0): B=%d T=%d Hk=%d HV=%d K=%d V=%d",
                 B, T, Hk, HV, K, V);
   if (HV % Hk != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "HV (%d) must be a multiple of Hk (%d)", HV, Hk);
+  const int Hg = num_gate_heads == 0 ? HV : num_gate_heads;
+  if (Hg < 0 || HV % Hg != 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "HV (%d) must be a multiple of the gate heads (%d)", HV, Hg);
   if (dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_UNSUPPORTED, "the state scans take bf16 io only");
   if (chunk_size != 64) return fail(GDN_ERR_UNSUPPORTED, "chunk_size must be 64 (got %d)", chunk_size);
   if (!((K == 64 && V == 64) || (K == 128 && V == 128)))
@@ -428,10 +456,13 @@ static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, c
   if ((g != nullptr) + (g_gamma != nullptr) + (gk != nullptr) > 1)
     return fail(GDN_ERR_INVALID_ARGUMENT, "pass at most one of g, g_gamma and gk");
   if (gk && gv) return fail(GDN_ERR_UNSUPPORTED, "gk together with gv is not supported");
-  if (snaps && (split_size <= 0 || split_size % 64 != 0))
-    return fail(GDN_ERR_INVALID_ARGUMENT, "split_size must be a positive multiple of 64 (got %d)", split_size);
   if ((long long)B * T >= (1LL << 31) / 64)
     return fail(GDN_ERR_UNSUPPORTED, "B*T too large (got %lld tokens)", (long long)B * T);
+  {
+    const int st = check_states(snaps, split_size, entries, state_dtype, cu_seqlens != nullptr, B, T,
+                                fwd ? "h" : "dh");
+    if (st != GDN_OK) return st;
+  }
   int N = B;
   if (cu_seqlens) {
     if (B != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens requires B == 1 (got B=%d)", B);
@@ -447,7 +478,10 @@ static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, c
   BwdDhArgs a;
   a.q = a_op; a.dout = b_op; a.g = g; a.g_gamma = g_gamma; a.gk = gk; a.gv = gv; a.fwd = fwd;
   a.scale = scale; a.dht = init; a.dh = snaps; a.split_chunks = snaps ? split_size / 64 : 1; a.dh0 = fin;
+  a.dh_bf16 = snaps && state_dtype == GDN_DTYPE_BF16;
+  a.dh_cap = snaps ? entries : 0;
   a.cu_seqlens = cu_seqlens; a.N = N; a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
+  a.Hg = Hg;
   prof_begin(stage, (hipStream_t)stream);
   const hipError_t e = launch_bwd_dh(a, (hipStream_t)stream);
   prof_end(stage, (hipStream_t)stream);
@@ -456,19 +490,23 @@ static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, c
 }
 
 int gdn_chunk_bwd_dh(const void* q, const void* dout, const float* g, const float* g_gamma,
-                     const float* gk, const float* gv, float scale, const float* dht, float* dh,
-                     int split_size, float* dh0, const int64_t* cu_seqlens, int num_seqs, int B, int T,
+                     const float* gk, const float* gv, int num_gate_heads, float scale,
+                     const float* dht, void* dh, int split_size, long long dh_entries, int state_dtype,
+                     float* dh0, const int64_t* cu_seqlens, int num_seqs, int B, int T,
                      int Hk, int HV, int K, int V, int chunk_size, int dtype, void* stream) {
-  return state_scan(false, GDN_STAGE_BWD_DH, q, dout, g, g_gamma, gk, gv, scale, dht, dh, split_size, dh0,
-                    cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size, dtype, stream);
+  return state_scan(false, GDN_STAGE_BWD_DH, q, dout, g, g_gamma, gk, gv, num_gate_heads, scale, dht, dh,
+                    split_size, dh_entries, state_dtype, dh0, cu_seqlens, num_seqs, B, T, Hk, HV, K, V,
+                    chunk_size, dtype, stream);
 }
 
 int gdn_chunk_fwd_h(const void* k, const void* v, const float* g, const float* g_gamma,
-                    const float* gk, const float* gv, const float* h0, float* h, int split_size,
-                    float* ht, const int64_t* cu_seqlens, int num_seqs, int B, int T, int Hk, int HV,
+                    const float* gk, const float* gv, int num_gate_heads, const float* h0, void* h,
+                    int split_size, long long h_entries, int state_dtype, float* ht,
+                    const int64_t* cu_seqlens, int num_seqs, int B, int T, int Hk, int HV,
                     int K, int V, int chunk_size, int dtype, void* stream) {
-  return state_scan(true, GDN_STAGE_FWD_H, k, v, g, g_gamma, gk, gv, 1.f, h0, h, split_size, ht,
-                    cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size, dtype, stream);
+  return state_scan(true, GDN_STAGE_FWD_H, k, v, g, g_gamma, gk, gv, num_gate_heads, 1.f, h0, h, split_size,
+                    h_entries, state_dtype, ht, cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size, dtype,
+                    stream);
 }
 
 int gdn_state_to_pool(const float* ht, const int32_t* indices, void* pool_state, int N, int HV,

@@ -38,6 +38,12 @@ __device__ __forceinline__ void store_nt16(void* p, const V& v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, v), reinterpret_cast<u32x4_nt*>(p));
 }
 
+// ... of 8 bytes
+__device__ __forceinline__ void store_nt8(void* p, uint2 v) {
+  typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u32x2_nt{v.x, v.y}, reinterpret_cast<u32x2_nt*>(p));
+}
+
 __device__ __forceinline__ float bf2f(bf16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
 }
@@ -52,6 +58,17 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// Four consecutive fp32 state values at element `off` of a stored-state array
+// (streaming store): fp32, or rounded to nearest-even bf16 when `bf16`.
+__device__ __forceinline__ void store_state4(void* base, size_t off, const float (&x)[4], bool bf16) {
+  if (bf16) {
+    store_nt8(reinterpret_cast<bf16_t*>(base) + off, uint2{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])});
+  } else {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    store_nt16(reinterpret_cast<float*>(base) + off, f4{x[0], x[1], x[2], x[3]});
+  }
 }
 
 // ------------------------------------------------------- 16-lane reductions

@@ -29,16 +29,19 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // dht, the stored states in dh, ht in dh0)
 struct BwdDhArgs {
   const void *q, *dout;
-  const float *g, *g_gamma, *gk;   // at most one
-  const float* gv;                 // [B*T, HV, V] or nullptr; not with gk
+  const float *g, *g_gamma, *gk;   // at most one; Hg gate heads
+  const float* gv;                 // [B*T, Hg, V] or nullptr; not with gk
   bool fwd;
   float scale;
   const float* dht;                // [N, HV, V, K] or nullptr
-  float* dh;                       // [splits, HV, V, K] or nullptr
+  void* dh;                        // [splits, HV, V, K] fp32 or bf16 (dh_bf16), or nullptr
+  bool dh_bf16;
+  long long dh_cap;                // entries of dh; later entries are not written
   int split_chunks;
   float* dh0;                      // [N, HV, V, K] or nullptr
   const int64_t* cu_seqlens;
   int N, B, T, Hk, HV, K, V;
+  int Hg;                          // gate heads (HV % Hg == 0)
 };
 hipError_t launch_bwd_dh(const BwdDhArgs& a, hipStream_t s);
 
@@ -54,7 +57,9 @@ struct ChunkArgs {
   float scale;
   const float* h0;
   float* ht;
-  float* hs;             // [splits, HV, V, K] fp32 state snapshots or nullptr
+  void* hs;              // [splits, HV, V, K] state snapshots (fp32, or bf16 when hs_bf16) or nullptr
+  bool hs_bf16;
+  long long hs_cap;      // entries of hs; later entries are not written
   int split_chunks;      // chunks per snapshot (split_size / 64)
   const int64_t* cu_seqlens;
   int N;                 // sequences (B without cu_seqlens)

@@ -18,10 +18,7 @@ namespace gdn {
 
 namespace {
 
-#ifndef GDN_POOL_ITEMS
-#define GDN_POOL_ITEMS 1
-#endif
-constexpr int ITEMS = GDN_POOL_ITEMS;          // 8-element vectors per thread
+constexpr int ITEMS = 1;                       // 8-element vectors per thread
 constexpr int PER_BLOCK = 256 * 8 * ITEMS;     // elements per work-group
 
 __global__ __launch_bounds__(256) void state_to_pool_kernel(

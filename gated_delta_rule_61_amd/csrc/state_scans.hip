@@ -45,10 +45,7 @@ namespace gdn {
 namespace {
 
 constexpr int BT = 64;
-#ifndef GDN_BWD_BVT
-#define GDN_BWD_BVT 32
-#endif
-constexpr int BVT = GDN_BWD_BVT;   // V columns per work-group
+constexpr int BVT = 32;            // V columns per work-group
 constexpr int CBN = BVT / 16;      // 16-column blocks per work-group
 static_assert(BVT * 64 / 8 <= 256, "one gating unit per thread");
 constexpr int TP = BT + 8;     // padded token row of the transposed tiles (bf16)
@@ -91,8 +88,8 @@ __device__ __forceinline__ void transpose8(const uint4 (&R)[8], uint4 (&O)[8]) {
 template <int DK, bool FWD>
 __global__ __launch_bounds__(256) void state_scan_gk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ gk, float scale,
-    const float* __restrict__ dht, float* __restrict__ dh, int nts, float* __restrict__ dh0,
-    const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV) {
+    const float* __restrict__ dht, void* __restrict__ dh, int nts, int sbf16, long long scap,
+    float* __restrict__ dh0, const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV, int Hg) {
   constexpr int DV = DK;
   constexpr int RW = DK / 4;          // key rows per wave
   constexpr int RB = RW / 16;         // 16-row blocks per wave
@@ -118,6 +115,7 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
   if (sh >= N * HV) return;
   const int sq = sh / HV, j = sh - sq * HV;
   const int jk = j / (HV / Hk);
+  const int jg = j / (HV / Hg);   // gate head: HV / Hg v-heads share one
   const int v0 = vt * BVT;
   int bos, eos;
   if (cu) {
@@ -148,12 +146,16 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
         acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
-  auto store_state = [&](float* dst) {
+  // the state into a [*, HV, V, K] array at entry `e` (fp32, or bf16 when `bf`)
+  auto store_state = [&](void* dst, size_t e, bool bf) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < CBN; ++cb)
-        store_nt16(dst + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq, acc[rb][cb]);
+      for (int cb = 0; cb < CBN; ++cb) {
+        const float x[4] = {acc[rb][cb][0], acc[rb][cb][1], acc[rb][cb][2], acc[rb][cb][3]};
+        store_state4(dst, (e * HV + j) * (size_t)DV * DK + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq,
+                     x, bf);
+      }
   };
 
   // this thread's 8 x 8 block: q (waves 0 .. NQB / 64 - 1) or dO (the next
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
 #pragma unroll
       for (int t = 0; t < BT; ++t) {
         const int tc = t < nrow ? t : nrow - 1;
-        gv[t] = gk[((size_t)(c0 + tc) * HV + j) * DK + tid];
+        gv[t] = gk[((size_t)(c0 + tc) * Hg + jg) * DK + tid];
       }
     }
   };
@@ -258,7 +260,8 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
     if (i + 2 < NC) load(chunk_at(i + 2), raw, gv);
 
     // ---- snapshot, decay, accumulate
-    if (dh && ic % nts == 0) store_state(dh + ((sbase + ic / nts) * HV + j) * (size_t)DV * DK);
+    // (entries past the buffer's capacity are not written)
+    if (dh && ic % nts == 0 && (long long)(sbase + ic / nts) < scap) store_state(dh, sbase + ic / nts, sbf16 != 0);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       f32x4 dec;
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
     step(chunk_at(i), i, rawA, gvA);
     if (i + 1 < NC) step(chunk_at(i + 1), i + 1, rawB, gvB);
   }
-  if (dh0) store_state(dh0 + hbase);
+  if (dh0) store_state(dh0, sq, false);
 }
 
 // Scalar gate (g or gamma) and / or the per-value-channel gate (gv): two
@@ -310,8 +313,8 @@ template <int DK, bool FWD, bool GV>
 __global__ __launch_bounds__(256) void state_scan_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ g,
     const float* __restrict__ gamma, const float* __restrict__ gvp, float scale,
-    const float* __restrict__ dht, float* __restrict__ dh, int nts, float* __restrict__ dh0,
-    const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV) {
+    const float* __restrict__ dht, void* __restrict__ dh, int nts, int sbf16, long long scap,
+    float* __restrict__ dh0, const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV, int Hg) {
   constexpr int DV = DK;
   constexpr int RW = DK / 4;
   constexpr int RB = RW / 16;
@@ -336,6 +339,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
   if (sh >= N * HV) return;
   const int sq = sh / HV, j = sh - sq * HV;
   const int jk = j / (HV / Hk);
+  const int jg = j / (HV / Hg);   // gate head: HV / Hg v-heads share one
   const int v0 = vt * BVT;
   int bos, eos;
   if (cu) {
@@ -365,12 +369,16 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
         acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
-  auto store_state = [&](float* dst) {
+  // the state into a [*, HV, V, K] array at entry `e` (fp32, or bf16 when `bf`)
+  auto store_state = [&](void* dst, size_t e, bool bf) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < CBN; ++cb)
-        store_nt16(dst + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq, acc[rb][cb]);
+      for (int cb = 0; cb < CBN; ++cb) {
+        const float x[4] = {acc[rb][cb][0], acc[rb][cb][1], acc[rb][cb][2], acc[rb][cb][3]};
+        store_state4(dst, (e * HV + j) * (size_t)DV * DK + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq,
+                     x, bf);
+      }
   };
 
   // roles: the first QB / 64 waves -> q blocks; waves 2, 3 -> dO (columns
@@ -406,7 +414,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
         const size_t off = ((size_t)(c0 + tc) * HV + j) * DV + v0 + 2 * dp;
         rd[r] = *reinterpret_cast<const uint32_t*>(dout + off);
         if constexpr (GV) {
-          const float2 x = *reinterpret_cast<const float2*>(gvp + off);
+          const float2 x = *reinterpret_cast<const float2*>(gvp + ((size_t)(c0 + tc) * Hg + jg) * DV + v0 + 2 * dp);
           gw[0][r] = t < nrow ? x.x : 0.f;
           gw[1][r] = t < nrow ? x.y : 0.f;
         }
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
       // a branch between a vector and a scalar load would make the compiler
       // wait for every load in flight where the two meet
       const int tc = lane < nrow ? lane : nrow - 1;
-      const float* gp = g ? g + (size_t)(c0 + tc) * HV + j : (gamma ? gamma + j : kNoGate);
+      const float* gp = g ? g + (size_t)(c0 + tc) * Hg + jg : (gamma ? gamma + jg : kNoGate);
       gv = *gp;
     }
   };
@@ -506,7 +514,8 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
     // ---- products; the next chunk's gate factors; the loads of the chunk after next
     if (w == 0 && i + 1 < NC) gates(chunk_at(i + 1), gvN, b ^ 1);
     if (i + 2 < NC) load(chunk_at(i + 2), rq, rd, gw, gv);
-    if (dh && ic % nts == 0) store_state(dh + ((sbase + ic / nts) * HV + j) * (size_t)DV * DK);
+    // (entries past the buffer's capacity are not written)
+    if (dh && ic % nts == 0 && (long long)(sbase + ic / nts) < scap) store_state(dh, sbase + ic / nts, sbf16 != 0);
     const float dec = sGam[b][BT];
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb) {
@@ -543,7 +552,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
     step(chunk_at(i), i, 0, rqA, rdA, gwA, gvA, gvB);
     if (i + 1 < NC) step(chunk_at(i + 1), i + 1, 1, rqB, rdB, gwB, gvB, gvA);
   }
-  if (dh0) store_state(dh0 + hbase);
+  if (dh0) store_state(dh0, sq, false);
 }
 
 template <int DK, bool FWD>
@@ -552,7 +561,8 @@ hipError_t launch_k(const BwdDhArgs& a, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((state_scan_gk_kernel<DK, FWD>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.dout, a.gk, a.scale, a.dht, a.dh,
-                     a.split_chunks, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV);
+                     a.split_chunks, a.dh_bf16 ? 1 : 0, a.dh_cap, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV,
+                     a.Hg);
   return hipGetLastError();
 }
 
@@ -564,7 +574,8 @@ hipError_t launch_gdn(const BwdDhArgs& a, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((state_scan_kernel<DK, FWD, GV>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.dout, a.g, a.g_gamma, a.gv, a.scale, a.dht, a.dh,
-                     a.split_chunks, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV);
+                     a.split_chunks, a.dh_bf16 ? 1 : 0, a.dh_cap, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV,
+                     a.Hg);
   return hipGetLastError();
 }
 

@@ -36,8 +36,21 @@
  *   - Every argument check runs on the host before any HIP call; a failed
  *     check returns GDN_ERR_INVALID_ARGUMENT or GDN_ERR_UNSUPPORTED and
  *     queues nothing.  gdn_last_error() then describes the failure.
- *   - A launch failure reported by the HIP runtime returns GDN_ERR_LAUNCH.
+ *   - A launch failure reported by the HIP runtime returns GDN_ERR_LAUNCH; a
+ *     missing or too small workspace GDN_ERR_WORKSPACE (the one code added
+ *     to the four of the plan: it tells the caller to query the size).
  *   - io dtype codes: GDN_DTYPE_F32 (0) or GDN_DTYPE_BF16 (1).
+ *   - Stored states (prefill snapshots, the state scans' h / dh) are kept in
+ *     fp32 or bf16 as the caller chooses (state_dtype; "fla ops/common/
+ *     chunk_h.py", chunk_fwd_h / chunk_bwd_dh: states in the input dtype
+ *     unless states_in_fp32).  A bf16 state is the fp32 state rounded to
+ *     nearest, ties to even.  Initial and final states (h0, ht, dht, dh0)
+ *     are always fp32.  A stored-state buffer comes with its capacity in
+ *     entries of [HV, V, K]: without cu_seqlens a buffer smaller than the
+ *     call needs is rejected (GDN_ERR_INVALID_ARGUMENT); with cu_seqlens
+ *     (whose values the host never reads) entries at or past the capacity
+ *     are not written.  sum_n ceil(L_n / split_size) <= ceil(T / split_size)
+ *     + N bounds the entries a varlen call needs.
  */
 #ifndef GDN61_H
 #define GDN61_H
@@ -53,8 +66,8 @@ typedef enum {
   GDN_OK = 0,
   GDN_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad size, bad layout */
   GDN_ERR_UNSUPPORTED = 2,      /* valid request outside the compiled set     */
-  GDN_ERR_WORKSPACE = 3,        /* workspace missing or smaller than needed   */
-  GDN_ERR_LAUNCH = 4            /* the HIP runtime rejected a kernel launch   */
+  GDN_ERR_LAUNCH = 3,           /* the HIP runtime rejected a kernel launch   */
+  GDN_ERR_WORKSPACE = 4         /* workspace missing or smaller than needed   */
 } gdn_status_t;
 
 enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 };
@@ -99,7 +112,8 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
  *   scale       output scale (callers usually pass K^-0.5)
  *   h0          [N, HV, V, K]   fp32 initial state, or NULL for zeros
  *   ht          [N, HV, V, K]   fp32 final state out, or NULL to skip
- *   h_snap      [S, HV, V, K]   fp32 state snapshots out, or NULL to skip:
+ *   h_snap      [S, HV, V, K]   state snapshots out (fp32 or bf16, state_dtype),
+ *                               or NULL to skip:
  *                               the state before the first token of every
  *                               split of split_size tokens of a sequence
  *                               ("fla ops/common/chunk_h.py",
@@ -115,14 +129,17 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
  *                               zeros).  The caller sizes the buffer.
  *   split_size  tokens per snapshot, a positive multiple of 64; read only
  *               when h_snap is not NULL
+ *   snap_entries  capacity of h_snap in [HV, V, K] entries (see above)
+ *   state_dtype   GDN_DTYPE_F32 or GDN_DTYPE_BF16: dtype of h_snap
  *   cu_seqlens  [N + 1]         int64 device array of packed sequence
  *                               boundaries, or NULL.  With it B must be 1 and
  *                               num_seqs = N; the values must satisfy
  *                               0 = cu[0] <= cu[1] <= ... <= cu[N] = T
- *                               (values outside [0, T] are clamped so no
- *                               access leaves the buffers; results are then
- *                               unspecified).  Without it num_seqs is ignored
- *                               and N = B.
+ *                               (values outside [0, T] are clamped, and
+ *                               non-monotone values only shorten what is
+ *                               computed, so no access leaves the buffers;
+ *                               results are then unspecified).  Without it
+ *                               num_seqs is ignored and N = B.
  *   o           [B, T, HV, V]   io dtype output
  *   workspace   device buffer of at least gdn_chunk_fwd_workspace_bytes()
  *
@@ -132,7 +149,8 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
  */
 int gdn_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* g, const float* g_gamma, const float* beta, float scale,
-                  const float* h0, float* ht, float* h_snap, int split_size,
+                  const float* h0, float* ht,
+                  void* h_snap, int split_size, long long snap_entries, int state_dtype,
                   const int64_t* cu_seqlens, int num_seqs,
                   int B, int T, int Hk, int HV, int K, int V,
                   int chunk_size, int dtype,
@@ -158,7 +176,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v,
  */
 int kda_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* gk, const float* beta, float scale,
-                  const float* h0, float* ht, float* h_snap, int split_size,
+                  const float* h0, float* ht,
+                  void* h_snap, int split_size, long long snap_entries, int state_dtype,
                   const int64_t* cu_seqlens, int num_seqs,
                   int B, int T, int Hk, int HV, int K, int V,
                   int chunk_size, int dtype,
@@ -221,18 +240,25 @@ int gdn_decode(const void* q, const void* k, const void* v,
  * (terms free of h), o_t = scale q_t . h_t; the delta rule's erase term is
  * not part of it.
  *
- *   q            [B, T, Hk, K]  bf16
+ *   q            [B, T, Hk, K]  bf16 (query head of v-head j: j / (HV / Hk))
  *   dout         [B, T, HV, V]  bf16 gradient of the output
- *   g [B,T,HV] | g_gamma [HV] | gk [B,T,HV,K]   fp32 log-gates, at most
+ *   num_gate_heads  Hg, the heads of the gate arrays (0 = HV); HV must be a
+ *                multiple of it and v-head j takes gate head j / (HV / Hg).
+ *                The page's grouped form (HQ query / output heads sharing
+ *                the gates of H = HQ / NG heads, one dh per query head) is
+ *                Hk = HV = HQ with Hg = H
+ *   g [B,T,Hg] | g_gamma [Hg] | gk [B,T,Hg,K]   fp32 log-gates, at most
  *                one (none = no decay); as in gdn_chunk_fwd / kda_chunk_fwd
- *   gv           [B, T, HV, V]  fp32 per-value-channel log-gates, or NULL;
+ *   gv           [B, T, Hg, V]  fp32 per-value-channel log-gates, or NULL;
  *                may come with g or g_gamma, not with gk (GDN_ERR_UNSUPPORTED)
  *   dht          [N, HV, V, K]  fp32 gradient of the final state, or NULL
- *   dh           [S, HV, V, K]  fp32 out, or NULL: sequence n of length L_n
- *                owns ceil(L_n / split_size) entries after those of
- *                sequences 0..n-1 (entry s = the gradient at the end of
- *                chunk s * split_size / 64)
+ *   dh           [S, HV, V, K]  out (fp32 or bf16, state_dtype), or NULL:
+ *                sequence n of length L_n owns ceil(L_n / split_size)
+ *                entries after those of sequences 0..n-1 (entry s = the
+ *                gradient at the end of chunk s * split_size / 64)
  *   split_size   a positive multiple of 64, read when dh is not NULL
+ *   dh_entries   capacity of dh in [HV, V, K] entries (see the conventions)
+ *   state_dtype  GDN_DTYPE_F32 or GDN_DTYPE_BF16: dtype of dh
  *   dh0          [N, HV, V, K]  fp32 out (gradient of the initial state), or NULL
  *   cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size  as in gdn_chunk_fwd
  * Supported: dtype = GDN_DTYPE_BF16, K = V in {64, 128}, chunk_size = 64.
@@ -240,9 +266,11 @@ int gdn_decode(const void* q, const void* k, const void* v,
  */
 int gdn_chunk_bwd_dh(const void* q, const void* dout,
                      const float* g, const float* g_gamma, const float* gk,
-                     const float* gv, float scale, const float* dht, float* dh,
-                     int split_size, float* dh0, const int64_t* cu_seqlens,
-                     int num_seqs, int B, int T, int Hk, int HV, int K, int V,
+                     const float* gv, int num_gate_heads, float scale,
+                     const float* dht, void* dh, int split_size,
+                     long long dh_entries, int state_dtype, float* dh0,
+                     const int64_t* cu_seqlens, int num_seqs,
+                     int B, int T, int Hk, int HV, int K, int V,
                      int chunk_size, int dtype, void* stream);
 
 /*
@@ -263,13 +291,15 @@ int gdn_chunk_bwd_dh(const void* q, const void* dout,
  *
  *   k            [B, T, Hk, K]  bf16 (key head of v-head j: j / (HV / Hk))
  *   v            [B, T, HV, V]  bf16
- *   g, g_gamma, gk, gv          as in gdn_chunk_bwd_dh
+ *   num_gate_heads, g, g_gamma, gk, gv   as in gdn_chunk_bwd_dh
  *   h0           [N, HV, V, K]  fp32 initial state, or NULL (zeros)
- *   h            [S, HV, V, K]  fp32 out, or NULL: sequence n of length L_n
- *                owns ceil(L_n / split_size) entries after those of
- *                sequences 0..n-1 (entry s = the state at the start of chunk
- *                s * split_size / 64)
+ *   h            [S, HV, V, K]  out (fp32 or bf16, state_dtype), or NULL:
+ *                sequence n of length L_n owns ceil(L_n / split_size)
+ *                entries after those of sequences 0..n-1 (entry s = the
+ *                state at the start of chunk s * split_size / 64)
  *   split_size   a positive multiple of 64, read when h is not NULL
+ *   h_entries    capacity of h in [HV, V, K] entries (see the conventions)
+ *   state_dtype  GDN_DTYPE_F32 or GDN_DTYPE_BF16: dtype of h
  *   ht           [N, HV, V, K]  fp32 out (final state), or NULL
  *   cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size  as in gdn_chunk_fwd
  * Supported: dtype = GDN_DTYPE_BF16, K = V in {64, 128}, chunk_size = 64.
@@ -278,8 +308,10 @@ int gdn_chunk_bwd_dh(const void* q, const void* dout,
  */
 int gdn_chunk_fwd_h(const void* k, const void* v,
                     const float* g, const float* g_gamma, const float* gk,
-                    const float* gv, const float* h0, float* h, int split_size,
-                    float* ht, const int64_t* cu_seqlens, int num_seqs,
+                    const float* gv, int num_gate_heads, const float* h0,
+                    void* h, int split_size, long long h_entries,
+                    int state_dtype, float* ht,
+                    const int64_t* cu_seqlens, int num_seqs,
                     int B, int T, int Hk, int HV, int K, int V,
                     int chunk_size, int dtype, void* stream);
 

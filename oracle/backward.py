@@ -7,6 +7,12 @@ chunk whose index is a multiple of split_size / chunk_size, then applies the
 chunk (decay the gradient, add scale * (q o e^G)^T do), and returns dh0 at the
 start of the sequence.
 
+Heads: q has Hk heads, dout and the gradients HV, the gates Hg (each a
+divisor of HV); v-head j reads q head j // (HV // Hk) and gate head
+j // (HV // Hg).  The page's grouped form -- HQ query / output heads whose
+programs read the gates of head i_hq // NG, with one dh per query head -- is
+Hk = HV = HQ and Hg = HQ // NG.
+
 That is the gradient of the decay-only recurrence
     h_t = D_t h_{t-1} + (terms free of h),   o_t = scale * h_t q_t
 (D_t = e^{g_t}, diag(e^{gk_t}) on the key channels and / or diag(e^{gv_t}) on
@@ -34,8 +40,16 @@ def state_grad_scan(q, dout, scale: float, g=None, g_gamma=None, gk=None, gv=Non
     g, gk, gv, dht = _f64(g), _f64(gk), _f64(gv), _f64(dht)
     B, T, Hk, K = q.shape
     HV, V = dout.shape[2], dout.shape[3]
+    # gate heads: Hg of them, a divisor of HV; v-head j takes gate head
+    # j // (HV // Hg) (the page's grouped form: several query / output heads
+    # share the gates of one head)
     if g_gamma is not None:
-        g = np.broadcast_to(_f64(g_gamma), (B, T, HV))
+        gam = _f64(g_gamma)
+        g = np.broadcast_to(gam, (B, T, gam.shape[0]))
+    heads = {x.shape[2] for x in (g, gk, gv) if x is not None}
+    assert len(heads) <= 1, "the gates disagree on their head count"
+    Hg = heads.pop() if heads else HV
+    assert HV % Hg == 0
     seqs = sequences(B, T, cu_seqlens)
     dh0 = np.zeros((len(seqs), HV, V, K))
     snaps = []
@@ -45,6 +59,7 @@ def state_grad_scan(q, dout, scale: float, g=None, g_gamma=None, gk=None, gv=Non
         seq_snaps = [None] * (0 if r is None else -(-(eos - bos) // split_size))
         for j in range(HV):
             kh = j // (HV // Hk)
+            jg = j // (HV // Hg)
             D = np.zeros((V, K)) if dht is None else dht[n, j].copy()
             for ic in range(nc - 1, -1, -1):
                 if r is not None and ic % r == 0:
@@ -54,11 +69,11 @@ def state_grad_scan(q, dout, scale: float, g=None, g_gamma=None, gk=None, gv=Non
                 for t in range(min(bos + (ic + 1) * chunk_size, eos) - 1, bos + ic * chunk_size - 1, -1):
                     D = D + scale * np.outer(dout[b, t, j], q[b, t, kh])
                     if g is not None:
-                        D = D * np.exp(g[b, t, j])
+                        D = D * np.exp(g[b, t, jg])
                     if gk is not None:
-                        D = D * np.exp(gk[b, t, j])[None, :]
+                        D = D * np.exp(gk[b, t, jg])[None, :]
                     if gv is not None:
-                        D = D * np.exp(gv[b, t, j])[:, None]
+                        D = D * np.exp(gv[b, t, jg])[:, None]
             dh0[n, j] = D
         snaps += seq_snaps
     dh = None

@@ -28,16 +28,25 @@ def state_scan(k, v, g=None, g_gamma=None, gk=None, gv=None, h0=None, cu_seqlens
                split_size=None, chunk_size: int = 64):
     """Return (h [S, HV, V, K] or None, ht [N, HV, V, K]), float64.
 
-    k [B, T, Hk, K]; v [B, T, HV, V]; g [B, T, HV]; g_gamma [HV]; gk [B, T, HV, K];
-    gv [B, T, HV, V]; h0 [N, HV, V, K].  h holds, per sequence (in order), the
+    k [B, T, Hk, K]; v [B, T, HV, V]; g [B, T, Hg]; g_gamma [Hg]; gk [B, T, Hg, K];
+    gv [B, T, Hg, V]; h0 [N, HV, V, K]; v-head j reads k head j // (HV // Hk)
+    and gate head j // (HV // Hg) (Hg = HV unless the gates have fewer heads).  h holds, per sequence (in order), the
     state at the start of chunks 0, r, 2r, ... (r = split_size / chunk_size):
     ceil(length / split_size) entries per sequence."""
     k, v = _f64(k), _f64(v)
     g, gk, gv, h0 = _f64(g), _f64(gk), _f64(gv), _f64(h0)
     B, T, Hk, K = k.shape
     HV, V = v.shape[2], v.shape[3]
+    # gate heads: Hg of them, a divisor of HV; v-head j takes gate head
+    # j // (HV // Hg) (the page's grouped form: several query / output heads
+    # share the gates of one head)
     if g_gamma is not None:
-        g = np.broadcast_to(_f64(g_gamma), (B, T, HV))
+        gam = _f64(g_gamma)
+        g = np.broadcast_to(gam, (B, T, gam.shape[0]))
+    heads = {x.shape[2] for x in (g, gk, gv) if x is not None}
+    assert len(heads) <= 1, "the gates disagree on their head count"
+    Hg = heads.pop() if heads else HV
+    assert HV % Hg == 0
     seqs = sequences(B, T, cu_seqlens)
     ht = np.zeros((len(seqs), HV, V, K))
     snaps = []
@@ -47,6 +56,7 @@ def state_scan(k, v, g=None, g_gamma=None, gk=None, gv=None, h0=None, cu_seqlens
         seq_snaps = [None] * (0 if r is None else -(-(eos - bos) // split_size))
         for j in range(HV):
             kh = j // (HV // Hk)
+            jg = j // (HV // Hg)
             S = np.zeros((V, K)) if h0 is None else h0[n, j].copy()
             for ic in range(nc):
                 if r is not None and ic % r == 0:
@@ -55,11 +65,11 @@ def state_scan(k, v, g=None, g_gamma=None, gk=None, gv=None, h0=None, cu_seqlens
                     seq_snaps[ic // r][j] = S
                 for t in range(bos + ic * chunk_size, min(bos + (ic + 1) * chunk_size, eos)):
                     if g is not None:
-                        S = S * np.exp(g[b, t, j])
+                        S = S * np.exp(g[b, t, jg])
                     if gk is not None:
-                        S = S * np.exp(gk[b, t, j])[None, :]
+                        S = S * np.exp(gk[b, t, jg])[None, :]
                     if gv is not None:
-                        S = S * np.exp(gv[b, t, j])[:, None]
+                        S = S * np.exp(gv[b, t, jg])[:, None]
                     S = S + np.outer(v[b, t, j], k[b, t, kh])
             ht[n, j] = S
         snaps += seq_snaps

@@ -46,13 +46,25 @@ def test_version_and_status_strings(L):
     assert L.gdn_status_string(99) == b"unknown status"
 
 
+def test_status_numbering():
+    """The planned numbering (OK 0, invalid argument 1, unsupported 2, launch
+    3), with the workspace code appended as 4."""
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "gdn61.h")).read(), flags=re.S)
+    codes = dict((n, int(v)) for n, v in re.findall(r"(GDN_(?:OK|ERR_[A-Z_]+))\s*=\s*(\d+)", src))
+    assert codes == {"GDN_OK": 0, "GDN_ERR_INVALID_ARGUMENT": 1, "GDN_ERR_UNSUPPORTED": 2,
+                     "GDN_ERR_LAUNCH": 3, "GDN_ERR_WORKSPACE": 4}
+    L = binding.lib()
+    assert L.gdn_status_string(3) == b"kernel launch failed"
+    assert L.gdn_status_string(4) == b"workspace too small"
+
+
 def _chunk(L, **kw):
-    a = dict(q=None, k=None, v=None, g=None, gg=None, beta=None, scale=1.0, h0=None, ht=None, hs=None, ss=0, cu=None, ns=0,
-             B=1, T=64, Hk=2, HV=2, K=64, V=64, cs=64, dt=1, o=None, ws=None, wsb=0, st=None)
+    a = dict(q=None, k=None, v=None, g=None, gg=None, beta=None, scale=1.0, h0=None, ht=None, hs=None, ss=0, se=1 << 30,
+             sdt=0, cu=None, ns=0, B=1, T=64, Hk=2, HV=2, K=64, V=64, cs=64, dt=1, o=None, ws=None, wsb=0, st=None)
     a.update(kw)
     return L.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["gg"], a["beta"], a["scale"], a["h0"], a["ht"],
-                           a["hs"], a["ss"], a["cu"], a["ns"], a["B"], a["T"], a["Hk"], a["HV"], a["K"], a["V"], a["cs"],
-                           a["dt"], a["o"], a["ws"], a["wsb"], a["st"])
+                           a["hs"], a["ss"], a["se"], a["sdt"], a["cu"], a["ns"], a["B"], a["T"], a["Hk"], a["HV"],
+                           a["K"], a["V"], a["cs"], a["dt"], a["o"], a["ws"], a["wsb"], a["st"])
 
 
 FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced (checks fail first)
@@ -66,12 +78,16 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced (checks
     (dict(B=-1), 1, b"sizes"),
     (dict(B=2, cu=FAKE, ns=3), 1, b"B == 1"),
     (dict(), 1, b"required"),
-    (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE), 3, b"workspace"),
+    (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE), 4, b"workspace"),
     (dict(q=FAKE + 4, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, ws=FAKE, wsb=1 << 40), 1, b"aligned"),
     (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE, ss=96), 1, b"split_size"),
     (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, g=FAKE, gg=FAKE, ws=FAKE, wsb=1 << 40), 1, b"not both"),
     (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE, ss=0), 1, b"split_size"),
     (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE + 8, ss=64, ws=FAKE, wsb=1 << 40), 1, b"aligned"),
+    # an undersized snapshot buffer (dense: B * ceil(T / split) = 2 * 3 entries needed) is rejected
+    (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE, ss=64, se=5, B=2, T=130, ws=FAKE, wsb=1 << 40),
+     1, b"6 needed"),
+    (dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, hs=FAKE, ss=64, sdt=5, ws=FAKE, wsb=1 << 40), 1, b"state dtype"),
 ])
 def test_chunk_fwd_rejects(L, kw, status, msg):
     assert _chunk(L, **kw) == status
@@ -79,9 +95,15 @@ def test_chunk_fwd_rejects(L, kw, status, msg):
 
 
 def test_kda_requires_gate(L):
-    r = L.kda_chunk_fwd(FAKE, FAKE, FAKE, None, FAKE, 1.0, None, None, None, 0, None, 0, 1, 64, 1, 1, 64, 64, 64, 1,
-                        FAKE, None, None, FAKE, 1 << 40, None)
+    r = L.kda_chunk_fwd(FAKE, FAKE, FAKE, None, FAKE, 1.0, None, None, None, 0, 0, 0, None, 0, 1, 64, 1, 1, 64, 64,
+                        64, 1, FAKE, None, None, FAKE, 1 << 40, None)
     assert r == 1 and b"gk" in L.gdn_last_error()
+
+
+def test_kda_rejects_undersized_snapshots(L):
+    r = L.kda_chunk_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, None, None, FAKE, 128, 1, 0, None, 0, 2, 64, 1, 1, 64, 64,
+                        64, 1, FAKE, None, None, FAKE, 1 << 40, None)
+    assert r == 1 and b"2 needed" in L.gdn_last_error()
 
 
 def _dec(L, **kw):
@@ -143,12 +165,12 @@ def test_state_to_pool_empty_is_a_no_op(L):
     assert _pool(L, N=0, pool=0) == 0
 
 
-def _bwd(L, q=FAKE, do=FAKE, g=None, gg=None, gk=None, gv=None, dht=None, dh=None, ss=64, dh0=FAKE, cu=None,
-         ns=0, B=1, T=64, Hk=1, HV=1, K=64, V=64, cs=64, dt=1, fwd=False):
+def _bwd(L, q=FAKE, do=FAKE, g=None, gg=None, gk=None, gv=None, hg=0, dht=None, dh=None, ss=64, se=1 << 30, sdt=0,
+         dh0=FAKE, cu=None, ns=0, B=1, T=64, Hk=1, HV=1, K=64, V=64, cs=64, dt=1, fwd=False):
     f = L.gdn_chunk_fwd_h if fwd else L.gdn_chunk_bwd_dh
     if fwd:
-        return f(q, do, g, gg, gk, gv, dht, dh, ss, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
-    return f(q, do, g, gg, gk, gv, 1.0, dht, dh, ss, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
+        return f(q, do, g, gg, gk, gv, hg, dht, dh, ss, se, sdt, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
+    return f(q, do, g, gg, gk, gv, hg, 1.0, dht, dh, ss, se, sdt, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
 
 
 @pytest.mark.parametrize("fwd", [False, True])
@@ -162,6 +184,9 @@ def _bwd(L, q=FAKE, do=FAKE, g=None, gg=None, gk=None, gv=None, dht=None, dh=Non
     (dict(do=FAKE + 2), 1, b"aligned"),
     (dict(gv=FAKE + 4), 1, b"aligned"),
     (dict(B=2, cu=FAKE, ns=2), 1, b"B == 1"),
+    (dict(HV=4, Hk=4, hg=3), 1, b"gate heads"),
+    (dict(dh=FAKE, B=3, T=100, se=5), 1, b"6 needed"),
+    (dict(dh=FAKE, sdt=2), 1, b"state dtype"),
 ])
 def test_state_scans_reject(L, kw, status, msg, fwd):
     assert _bwd(L, fwd=fwd, **kw) == status
@@ -173,3 +198,27 @@ def test_state_scans_nothing_to_do(L, fwd):
     # no sequences, or no output requested: returns before any HIP call
     assert _bwd(L, fwd=fwd, B=0) == 0
     assert _bwd(L, fwd=fwd, dh0=None) == 0
+
+
+def test_snapshot_count_reads_no_device_memory(monkeypatch):
+    """No binding path synchronises the host: the varlen snapshot count takes
+    host boundaries only (a device -- here a meta -- tensor is refused, and
+    Tensor.cpu is never called)."""
+    import torch
+
+    def no_cpu(*a, **k):
+        raise AssertionError("Tensor.cpu called")
+
+    monkeypatch.setattr(torch.Tensor, "cpu", no_cpu)
+    assert binding.snapshot_count(2, 130, 64) == 6
+    assert binding.snapshot_count(1, 400, 64, [0, 130, 194, 195, 400]) == 3 + 1 + 1 + 4
+    assert binding.snapshot_count(1, 400, 128, torch.tensor([0, 130, 194, 195, 400])) == 2 + 1 + 1 + 2
+    with pytest.raises(ValueError):
+        binding.snapshot_count(1, 400, 64, torch.zeros(5, dtype=torch.int64, device="meta"))
+
+
+def test_binding_sources_never_copy_to_host():
+    src = open(os.path.join(ROOT, "gated_delta_rule_61_amd", "binding.py")).read()
+    for pat in (".cpu(", ".item(", ".tolist(", "numpy("):
+        hits = [l for l in src.splitlines() if pat in l and "cu_seqlens_host" not in l]
+        assert not hits, hits

@@ -12,16 +12,18 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _run(inp, batches=None, use_norm=True):
+def _run(inp, batches=None, use_norm=True, sp_beta=1.0, sp_thr=20.0):
     d = {n: getattr(inp, n) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
     g = {n: t.to(DEV) for n, t in d.items()}
     state = inp.state.to(DEV).clone()
     idx = None if inp.indices is None else inp.indices.to(DEV)
     o = binding.gdn_decode(g["q"], g["k"], g["v"], g["a"], g["b"], g["A_log"], g["dt_bias"], state,
-                           idx, scale=inp.scale, use_qk_l2norm=use_norm)
+                           idx, scale=inp.scale, use_qk_l2norm=use_norm, softplus_beta=sp_beta,
+                           softplus_threshold=sp_thr)
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.gdn_decode(inp.q, inp.k, inp.v, inp.a, inp.b, inp.A_log, inp.dt_bias,
                                      inp.state, indices=inp.indices, scale=inp.scale,
+                                     softplus_beta=sp_beta, softplus_threshold=sp_thr,
                                      use_qk_l2norm=use_norm, batches=batches, round_state=False)
     return o.cpu(), state.cpu(), o_ref, s_ref
 
@@ -119,3 +121,27 @@ def test_decode_empty_batch():
                            inp.dt_bias.to(DEV), state)
     torch.cuda.synchronize()
     assert o.shape[0] == 0
+
+
+@pytest.mark.parametrize("sp_beta", [1.0, 2.0])
+@pytest.mark.parametrize("T", [1, 3])
+def test_decode_softplus_threshold(T, sp_beta):
+    """Gate inputs on both sides of the softplus threshold: per v-head,
+    dt_bias puts softplus_beta * (a + dt_bias) well above, just above, just
+    below and well below the threshold of 20 (a ~ N(0, 1) in bf16), in the
+    per-token kernel (T = 1) and the closed-form kernel (T = 3); softplus_beta
+    = 2 moves the switch to x = 10.  Small A_log keeps the decay of the
+    linear branch (g = -exp(A_log) * x) inside fp32 range."""
+    print(f"decode softplus T={T} sp_beta={sp_beta}", flush=True)
+    inp = workloads.make_decode(5, T, 2, 8, 128, 128, seed=90 + T)
+    thr_x = 20.0 / sp_beta
+    inp.dt_bias = torch.tensor([thr_x + d for d in (6.0, 1.5, 0.25, -0.25, -1.5, -6.0, 0.0, -thr_x)],
+                               dtype=torch.float32)
+    inp.A_log = torch.full((8,), -3.0, dtype=torch.float32)
+    x = inp.a.float() + inp.dt_bias
+    above = (sp_beta * x > 20.0).float().mean().item()
+    assert 0.2 < above < 0.8, f"threshold not straddled ({above:.2f} above)"
+    o, s, o_ref, s_ref = _run(inp, sp_beta=sp_beta)
+    check("o", o, o_ref, torch.bfloat16)
+    check("state", s, s_ref, torch.bfloat16)
+    _ulp_consistent(s, s_ref)

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from gated_delta_rule_61_amd import binding, workloads
-from tests.tolerance import check
+from tests.tolerance import STATE_SCAN_REL, check
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -29,25 +29,35 @@ def _gates(inp, gate, rng):
     return g, gamma, gk, gv
 
 
-def _case(inp, gate, S, seed=0):
+def _rel(t):
+    """fp32-stored states: the state scans' tight bar; bf16-stored: the bf16 bar."""
+    return STATE_SCAN_REL if t.dtype == torch.float32 else None
+
+
+def _case(inp, gate, S, seed=0, fp32_states=False):
     rng = np.random.default_rng(seed)
     g, gamma, gk, gv = _gates(inp, gate, rng)
-    print(f"fwd h {inp.name} gate={gate} split={S} dims={inp.dims} h0={inp.h0 is not None}", flush=True)
+    print(f"fwd h {inp.name} gate={gate} split={S} dims={inp.dims} h0={inp.h0 is not None} "
+          f"fp32 states={fp32_states}", flush=True)
     h, ht = binding.chunk_fwd_h(dv(inp.k), dv(inp.v), g=dv(g), g_gamma=dv(gamma), gk=dv(gk), gv=dv(gv),
-                                h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens), split_size=S)
+                                h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens), split_size=S,
+                                states_in_fp32=fp32_states, cu_seqlens_cpu=inp.cu_seqlens)
     torch.cuda.synchronize()
+    assert h.dtype == (torch.float32 if fp32_states else torch.bfloat16)
     h_ref, ht_ref = oracle.state_scan(inp.k, inp.v, g=g, g_gamma=gamma, gk=gk, gv=gv, h0=inp.h0,
                                       cu_seqlens=inp.cu_seqlens, split_size=S)
     assert h.shape == h_ref.shape
-    print("  h", check("h", h.cpu(), h_ref, torch.bfloat16),
-          " ht", check("ht", ht.cpu(), ht_ref, torch.bfloat16), flush=True)
+    h = h.cpu()
+    print("  h", check("h", h, h_ref, torch.bfloat16, rel=_rel(h)),
+          " ht", check("ht", ht.cpu(), ht_ref, torch.bfloat16, rel=STATE_SCAN_REL), flush=True)
 
 
+@pytest.mark.parametrize("fp32_states", [False, True])
 @pytest.mark.parametrize("gate", ["gdn", "gamma", None, "gv", "gdn+gv", "gamma+gv"])
-def test_fwd_h_varlen_gqa(gate):
+def test_fwd_h_varlen_gqa(gate, fp32_states):
     inp = workloads.make_prefill(1, 331, 2, 4, 128, 128, dtype=torch.bfloat16, seed=70, h0=True,
                                  seqlens=[200, 1, 0, 130], name="fwd_h_varlen")
-    _case(inp, gate, 64, seed=71)
+    _case(inp, gate, 64, seed=71, fp32_states=fp32_states)
 
 
 @pytest.mark.parametrize("gate", ["gdn", "gv", "gdn+gv", "kda"])
@@ -57,10 +67,11 @@ def test_fwd_h_k64(gate):
     _case(inp, gate, 128, seed=73)
 
 
-def test_fwd_h_kda_k128_varlen():
+@pytest.mark.parametrize("fp32_states", [False, True])
+def test_fwd_h_kda_k128_varlen(fp32_states):
     inp = workloads.make_prefill(1, 200, 2, 2, 128, 128, dtype=torch.bfloat16, seed=74, gate="kda", h0=True,
                                  seqlens=[64, 136], name="fwd_h_kda_K128")
-    _case(inp, "kda", 64, seed=75)
+    _case(inp, "kda", 64, seed=75, fp32_states=fp32_states)
 
 
 def test_fwd_h_final_state_only():
@@ -69,7 +80,7 @@ def test_fwd_h_final_state_only():
     torch.cuda.synchronize()
     assert h is None
     _, ht_ref = oracle.state_scan(inp.k, inp.v, g=inp.g, h0=inp.h0)
-    check("ht", ht.cpu(), ht_ref, torch.bfloat16)
+    check("ht", ht.cpu(), ht_ref, torch.bfloat16, rel=STATE_SCAN_REL)
 
 
 def test_fwd_h_b4_t4096_sampled_heads():
@@ -78,12 +89,12 @@ def test_fwd_h_b4_t4096_sampled_heads():
     inp = workloads.gdn_bf16_b4_t4096()
     heads = [0, 13]
     print(f"fwd h full size heads={heads}", flush=True)
-    h, ht = binding.chunk_fwd_h(dv(inp.k), dv(inp.v), g=dv(inp.g), split_size=64)
+    h, ht = binding.chunk_fwd_h(dv(inp.k), dv(inp.v), g=dv(inp.g), split_size=64, states_in_fp32=True)
     torch.cuda.synchronize()
     # Hk = HV here: v-head h reads k head h
     h_ref, ht_ref = oracle.state_scan(inp.k[:, :, heads], inp.v[:, :, heads], g=inp.g[:, :, heads], split_size=64)
-    check("h", h.cpu()[:, heads], h_ref, torch.bfloat16)
-    check("ht", ht.cpu()[:, heads], ht_ref, torch.bfloat16)
+    check("h", h.cpu()[:, heads], h_ref, torch.bfloat16, rel=STATE_SCAN_REL)
+    check("ht", ht.cpu()[:, heads], ht_ref, torch.bfloat16, rel=STATE_SCAN_REL)
 
 
 @pytest.mark.parametrize("gate", ["gamma+gv", "kda"])
@@ -92,3 +103,37 @@ def test_fwd_h_split_of_three_chunks(gate):
     inp = workloads.make_prefill(1, 455, 1, 2, 64, 64, dtype=torch.bfloat16, seed=77, h0=True,
                                  gate="kda" if gate == "kda" else "gdn", seqlens=[390, 0, 65], name="fwd_h_split192")
     _case(inp, gate, 192, seed=78)
+
+
+def test_fwd_h_b4_t4096_bf16_states_sampled_heads():
+    """The same shape with the page's default storage (states in the input
+    dtype, bf16): two sampled heads."""
+    inp = workloads.gdn_bf16_b4_t4096()
+    heads = [5, 10]
+    print(f"fwd h full size bf16 states heads={heads}", flush=True)
+    h, ht = binding.chunk_fwd_h(dv(inp.k), dv(inp.v), g=dv(inp.g), split_size=64)
+    torch.cuda.synchronize()
+    assert h.dtype == torch.bfloat16
+    h_ref, ht_ref = oracle.state_scan(inp.k[:, :, heads], inp.v[:, :, heads], g=inp.g[:, :, heads], split_size=64)
+    check("h", h.cpu()[:, heads], h_ref, torch.bfloat16)
+    check("ht", ht.cpu()[:, heads], ht_ref, torch.bfloat16, rel=STATE_SCAN_REL)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda", "gamma+gv"])
+def test_fwd_h_grouped_gate_heads(gate):
+    """Gates of Hg = 2 heads shared by HV = 4 v-heads (gate head j // 2)."""
+    inp = workloads.make_prefill(1, 300, 4, 4, 64, 64, dtype=torch.bfloat16, seed=81, h0=True,
+                                 gate="kda" if gate == "kda" else "gdn", seqlens=[170, 130], name="fwd_h_grouped")
+    rng = np.random.default_rng(82)
+    g, gamma, gk, gv = _gates(inp, gate, rng)
+    cut = lambda x, ax: None if x is None else x.narrow(ax, 0, 2).contiguous()
+    g, gk, gv, gamma = cut(g, 2), cut(gk, 2), cut(gv, 2), cut(gamma, 0)
+    print(f"fwd h grouped gates {gate}", flush=True)
+    h, ht = binding.chunk_fwd_h(dv(inp.k), dv(inp.v), g=dv(g), g_gamma=dv(gamma), gk=dv(gk), gv=dv(gv),
+                                h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens), split_size=128,
+                                states_in_fp32=True, cu_seqlens_cpu=inp.cu_seqlens)
+    torch.cuda.synchronize()
+    h_ref, ht_ref = oracle.state_scan(inp.k, inp.v, g=g, g_gamma=gamma, gk=gk, gv=gv, h0=inp.h0,
+                                      cu_seqlens=inp.cu_seqlens, split_size=128)
+    check("h", h.cpu(), h_ref, torch.bfloat16, rel=STATE_SCAN_REL)
+    check("ht", ht.cpu(), ht_ref, torch.bfloat16, rel=STATE_SCAN_REL)

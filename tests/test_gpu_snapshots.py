@@ -15,11 +15,12 @@ DEV = "cuda:0"
 dv = lambda t: None if t is None else t.to(DEV)
 
 
-def _gdn(inp, S):
-    print(f"snapshots GDN {inp.name} dims={inp.dims} split={S}", flush=True)
+def _gdn(inp, S, fp32_states=False):
+    print(f"snapshots GDN {inp.name} dims={inp.dims} split={S} fp32 states={fp32_states}", flush=True)
     o, ht, hs = binding.gdn_chunk_fwd(dv(inp.q), dv(inp.k), dv(inp.v), dv(inp.g), dv(inp.beta),
                                       scale=inp.scale, h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens),
-                                      split_size=S)
+                                      split_size=S, states_in_fp32=fp32_states, cu_seqlens_cpu=inp.cu_seqlens)
+    assert hs.dtype == (torch.float32 if fp32_states or inp.q.dtype == torch.float32 else torch.bfloat16)
     torch.cuda.synchronize()
     o_ref, ht_ref, hs_ref = oracle.gdn_recurrent(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale,
                                                  h0=inp.h0, cu_seqlens=inp.cu_seqlens, split_size=S)
@@ -30,11 +31,12 @@ def _gdn(inp, S):
     print("  h_snap", check("h_snap", hs.cpu(), hs_ref, dt), flush=True)
 
 
-def _kda(inp, S):
-    print(f"snapshots KDA {inp.name} dims={inp.dims} split={S}", flush=True)
+def _kda(inp, S, fp32_states=False):
+    print(f"snapshots KDA {inp.name} dims={inp.dims} split={S} fp32 states={fp32_states}", flush=True)
     o, ht, _, _, hs = binding.kda_chunk_fwd(dv(inp.q), dv(inp.k), dv(inp.v), dv(inp.gk), dv(inp.beta),
                                             scale=inp.scale, h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens),
-                                            return_intra=False, split_size=S)
+                                            return_intra=False, split_size=S, states_in_fp32=fp32_states,
+                                            cu_seqlens_cpu=inp.cu_seqlens)
     torch.cuda.synchronize()
     o_ref, ht_ref, hs_ref = oracle.kda_recurrent(inp.q, inp.k, inp.v, inp.gk, inp.beta, inp.scale,
                                                  h0=inp.h0, cu_seqlens=inp.cu_seqlens, split_size=S)
@@ -44,11 +46,12 @@ def _kda(inp, S):
     print("  h_snap", check("h_snap", hs.cpu(), hs_ref, dt), flush=True)
 
 
+@pytest.mark.parametrize("fp32_states", [False, True])
 @pytest.mark.parametrize("S", [64, 128])
-def test_gdn_bf16_varlen_snapshots(S):
+def test_gdn_bf16_varlen_snapshots(S, fp32_states):
     inp = workloads.make_prefill(1, 400, 2, 4, 128, 128, dtype=torch.bfloat16, seed=S, h0=True,
                                  seqlens=[130, 64, 1, 205], name="bf16_varlen")
-    _gdn(inp, S)
+    _gdn(inp, S, fp32_states)
 
 
 def test_gdn_bf16_fixed_snapshots_every_chunk():
@@ -63,11 +66,12 @@ def test_gdn_fp32_snapshots():
     _gdn(inp, 64)
 
 
+@pytest.mark.parametrize("fp32_states", [False, True])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_kda_snapshots(dtype):
+def test_kda_snapshots(dtype, fp32_states):
     inp = workloads.make_prefill(1, 260, 2, 2, 128, 128, dtype=dtype, seed=7, gate="kda", h0=True,
                                  seqlens=[70, 190], name=f"kda_{dtype}")
-    _kda(inp, 128 if dtype == torch.bfloat16 else 64)
+    _kda(inp, 128 if dtype == torch.bfloat16 else 64, fp32_states)
 
 
 def test_snapshot_buffer_untouched_without_snapshots():
@@ -100,10 +104,31 @@ def test_snapshots_b4_t4096_sampled_heads():
     heads = [3, 12]
     print(f"snapshots full size heads={heads}", flush=True)
     o, ht, hs = binding.gdn_chunk_fwd(dv(inp.q), dv(inp.k), dv(inp.v), dv(inp.g), dv(inp.beta),
-                                      scale=inp.scale, split_size=64)
+                                      scale=inp.scale, split_size=64, states_in_fp32=True)
     torch.cuda.synchronize()
     _, ht_ref, hs_ref = oracle.gdn_recurrent(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale,
                                              heads=heads, split_size=64)
     hs = hs.cpu()
     print("  h_snap", check("h_snap", hs[:, heads], hs_ref[:, heads], torch.bfloat16), flush=True)
     check("ht", ht.cpu()[:, heads], ht_ref[:, heads], torch.bfloat16)
+
+
+def test_snapshot_capacity_bounds_varlen_writes():
+    """A varlen call whose snapshot buffer holds fewer entries than the call
+    has: the entries within the capacity are the oracle's, the guard rows
+    after them are untouched (no write past the capacity)."""
+    inp = workloads.make_prefill(1, 400, 2, 4, 64, 64, dtype=torch.bfloat16, seed=11, h0=True,
+                                 seqlens=[130, 64, 1, 205], name="bf16_varlen_cap")
+    S, cap = 64, 5                   # the call has 3 + 1 + 1 + 4 = 9 snapshots
+    buf = torch.full((cap + 3, 4, 64, 64), 7.0, dtype=torch.float32, device=DEV)
+    print("snapshot capacity", flush=True)
+    o, ht, hs = binding.gdn_chunk_fwd(dv(inp.q), dv(inp.k), dv(inp.v), dv(inp.g), dv(inp.beta),
+                                      scale=inp.scale, h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens),
+                                      split_size=S, h_snap=buf[:cap], states_in_fp32=True)
+    torch.cuda.synchronize()
+    _, _, hs_ref = oracle.gdn_recurrent(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, h0=inp.h0,
+                                        cu_seqlens=inp.cu_seqlens, split_size=S)
+    assert hs_ref.shape[0] == 9
+    got = buf.cpu()
+    check("h_snap", got[:cap], hs_ref[:cap], torch.bfloat16)
+    assert torch.all(got[cap:] == 7.0), "entries past the capacity were written"

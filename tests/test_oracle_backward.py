@@ -54,6 +54,8 @@ def _autograd_grad(q, do, g, gk, gamma, dht, scale, b, bos, eos, start, j, kh, r
         loss = loss + o @ torch.from_numpy(do[b, t, j])
     if dht is not None:
         loss = loss + (S * torch.from_numpy(dht)).sum()
+    if not loss.requires_grad:        # no token after `start` and no dht: the gradient is 0
+        return np.zeros((V, K))
     loss.backward()
     return S0.grad.numpy()
 
@@ -87,12 +89,13 @@ def test_state_grad_matches_autograd(gate):
 MUTATIONS = [
     ("""                    D = D + scale * np.outer(dout[b, t, j], q[b, t, kh])
                     if g is not None:
-                        D = D * np.exp(g[b, t, j])""", """                    if g is not None:
-                        D = D * np.exp(g[b, t, j])
+                        D = D * np.exp(g[b, t, jg])""", """                    if g is not None:
+                        D = D * np.exp(g[b, t, jg])
                     D = D + scale * np.outer(dout[b, t, j], q[b, t, kh])"""),   # decay before the output term
     ("D = D + scale * np.outer(dout[b, t, j], q[b, t, kh])", "D = D + np.outer(dout[b, t, j], q[b, t, kh])"),  # scale dropped
     ("seq_snaps[ic // r][j] = D", "seq_snaps[ic // r][j] = D * 0 + dh0[n, j]"),  # snapshot of the wrong state
-    ("D = D * np.exp(gv[b, t, j])[:, None]", "D = D * np.exp(gv[b, t, j])[None, :]"),     # gv on the key axis
+    ("D = D * np.exp(gv[b, t, jg])[:, None]", "D = D * np.exp(gv[b, t, jg])[None, :]"),   # gv on the key axis
+    ("jg = j // (HV // Hg)", "jg = j % Hg"),                                                # wrong gate-head map
 ]
 
 
@@ -104,11 +107,43 @@ def test_state_grad_mutant_is_caught(old, new):
     m = types.ModuleType("bwd_mutant")
     exec(compile(src, "<mutant>", "exec"), m.__dict__)
     rng = np.random.default_rng(51)
-    q, do, g, gk, gamma, gv = _problem(rng, 1, 6, 1, 1, 3, 3, "gdn+gv")   # K = V: a wrong axis still runs
+    # K = V: a wrong axis still runs; HV = 4 query / output heads share the
+    # gates of Hg = 2 heads (the page's grouped form), so a wrong map shows
+    q, do, g, gk, gamma, gv = _problem(rng, 1, 6, 4, 4, 3, 3, "gdn+gv")
+    g, gv = g[:, :, :2], gv[:, :, :2]
+    eg, egv = np.repeat(g, 2, axis=2), np.repeat(gv, 2, axis=2)
     dh, dh0 = m.state_grad_scan(q, do, 0.7, g=g, gv=gv, split_size=2, chunk_size=2)
-    ok = np.allclose(dh0[0, 0], _autograd_grad(q, do, g, None, None, None, 0.7, 0, 0, 6, 0, 0, 0, rng, gv=gv),
-                     atol=1e-12)
-    ok = ok and all(np.allclose(dh[s, 0], _autograd_grad(q, do, g, None, None, None, 0.7, 0, 0, 6,
-                                                           min(2 * s + 2, 6), 0, 0, rng, gv=gv), atol=1e-12)
-                    for s in range(3))
+    ok = True
+    for j in range(4):
+        ok = ok and np.allclose(dh0[0, j], _autograd_grad(q, do, eg, None, None, None, 0.7, 0, 0, 6, 0, j, j, rng,
+                                                          gv=egv), atol=1e-12)
+        ok = ok and all(np.allclose(dh[s, j], _autograd_grad(q, do, eg, None, None, None, 0.7, 0, 0, 6,
+                                                               min(2 * s + 2, 6), j, j, rng, gv=egv), atol=1e-12)
+                        for s in range(3))
     assert not ok
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda", "gamma", "gdn+gv"])
+def test_state_grad_grouped_gate_heads(gate):
+    """The page's grouped form of chunk_bwd_kernel_dh: HQ = 4 query / output
+    heads (q and dO per query head, one gradient each) read the gates of
+    head i_hq // NG, NG = 2.  Pinned by autograd with the gates repeated per
+    query head."""
+    rng = np.random.default_rng(52)
+    B, T, HQ, NG, K, V, C = 1, 9, 4, 2, 4, 3, 4
+    q, do, g, gk, gamma, gv = _problem(rng, B, T, HQ, HQ, K, V, gate)
+    H = HQ // NG
+    cut = lambda x, ax: None if x is None else np.take(x, range(H), axis=ax)
+    g, gk, gv, gamma = cut(g, 2), cut(gk, 2), cut(gv, 2), cut(gamma, 0)
+    rep = lambda x, ax: None if x is None else np.repeat(x, NG, axis=ax)
+    eg, egk, egv, egam = rep(g, 2), rep(gk, 2), rep(gv, 2), rep(gamma, 0)
+    dht = rng.standard_normal((1, HQ, V, K))
+    dh, dh0 = oracle.state_grad_scan(q, do, 0.7, g=g, g_gamma=gamma, gk=gk, gv=gv, dht=dht,
+                                     split_size=C, chunk_size=C)
+    for j in range(HQ):
+        np.testing.assert_allclose(dh0[0, j], _autograd_grad(q, do, eg, egk, egam, dht[0, j], 0.7, 0, 0, T, 0, j, j,
+                                                             rng, gv=egv), atol=1e-12)
+        for s in range(-(-T // C)):
+            end = min((s + 1) * C, T)
+            np.testing.assert_allclose(dh[s, j], _autograd_grad(q, do, eg, egk, egam, dht[0, j], 0.7, 0, 0, T, end,
+                                                                j, j, rng, gv=egv), atol=1e-12)

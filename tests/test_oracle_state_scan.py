@@ -101,10 +101,10 @@ def test_state_scan_no_gate_is_matrix_product():
 
 MUTATIONS = [
     ("""                    if g is not None:
-                        S = S * np.exp(g[b, t, j])
+                        S = S * np.exp(g[b, t, jg])
                     if gk""", """                    if gk"""),                                       # scalar gate dropped
-    ("S = S * np.exp(gv[b, t, j])[:, None]", "S = S * np.exp(gv[b, t, j])[None, :]"),           # gv on the key axis
-    ("S = S + np.outer(v[b, t, j], k[b, t, kh])", "S = S + np.outer(v[b, t, j], k[b, t, kh]) * np.exp(g[b, t, j])"),
+    ("S = S * np.exp(gv[b, t, jg])[:, None]", "S = S * np.exp(gv[b, t, jg])[None, :]"),         # gv on the key axis
+    ("S = S + np.outer(v[b, t, j], k[b, t, kh])", "S = S + np.outer(v[b, t, j], k[b, t, kh]) * np.exp(g[b, t, jg])"),
     ("seq_snaps[ic // r][j] = S", "seq_snaps[ic // r][j] = S * np.exp(g[b, bos, j])"),         # wrong snapshot
 ]
 
@@ -127,3 +127,61 @@ def test_state_scan_mutant_is_caught(old, new):
     ok = ok and all(np.allclose(h[s, 0], _closed_form(k, v, g, None, None, gv, h0[0, 0], 0, 0, 2 * s, 0, 0),
                                 atol=1e-12) for s in range(4))
     assert not ok
+
+
+def _grouped_problem(rng, forms):
+    """Gates with fewer heads than v (Hg = 2 of HV = 4), k per v-head."""
+    Hk, HV, Hg, K, V = 4, 4, 2, 4, 3
+    lens = [9, 5]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    k = rng.standard_normal((1, T, Hk, K))
+    v = rng.standard_normal((1, T, HV, V))
+    g, gamma, gk, gv = _gates(rng, 1, T, Hg, K, V, forms)
+    h0 = rng.standard_normal((len(lens), HV, V, K))
+    return lens, cu, k, v, (g, gamma, gk, gv), h0, HV // Hg
+
+
+def _expand(gates, r):
+    """The same gates repeated per v-head (head j gets gate head j // r)."""
+    g, gamma, gk, gv = gates
+    rep = lambda x, ax: None if x is None else np.repeat(x, r, axis=ax)
+    return rep(g, 2), rep(gamma, 0), rep(gk, 2), rep(gv, 2)
+
+
+@pytest.mark.parametrize("forms", [("g",), ("gamma", "gv"), ("gk",)])
+def test_state_scan_grouped_gate_heads(forms):
+    """The page's grouped form: v-head j takes gate head j // (HV / Hg).
+    Checked against the closed form with the gates repeated per head."""
+    rng = np.random.default_rng(63)
+    lens, cu, k, v, gates, h0, r = _grouped_problem(rng, forms)
+    g, gamma, gk, gv = gates
+    h, ht = oracle.state_scan(k, v, g=g, g_gamma=gamma, gk=gk, gv=gv, h0=h0, cu_seqlens=cu,
+                              split_size=4, chunk_size=4)
+    eg, egam, egk, egv = _expand(gates, r)
+    i = 0
+    for n, L in enumerate(lens):
+        bos, eos = int(cu[n]), int(cu[n + 1])
+        for j in range(4):
+            np.testing.assert_allclose(ht[n, j], _closed_form(k, v, eg, egam, egk, egv, h0[n, j], 0, bos, eos, j, j),
+                                       rtol=1e-12, atol=1e-12)
+            for s in range(-(-L // 4)):
+                np.testing.assert_allclose(h[i + s, j], _closed_form(k, v, eg, egam, egk, egv, h0[n, j], 0, bos,
+                                                                     bos + 4 * s, j, j), rtol=1e-12, atol=1e-12)
+        i += -(-L // 4)
+
+
+def test_state_scan_grouped_gate_mutant_is_caught():
+    """A wrong gate-head map (j % Hg instead of j // (HV / Hg)) fails the pin."""
+    src = inspect.getsource(ss)
+    old = "jg = j // (HV // Hg)"
+    assert old in src
+    src = src.replace(old, "jg = j % Hg", 1).replace("from .recurrence import", "from oracle.recurrence import")
+    m = types.ModuleType("ss_mutant")
+    exec(compile(src, "<mutant>", "exec"), m.__dict__)
+    rng = np.random.default_rng(64)
+    lens, cu, k, v, gates, h0, r = _grouped_problem(rng, ("g",))
+    _, ht = m.state_scan(k, v, g=gates[0], h0=h0, cu_seqlens=cu, chunk_size=4)
+    eg = _expand(gates, r)[0]
+    assert not all(np.allclose(ht[0, j], _closed_form(k, v, eg, None, None, None, h0[0, j], 0, 0, 9, j, j),
+                               atol=1e-12) for j in range(4))
