@@ -42,6 +42,11 @@ _SIGNATURES = {
                                _c_void_p, _c_void_p, _c_void_p, _c_int, _c_ll, _c_int, _c_void_p, _c_int,
                                _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "gdn_chunk_fwd_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                       _c_float, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_ll, _c_int,
+                                       _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, _c_void_p, _c_void_p]),
+    "gdn_chunk_fwd_noalloc_max_bytes": (_c_size_t, []),
     "gdn_profile_enable": (_c_int, [_c_int]),
     "gdn_profile_read": (_c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int)]),
     "gdn_decode": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -248,6 +253,43 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
                                B, T, Hk, HV, K, V, chunk_size, _io_code(io),
                                _ptr(o), _ptr(workspace), workspace.numel(), _stream(dev)))
     return (o, ht) if hs is None else (o, ht, hs)
+
+
+def gdn_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
+                          beta: torch.Tensor, out: torch.Tensor, ht: Optional[torch.Tensor] = None,
+                          scale: Optional[float] = None, h0: Optional[torch.Tensor] = None,
+                          cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                          split_size: Optional[int] = None, h_snap: Optional[torch.Tensor] = None,
+                          g_gamma: Optional[torch.Tensor] = None) -> None:
+    """``gdn_chunk_fwd`` through the library's no-allocation entry point: the
+    caller passes every output (``out`` [B,T,HV,V], optional ``ht`` [N,HV,V,K]
+    fp32 and ``h_snap`` with its ``split_size``; the snapshot dtype is
+    ``h_snap``'s), and no workspace: the library uses its own per-GPU scratch
+    (``noalloc_max_bytes()``).  Allocates nothing."""
+    B, T, Hk, HV, K, V, N, dev, io = _chunk_common(q, k, v, beta, h0, cu_seqlens, chunk_size, g, (), "g")
+    if g_gamma is not None:
+        _need(g_gamma, "g_gamma", torch.float32, (HV,), dev)
+    _need(out, "out", io, (B, T, HV, V), dev)
+    _need(ht, "ht", torch.float32, (N, HV, V, K), dev)
+    if h_snap is not None:
+        if split_size is None or split_size <= 0 or split_size % 64:
+            raise ValueError("h_snap needs split_size, a positive multiple of 64")
+        if h_snap.dim() != 4 or h_snap.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("h_snap must be [S, HV, V, K] fp32 or bf16")
+        _need(h_snap, "h_snap", h_snap.dtype, (h_snap.shape[0], HV, V, K), dev)
+    if scale is None:
+        scale = K ** -0.5
+    _check(lib().gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma), _ptr(beta), float(scale),
+                                       _ptr(h0), _ptr(ht), _ptr(h_snap), split_size or 0,
+                                       0 if h_snap is None else h_snap.shape[0],
+                                       GDN_DTYPE_F32 if h_snap is None else _dtype_code(h_snap.dtype),
+                                       _ptr(cu_seqlens), N, B, T, Hk, HV, K, V, chunk_size, _io_code(io),
+                                       _ptr(out), _stream(dev)))
+
+
+def noalloc_max_bytes() -> int:
+    """Scratch bytes of the no-allocation entry point (per GPU)."""
+    return int(lib().gdn_chunk_fwd_noalloc_max_bytes())
 
 
 def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gk: torch.Tensor,

@@ -340,10 +340,75 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   a.GF = ws + L.gf_off;
   a.chunk_off = cu_seqlens ? (int32_t*)(ws + L.coff_off) : nullptr;
   a.seq_order = cu_seqlens ? (int32_t*)(ws + L.order_off) : nullptr;
-  a.max_chunks = (T + 63) / 64 + (cu_seqlens ? P.N : 0);
+  a.max_chunks = (T + 63) / 64 * B + (cu_seqlens ? P.N : 0);
   const hipError_t e = launch_chunk_fwd(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ no-allocation prefill entry
+namespace {
+// Scratch of gdn_chunk_fwd_noalloc: the workspace of gdn_chunk_fwd, one copy
+// per GPU, held until the process ends.  On the host this name is only a
+// stand-in, never an address: host code uses the per-device address that
+// scratch_address() looks up.
+constexpr size_t kScratchBytes = (size_t)96 << 20;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device of `stream` (which must be the
+// current device), looked up once per device.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "stream belongs to device %d, the current device is %d", (int)sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GDN_ERR_UNSUPPORTED, "device %d is beyond the %d devices the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GDN_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t gdn_chunk_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                          const float* g_gamma, const float* beta, float scale, const float* h0, float* ht,
+                          void* h_snap, int split_size, long long snap_entries, int state_dtype,
+                          const int64_t* cu_seqlens,
+                          int num_seqs, int B, int T, int Hk, int HV, int K, int V, int chunk_size,
+                          int dtype, void* o, void* stream) {
+  const size_t need = gdn_chunk_fwd_workspace_bytes(B, T, Hk, HV, K, V, num_seqs, dtype);
+  if (need > kScratchBytes)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "the call needs %zu bytes of scratch; the no-allocation entry point holds %zu (use gdn_chunk_fwd "
+                "with a workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  const int st = scratch_address((hipStream_t)stream, &ws);
+  if (st != GDN_OK) return st;
+  return gdn_chunk_fwd(q, k, v, g, g_gamma, beta, scale, h0, ht, h_snap, split_size, snap_entries, state_dtype,
+                       cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size, dtype, o, ws, kScratchBytes, stream);
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* gk, const float* beta,

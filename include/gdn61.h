@@ -158,6 +158,29 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v,
                   void* stream);
 
 /*
+ * gdn_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * errors as gdn_chunk_fwd; the workspace is a scratch array inside the
+ * library (one per GPU, gdn_chunk_fwd_noalloc_max_bytes() = 96 MiB, held
+ * until the process ends; looked up once per device, on the first call).
+ * A call needing more (gdn_chunk_fwd_workspace_bytes() > that) returns
+ * GDN_ERR_UNSUPPORTED and queues nothing.  `stream` must belong to the
+ * current device.  Every call on a GPU shares that GPU's scratch, so calls
+ * that overlap on one GPU (different streams, or host threads) race; calls
+ * in one stream are ordered.  Calls no hipMalloc, hipFree or allocating
+ * library routine.
+ */
+size_t gdn_chunk_fwd_noalloc_max_bytes(void);
+int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                          const float* g, const float* g_gamma, const float* beta, float scale,
+                          const float* h0, float* ht,
+                          void* h_snap, int split_size, long long snap_entries, int state_dtype,
+                          const int64_t* cu_seqlens, int num_seqs,
+                          int B, int T, int Hk, int HV, int K, int V,
+                          int chunk_size, int dtype, void* o, void* stream);
+
+/*
  * KDA chunked prefill forward (one log-gate per key channel).
  *
  * As gdn_chunk_fwd, with
