@@ -200,10 +200,12 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       // (entries past the buffer's capacity are not written)
       if (hs && c % nts == 0 && (long long)(sbase + c / nts) < scap) {
         const size_t hp = ((sbase + c / nts) * HV + j) * (size_t)V * DK + (size_t)(v0 + 16 * cb + n) * DK;
+        // blocks 2m and 2m + 1 hold keys 32 m + 8 g + [0, 8) of this lane's row
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const float x[4] = {St[kb][0], St[kb][1], St[kb][2], St[kb][3]};
-          store_state4(hs, hp + perm_row(kb, 4 * g), x, sbf16 != 0);
+        for (int kb = 0; kb < KB; kb += 2) {
+          const float x[8] = {St[kb][0], St[kb][1], St[kb][2], St[kb][3],
+                              St[kb + 1][0], St[kb + 1][1], St[kb + 1][2], St[kb + 1][3]};
+          store_state8(hs, hp + perm_row(kb, 4 * g), x, sbf16 != 0);
         }
       }
       const char* sAi = S1 ? sAi1 : sAi0;

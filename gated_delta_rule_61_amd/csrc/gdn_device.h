@@ -70,6 +70,20 @@ __device__ __forceinline__ void store_state4(void* base, size_t off, const float
     store_nt16(reinterpret_cast<float*>(base) + off, f4{x[0], x[1], x[2], x[3]});
   }
 }
+// Eight consecutive fp32 state values at element `off`: one 16-byte store in
+// bf16 (a full 16-byte unit per lane, so that four lanes on one row fill a
+// 64-byte segment), two in fp32.
+__device__ __forceinline__ void store_state8(void* base, size_t off, const float (&x)[8], bool bf16) {
+  if (bf16) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    store_nt16(reinterpret_cast<bf16_t*>(base) + off,
+               u4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])});
+  } else {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    store_nt16(reinterpret_cast<float*>(base) + off, f4{x[0], x[1], x[2], x[3]});
+    store_nt16(reinterpret_cast<float*>(base) + off + 4, f4{x[4], x[5], x[6], x[7]});
+  }
+}
 
 // ------------------------------------------------------- 16-lane reductions
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the total.

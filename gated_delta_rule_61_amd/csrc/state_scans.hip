@@ -82,6 +82,41 @@ __device__ __forceinline__ void transpose8(const uint4 (&R)[8], uint4 (&O)[8]) {
   }
 }
 
+// A work-group's accumulators into a [*, HV, V, K] state array: lane (n, gq)
+// of a wave holds keys 16 rb + 4 gq + [0, 4) of the wave's key range in
+// column 16 cb + n; `base` is the element of (column n, first key of the
+// range).  With two 16-key blocks and bf16 storage, lanes gq and gq ^ 1 (lane
+// ^ 16) first trade one 4-key half, so that each lane stores 8 consecutive
+// keys in one 16-byte store and the four lanes of a column fill 64 contiguous
+// bytes (instead of 32-byte pieces).
+template <int DK, int RB>
+__device__ __forceinline__ void store_tile(void* dst, size_t base, const f32x4 (&acc)[RB][CBN], int gq, bool bf) {
+#pragma unroll
+  for (int cb = 0; cb < CBN; ++cb) {
+    const size_t row = base + (size_t)16 * cb * DK;
+    if constexpr (RB == 2) {
+      if (bf) {
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+        const bool odd = gq & 1;
+        const uint32_t a0 = pack_bf2(acc[0][cb][0], acc[0][cb][1]), a1 = pack_bf2(acc[0][cb][2], acc[0][cb][3]);
+        const uint32_t b0 = pack_bf2(acc[1][cb][0], acc[1][cb][1]), b1 = pack_bf2(acc[1][cb][2], acc[1][cb][3]);
+        // even gq keeps block 0 and takes the partner's block-0 keys 4 gq + [4, 8);
+        // odd gq keeps block 1 and takes the partner's block-1 keys 16 + 4 (gq - 1) + [0, 4)
+        const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? a0 : b0), 16);
+        const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? a1 : b1), 16);
+        const u4 v = odd ? u4{r0, r1, b0, b1} : u4{a0, a1, r0, r1};
+        store_nt16(reinterpret_cast<bf16_t*>(dst) + row + (odd ? 16 + 4 * (gq - 1) : 4 * gq), v);
+        continue;
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float x[4] = {acc[rb][cb][0], acc[rb][cb][1], acc[rb][cb][2], acc[rb][cb][3]};
+      store_state4(dst, row + 16 * rb + 4 * gq, x, bf);
+    }
+  }
+}
+
 // Per-key-channel gate (gk): the gated operand is the A side (q / k), one
 // thread per key channel forms the chunk-local cumulative gates in LDS, the
 // value side transposes raw; three barriers per chunk.
@@ -148,14 +183,7 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
     }
   // the state into a [*, HV, V, K] array at entry `e` (fp32, or bf16 when `bf`)
   auto store_state = [&](void* dst, size_t e, bool bf) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < CBN; ++cb) {
-        const float x[4] = {acc[rb][cb][0], acc[rb][cb][1], acc[rb][cb][2], acc[rb][cb][3]};
-        store_state4(dst, (e * HV + j) * (size_t)DV * DK + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq,
-                     x, bf);
-      }
+    store_tile<DK, RB>(dst, (e * HV + j) * (size_t)DV * DK + (size_t)(v0 + n) * DK + RW * w, acc, gq, bf);
   };
 
   // this thread's 8 x 8 block: q (waves 0 .. NQB / 64 - 1) or dO (the next
@@ -371,14 +399,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
     }
   // the state into a [*, HV, V, K] array at entry `e` (fp32, or bf16 when `bf`)
   auto store_state = [&](void* dst, size_t e, bool bf) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < CBN; ++cb) {
-        const float x[4] = {acc[rb][cb][0], acc[rb][cb][1], acc[rb][cb][2], acc[rb][cb][3]};
-        store_state4(dst, (e * HV + j) * (size_t)DV * DK + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq,
-                     x, bf);
-      }
+    store_tile<DK, RB>(dst, (e * HV + j) * (size_t)DV * DK + (size_t)(v0 + n) * DK + RW * w, acc, gq, bf);
   };
 
   // roles: the first QB / 64 waves -> q blocks; waves 2, 3 -> dO (columns
