@@ -24,6 +24,10 @@ implementation's intermediates):
 duration of the dominant kernel (library HIP events on the launch stream,
 inside the timed loop); ``roofline.call`` the same bytes over the whole call.
 
+Every timing starts with ~0.25 s of untimed back-to-back calls of the same
+step (``clock_settle_s``: the GPU clock ramps over the first ~30 ms of a
+burst), then the W warm-up calls, then the K timed calls.
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
 
@@ -84,8 +88,28 @@ def parse():
     return p.parse_args()
 
 
+CLOCK_SETTLE_S = 0.25
+
+
+def settle(fn, seconds=CLOCK_SETTLE_S):
+    """Untimed back-to-back calls for `seconds`: the GPU clock ramps up over
+    the first tens of milliseconds of a burst of work (the prefill call takes
+    ~20 % longer during the first ~30 ms), and every timing here is of the
+    steady state."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+        n += 8
+    return n
+
+
 def timed(fn, steps, warmup):
     import torch
+    settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -596,6 +620,7 @@ def main():
         "config": {"workload": "gdn_chunk_fwd B=4 T=4096 H=16 K=V=128 BT=64, bf16 q/k/v, fp32 g/beta/state, "
                                "zero h0, ht stored",
                    "global_batch": 4, "seq_len": 4096},
+        "clock_settle_s": CLOCK_SETTLE_S,
         "mfma_frac_method_flops": roof["call"]["mfma_frac_method_flops"],
         "cold_ms_per_step": None if pf["cold_ms"] is None else round(pf["cold_ms"], 5),
         "kernels_ms": {s: round(v, 5) for s, v in pf["stage_ms"].items()},
