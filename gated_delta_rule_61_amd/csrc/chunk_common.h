@@ -67,13 +67,16 @@ __device__ __forceinline__ bool locate_chunk(int c, const int64_t* __restrict__ 
 
 // Store the 64 x 64 fp32 LDS tile as rows of an [tokens, HV, 64] io-dtype
 // array (rows >= nrow skipped), 16 bytes per lane and access.
-template <typename T>
+// (part `part` of NPART: rows part * BT / NPART .. of the tile)
+template <typename T, int NPART = 1>
 __device__ __forceinline__ void store_tile(const float (*sA)[AP], T* __restrict__ out,
-                                          int c0, int nrow, int HV, int j, int lane) {
+                                          int c0, int nrow, int HV, int j, int lane, int part = 0) {
   constexpr int PER = 16 / sizeof(T);        // elements per 16-byte vector
   constexpr int SEGS = BT / PER;             // vectors per row
+  constexpr int ITS = BT * SEGS / 64 / NPART;
+  static_assert(BT * SEGS % (64 * NPART) == 0, "whole iterations per part");
 #pragma unroll
-  for (int it = 0; it < BT * SEGS / 64; ++it) {
+  for (int it = part * ITS; it < (part + 1) * ITS; ++it) {
     const int idx = it * 64 + lane;
     const int r = idx / SEGS, sg = idx % SEGS;
     if (r < nrow) {
@@ -99,11 +102,16 @@ __host__ __device__ constexpr int tix(int rb, int cb) { return rb * (rb + 1) / 2
 
 // -------------------------------------------------------------------------
 // Solve (I + A)^-1 for the strictly lower 64 x 64 fp32 matrix held in sA and
-// leave the inverse (unit lower, zero upper part) in sA.  One wave does the
-// work (`active`); every wave of the work-group must call it (it holds
-// block barriers).
+// leave the inverse (unit lower, zero upper part) in sA.  Wave 0 does the
+// forward substitution on the diagonal blocks.  The block merge has three
+// independent column blocks (0: X10 -> X20 -> X30, 1: X21 -> X31, 2: X32);
+// with NW = 1 wave 0 does all of them, with NW >= 3 waves 0, 1, 2 one each.
+// Every wave of the work-group must call it (it holds block barriers).
 // -------------------------------------------------------------------------
-__device__ __forceinline__ void solve_unit_lower_64(float (*sA)[AP], int lane, bool active) {
+template <int NW>
+__device__ __forceinline__ void solve_unit_lower_64(float (*sA)[AP], int lane, int wave) {
+  static_assert(NW == 1 || NW >= 3, "one wave, or one wave per column block");
+  const bool active = wave == 0;
   const int b = lane >> 4, jj = lane & 15;
   // forward substitution, column jj of diagonal block b
   float X[16];
@@ -144,37 +152,73 @@ __device__ __forceinline__ void solve_unit_lower_64(float (*sA)[AP], int lane, b
     return r;
   };
   f32x4 X10, X20, X30, X21, X31, X32;
-  if (active) {
-  const f32x4 X00 = diagB(0), X11 = diagB(1), X22 = diagB(2);
-  f32x4 P;
-  // column block 0
-  P = mmA(1, 0, X00, zero4());
-  X10 = -mmA(1, 1, P, zero4());
-  P = mmA(2, 0, X00, zero4());
-  P = mmA(2, 1, X10, P);
-  X20 = -mmA(2, 2, P, zero4());
-  P = mmA(3, 0, X00, zero4());
-  P = mmA(3, 1, X10, P);
-  P = mmA(3, 2, X20, P);
-  X30 = -mmA(3, 3, P, zero4());
-  // column block 1
-  P = mmA(2, 1, X11, zero4());
-  X21 = -mmA(2, 2, P, zero4());
-  P = mmA(3, 1, X11, zero4());
-  P = mmA(3, 2, X21, P);
-  X31 = -mmA(3, 3, P, zero4());
-  // column block 2
-  P = mmA(3, 2, X22, zero4());
-  X32 = -mmA(3, 3, P, zero4());
-  }
-  __syncthreads();
   auto put = [&](int br, int bc, const f32x4& Xv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sA[16 * br + 4 * grp + i][16 * bc + row] = Xv[i];
   };
-  if (active) {
-    put(1, 0, X10); put(2, 0, X20); put(3, 0, X30);
-    put(2, 1, X21); put(3, 1, X31); put(3, 2, X32);
+  if constexpr (NW == 1) {
+    if (active) {
+      const f32x4 X00 = diagB(0), X11 = diagB(1), X22 = diagB(2);
+      f32x4 P;
+      // column block 0
+      P = mmA(1, 0, X00, zero4());
+      X10 = -mmA(1, 1, P, zero4());
+      P = mmA(2, 0, X00, zero4());
+      P = mmA(2, 1, X10, P);
+      X20 = -mmA(2, 2, P, zero4());
+      P = mmA(3, 0, X00, zero4());
+      P = mmA(3, 1, X10, P);
+      P = mmA(3, 2, X20, P);
+      X30 = -mmA(3, 3, P, zero4());
+      // column block 1
+      P = mmA(2, 1, X11, zero4());
+      X21 = -mmA(2, 2, P, zero4());
+      P = mmA(3, 1, X11, zero4());
+      P = mmA(3, 2, X21, P);
+      X31 = -mmA(3, 3, P, zero4());
+      // column block 2
+      P = mmA(3, 2, X22, zero4());
+      X32 = -mmA(3, 3, P, zero4());
+    }
+    __syncthreads();
+    if (active) {
+      put(1, 0, X10); put(2, 0, X20); put(3, 0, X30);
+      put(2, 1, X21); put(3, 1, X31); put(3, 2, X32);
+    }
+  } else {
+    // one column block per wave (the same products, in the same order)
+    f32x4 P;
+    if (wave == 0) {
+      const f32x4 X00 = diagB(0);
+      P = mmA(1, 0, X00, zero4());
+      X10 = -mmA(1, 1, P, zero4());
+      P = mmA(2, 0, X00, zero4());
+      P = mmA(2, 1, X10, P);
+      X20 = -mmA(2, 2, P, zero4());
+      P = mmA(3, 0, X00, zero4());
+      P = mmA(3, 1, X10, P);
+      P = mmA(3, 2, X20, P);
+      X30 = -mmA(3, 3, P, zero4());
+    } else if (wave == 1) {
+      const f32x4 X11 = diagB(1);
+      P = mmA(2, 1, X11, zero4());
+      X21 = -mmA(2, 2, P, zero4());
+      P = mmA(3, 1, X11, zero4());
+      P = mmA(3, 2, X21, P);
+      X31 = -mmA(3, 3, P, zero4());
+    } else if (wave == 2) {
+      const f32x4 X22 = diagB(2);
+      P = mmA(3, 2, X22, zero4());
+      X32 = -mmA(3, 3, P, zero4());
+    }
+    __syncthreads();
+    if (wave == 0) {
+      put(1, 0, X10); put(2, 0, X20); put(3, 0, X30);
+    } else if (wave == 1) {
+      put(2, 1, X21); put(3, 1, X31);
+    } else if (wave == 2) {
+      put(3, 2, X32);
+    }
   }
   __syncthreads();
 }

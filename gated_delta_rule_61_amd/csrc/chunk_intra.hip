@@ -155,7 +155,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void gd
   __syncthreads();
 
   // Steps 3-4: substitution + merge
-  solve_unit_lower_64(sA, lane, true);
+  solve_unit_lower_64<1>(sA, lane, 0);
 
   // Step 5: store
   store_tile<C>(sA, Ainv, c0, nrow, HV, j, lane);

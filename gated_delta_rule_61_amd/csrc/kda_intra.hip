@@ -327,13 +327,15 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(
   }
   __syncthreads();
 
-  // ---- (I + A)^-1 (wave 0), then the tiles to memory in 16-byte row pieces,
-  // one tile per wave
-  solve_unit_lower_64(sA, lane, w == 0);
-  if (w == 0) store_tile<P>(sA, Ainv_ws, c0, nrow, HV, hv, lane);
-  if (w == 1 && Akk_out) store_tile<T>(sA, Akk_out, c0, nrow, HV, hv, lane);
+  // ---- the tiles to memory in 16-byte row pieces: the Aqk tiles first (waves
+  // 2, 3, while wave 0 runs the substitution), then (I + A)^-1 (substitution
+  // on wave 0, the merge's three column blocks on waves 0 - 2), half a tile
+  // per wave
   if (w == 2) store_tile<P>(sQ, Aqk_ws, c0, nrow, HV, hv, lane);
   if (w == 3 && Aqk_out) store_tile<T>(sQ, Aqk_out, c0, nrow, HV, hv, lane);
+  solve_unit_lower_64<4>(sA, lane, w);
+  if (w < 2) store_tile<P, 2>(sA, Ainv_ws, c0, nrow, HV, hv, lane, w);
+  else if (Akk_out) store_tile<T, 2>(sA, Akk_out, c0, nrow, HV, hv, lane, w - 2);
 }
 
 template <typename T, int DK>
