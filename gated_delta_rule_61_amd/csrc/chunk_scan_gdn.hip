@@ -193,12 +193,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 
     // state snapshots: the state at the start of every nts-th chunk
     const size_t sbase = hs ? (size_t)snapshot_offset(cu, ns, Tlen, nts * BT) : 0;
-    auto chunk = [&](auto stg, int c) __attribute__((always_inline)) {
-      constexpr bool S1 = decltype(stg)::value;
-      const char* sK = S1 ? sK1 : sK0;
-      const char* sKt = KDA ? (S1 ? sT1 : sT0) : sK;   // source of the update's K^T
-      // (entries past the buffer's capacity are not written)
-      if (hs && c % nts == 0 && (long long)(sbase + c / nts) < scap) {
+    // the state at the start of chunk c, if it is a snapshot chunk (entries
+    // past the buffer's capacity are not written); stored at the end of the
+    // chunk before, while the wave waits at the barrier
+    auto snapshot = [&](int c) __attribute__((always_inline)) {
+      if (hs && c < NC && c % nts == 0 && (long long)(sbase + c / nts) < scap) {
         const size_t hp = ((sbase + c / nts) * HV + j) * (size_t)V * DK + (size_t)(v0 + 16 * cb + n) * DK;
         // blocks 2m and 2m + 1 hold keys 32 m + 8 g + [0, 8) of this lane's row
 #pragma unroll
@@ -208,6 +207,12 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
           store_state8(hs, hp + perm_row(kb, 4 * g), x, sbf16 != 0);
         }
       }
+    };
+    snapshot(0);
+    auto chunk = [&](auto stg, int c) __attribute__((always_inline)) {
+      constexpr bool S1 = decltype(stg)::value;
+      const char* sK = S1 ? sK1 : sK0;
+      const char* sKt = KDA ? (S1 ? sT1 : sT0) : sK;   // source of the update's K^T
       const char* sAi = S1 ? sAi1 : sAi0;
       const char* sV = S1 ? sV1 : sV0;
       const float (*sG)[BT] = S1 ? sG1 : sG0;
@@ -336,6 +341,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
           St[kb] = KDA ? mma_h(Kt[kb][s], Vl[s], St[kb]) : mma_bf(Kt[kb][s], Vl[s], St[kb]);
       }
       publish_s();
+      snapshot(c + 1);
       lds_barrier();
     };
     for (int c = 0; c < NC; c += 2) {
