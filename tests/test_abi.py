@@ -213,6 +213,9 @@ def test_snapshot_count_reads_no_device_memory(monkeypatch):
     assert binding.snapshot_count(2, 130, 64) == 6
     assert binding.snapshot_count(1, 400, 64, [0, 130, 194, 195, 400]) == 3 + 1 + 1 + 4
     assert binding.snapshot_count(1, 400, 128, torch.tensor([0, 130, 194, 195, 400])) == 2 + 1 + 1 + 2
+    # invalid boundaries clamp per sequence into [0, T] with the end not below
+    # the start, as the device tables do: (0, 300), empty, (0, 300), empty, (0, 300)
+    assert binding.snapshot_count(1, 300, 64, [-7, 300, 0, 300, 0, 1000]) == 5 + 0 + 5 + 0 + 5
     with pytest.raises(ValueError):
         binding.snapshot_count(1, 400, 64, torch.zeros(5, dtype=torch.int64, device="meta"))
 
