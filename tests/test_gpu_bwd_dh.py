@@ -128,3 +128,18 @@ def test_bwd_dh_b4_t4096_bf16_states_sampled_heads():
                                              g=inp.g[:, :, heads], dht=dht[:, heads], split_size=64)
     check("dh", dh.cpu()[:, heads], dh_ref, torch.bfloat16)
     check("dh0", dh0.cpu()[:, heads], dh0_ref, torch.bfloat16, rel=STATE_SCAN_REL)
+
+
+# the scalar-gate kernel's ring of four LDS slots (loads three chunks ahead)
+# and its loop unrolled by four: sequences of 0, 1, 2, ..., 8, 9 and 10 chunks
+# with ragged tails, both key widths, bf16 and fp32 stored states
+RING_LENS = [0, 1, 65, 130, 255, 320, 384, 448, 512, 513, 577]
+
+
+@pytest.mark.parametrize("K", [64, 128])
+@pytest.mark.parametrize("S,fp32_states", [(64, False), (128, True)])
+@pytest.mark.parametrize("gate", ["gdn", "gamma"])
+def test_bwd_dh_ring_chunk_counts(K, S, fp32_states, gate):
+    inp = workloads.make_prefill(1, sum(RING_LENS), 2, 4, K, K, dtype=torch.bfloat16, seed=90 + K, h0=True,
+                                 seqlens=RING_LENS, name="bwd_dh_ring")
+    _case(inp, gate, S, seed=91, fp32_states=fp32_states)

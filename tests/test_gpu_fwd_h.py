@@ -137,3 +137,18 @@ def test_fwd_h_grouped_gate_heads(gate):
                                       cu_seqlens=inp.cu_seqlens, split_size=128)
     check("h", h.cpu(), h_ref, torch.bfloat16, rel=STATE_SCAN_REL)
     check("ht", ht.cpu(), ht_ref, torch.bfloat16, rel=STATE_SCAN_REL)
+
+
+# the scalar-gate kernel's ring of four LDS slots (loads three chunks ahead)
+# and its loop unrolled by four: sequences of 0, 1, 2, ..., 8, 9 and 10 chunks
+# with ragged tails, both key widths, bf16 and fp32 stored states
+RING_LENS = [0, 1, 65, 130, 255, 320, 384, 448, 512, 513, 577]
+
+
+@pytest.mark.parametrize("K", [64, 128])
+@pytest.mark.parametrize("S,fp32_states", [(64, False), (128, True)])
+@pytest.mark.parametrize("gate", ["gdn", "gamma"])
+def test_fwd_h_ring_chunk_counts(K, S, fp32_states, gate):
+    inp = workloads.make_prefill(1, sum(RING_LENS), 2, 4, K, K, dtype=torch.bfloat16, seed=90 + K, h0=True,
+                                 seqlens=RING_LENS, name="fwd_h_ring")
+    _case(inp, gate, S, seed=93, fp32_states=fp32_states)
