@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   typedef Lds<DK> L;
   constexpr int KS = L::KS, KB = L::KB, NQK = L::NQK;
   // q / k tile sources (GDN: the raw bf16 inputs, one row per q / k head;
-  // KDA: the gated fp16 operands, one row per v-head)
+  // KDA: the gated fp16 operands, head- and slab-major: [HV][DK / 32][tokens][32])
   const char* const qsrc = reinterpret_cast<const char*>(qop);
   const char* const ksrc = reinterpret_cast<const char*>(kop);
   // two stages of the chunk inputs, separate arrays so that the compiler can
@@ -432,10 +432,14 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // per-lane byte offsets within a full chunk: LDS slot (row, unit')
     // receives global unit unit' ^ swizzle(row)
     uint32_t o_qk[NQK], o_a[8], o_v[4];
+    // KDA's gated planes are head- and slab-major (a chunk's 32-channel slab
+    // is one 4 KB block, the slabs of a head ttot * 64 bytes apart)
+    const uint32_t slab_bytes = (uint32_t)ttot * 64u;
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int row = i * L::QROWS + lane / (DK / 8);
-      o_qk[i] = (uint32_t)row * qk_row + 16 * ((lane % (DK / 8)) ^ qk_swz<DK>(row));
+      o_qk[i] = KDA ? plane_off<DK>(row, lane % (DK / 8), slab_bytes)
+                    : (uint32_t)row * qk_row + 16 * ((lane % (DK / 8)) ^ qk_swz<DK>(row));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     auto dma_chunk = [&](int c0, lchar* dK, lchar* dQ, lchar* dT, lchar* dAi, lchar* dAq, lchar* dV,
                          lchar* dG, lchar* dD) __attribute__((always_inline)) {
       const int nr = eos - c0 < BT ? eos - c0 : BT;
-      const size_t xo = (size_t)c0 * qk_row + (size_t)jo * DK * 2;
+      const size_t xo = KDA ? ((size_t)j * (DK / 32) * ttot + c0) * 64 : (size_t)c0 * qk_row + (size_t)jo * DK * 2;
       const char* ac0 = reinterpret_cast<const char*>(Ainv + ((size_t)c0 * HV + j) * BT);
       const char* ac1 = reinterpret_cast<const char*>(Aqk + ((size_t)c0 * HV + j) * BT);
       const char* vc = reinterpret_cast<const char*>(v + ((size_t)c0 * HV + j) * V + v0);
@@ -458,16 +462,16 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       const float* gp = GF + (size_t)j * 4 * gs + c0 + rg;
       if constexpr (KDA) {
         if (mr == 0) {
-          dma_qk_tile<DK>(ksrc + xo, o_qk, nr, qk_row, dK, lane);
+          dma_plane_tile<DK>(ksrc + xo, o_qk, nr, slab_bytes, dK, lane);
           dma_v_tile(vc, o_v, nr, v_row, dV, lane);
         } else if (mr == 1) {
-          dma_qk_tile<DK>(qsrc + xo, o_qk, nr, qk_row, dQ, lane);
+          dma_plane_tile<DK>(qsrc + xo, o_qk, nr, slab_bytes, dQ, lane);
           dma4(gp + 2 * gs, dG + 512);
           const float* dp = DG + ((size_t)(chunk0 + (c0 - bos) / BT) * HV + j) * DK;
 #pragma unroll
           for (int i = 0; i < DK / 64; ++i) dma4(dp + 64 * i + lane, dD + 256 * i);
         } else if (mr == 2) {
-          dma_qk_tile<DK>(reinterpret_cast<const char*>(ktop) + xo, o_qk, nr, qk_row, dT, lane);
+          dma_plane_tile<DK>(reinterpret_cast<const char*>(ktop) + xo, o_qk, nr, slab_bytes, dT, lane);
         } else {
           dma_a_tile(ac0, o_a, nr, a_row, dAi, lane);
           dma_a_tile(ac1, o_a, nr, a_row, dAq, lane);
@@ -502,9 +506,16 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       if (piece < NXT * QKP) {
         const int t = piece / QKP;
         const char* x = pick(t == 0, qsrc, pick(t == 1, ksrc, reinterpret_cast<const char*>(ktop)));
-        const int row0 = (piece % QKP) * (64 / QKP) + lane / QKP;
-        const int row = row0 < nr ? row0 : nr - 1;
-        p = x + (size_t)(c0 + row) * qk_row + (size_t)jo * DK * 2 + 128 * (lane % QKP);
+        if constexpr (KDA) {
+          // slabs 2 * (piece % QKP) and the next one: 32 lines (two rows each) per slab
+          const int row = 2 * (lane & 31) < nr ? 2 * (lane & 31) : nr - 1;
+          p = x + ((size_t)j * (DK / 32) * ttot + c0 + row) * 64 +
+              (size_t)(2 * (piece % QKP) + (lane >> 5)) * slab_bytes;
+        } else {
+          const int row0 = (piece % QKP) * (64 / QKP) + lane / QKP;
+          const int row = row0 < nr ? row0 : nr - 1;
+          p = x + (size_t)(c0 + row) * qk_row + (size_t)jo * DK * 2 + 128 * (lane % QKP);
+        }
       } else {
         const int row = lane < nr ? lane : nr - 1;
         p = reinterpret_cast<const char*>(pick(piece == NXT * QKP, Ainv, Aqk) +

@@ -424,6 +424,9 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* gk, 
   if (st != GDN_OK) return st;
   if ((Aqk && !aligned16(Aqk)) || (Akk_inv && !aligned16(Akk_inv)))
     return fail(GDN_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  // the gated planes of one head span B*T*K*2 bytes, addressed with 32-bit offsets
+  if ((long long)B * T * K * 2 >= (1LL << 32))
+    return fail(GDN_ERR_UNSUPPORTED, "B*T too large for KDA (got %lld tokens)", (long long)B * T);
   const int eb = dtype == GDN_DTYPE_BF16 ? 2 : 4;
   const ChunkWorkspace L = chunk_workspace_layout((long long)B * T, HV, K, P.N,
                                                   (T + 63) / 64 * B + P.N, eb, true);

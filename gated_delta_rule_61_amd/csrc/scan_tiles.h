@@ -186,6 +186,33 @@ __device__ __forceinline__ void dma_qk_tile(const char* xc, const uint32_t* o_qk
     }
   }
 }
+// A q / k-like tile stored head- and slab-major: for each 32-channel slab a
+// block of [tokens][32] rows (64 bytes each), the slabs `slab_bytes` apart.
+// Byte offset of the global unit that lands in LDS slot (row t, unit u): the
+// unit u ^ swizzle(t) of row t, as for the row-major tiles.
+template <int DK>
+__device__ __forceinline__ uint32_t plane_off(int t, int u, uint32_t slab_bytes) {
+  const int gu = u ^ qk_swz<DK>(t);
+  return (uint32_t)(gu >> 2) * slab_bytes + (uint32_t)(t * 64 + ((gu & 3) << 4));
+}
+template <int DK>
+__device__ __forceinline__ void dma_plane_tile(const char* xc, const uint32_t* o_pl, int nr,
+                                               uint32_t slab_bytes, lchar* dX, int lane) {
+  typedef Lds<DK> L;
+  if (nr == BT) {
+#pragma unroll
+    for (int i = 0; i < L::NQK; ++i) dma16(xc + o_pl[i], dX + 1024 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < L::NQK; ++i) {
+      const int row = i * L::QROWS + lane / (DK / 8);
+      const int rr = row < nr ? row : nr - 1;
+      // the unit of the clamped row at the position the swizzle of `row` selects
+      const uint32_t off = plane_off<DK>(row, lane % (DK / 8), slab_bytes) - (uint32_t)(row - rr) * 64u;
+      dma16(xc + off, dX + 1024 * i);
+    }
+  }
+}
 __device__ __forceinline__ void dma_a_tile(const char* ac, const uint32_t* o_a, int nr, uint32_t a_row,
                                            lchar* dA, int lane) {
   if (nr == BT) {
