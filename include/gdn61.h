@@ -196,6 +196,9 @@ int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
  *                               exp(G_t,c - G_s,c) for s < t in the chunk;
  *                               0 above the diagonal and past the chunk end
  * (G = cumulative log-gate from the chunk start).
+ * B * T * K * 2 must stay below 2^32 (16.7 M tokens at K = 128): the
+ * workspace's gated operands of one head are addressed with 32-bit offsets;
+ * larger calls return GDN_ERR_UNSUPPORTED.
  */
 int kda_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* gk, const float* beta, float scale,

@@ -100,6 +100,13 @@ def test_kda_requires_gate(L):
     assert r == 1 and b"gk" in L.gdn_last_error()
 
 
+def test_kda_rejects_planes_past_32_bit_offsets(L):
+    # one head's gated planes span B*T*K*2 bytes, addressed with 32-bit offsets: 2^24 tokens at K = 128 is too many
+    r = L.kda_chunk_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, None, None, None, 0, 0, 0, None, 0, 1, 1 << 24, 1, 1, 128,
+                        128, 64, 1, FAKE, None, None, FAKE, 1 << 44, None)
+    assert r == 2 and b"too large for KDA" in L.gdn_last_error()
+
+
 def test_kda_rejects_undersized_snapshots(L):
     r = L.kda_chunk_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, None, None, FAKE, 128, 1, 0, None, 0, 2, 64, 1, 1, 64, 64,
                         64, 1, FAKE, None, None, FAKE, 1 << 40, None)
