@@ -116,10 +116,11 @@ union IntraSmem {
   SolveTiles t;
 };
 
-// Occupancy: 4 work-groups per CU for bf16 io (<= 128 VGPRs, 34 KB LDS), 3
-// for fp32 io.
+// Occupancy: 3 work-groups per CU (<= 168 VGPRs; 34 KB of LDS for bf16 io,
+// 42 KB for fp32 io).  A cap of 128 VGPRs for a fourth spills 30 - 57
+// registers and about doubles the time.
 template <typename T, int DK, typename P = typename ComputeOf<T>::type>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 3) void kda_intra_kernel(
+__global__ __launch_bounds__(256, 3) void kda_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ gk,
     const float* __restrict__ beta, float scale, T* __restrict__ Aqk_out,
     T* __restrict__ Akk_out, P* __restrict__ Ainv_ws, P* __restrict__ Aqk_ws,
@@ -287,9 +288,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 3) void kda_intra_kernel(
           *reinterpret_cast<float4*>(&S.c[t][cb + e]) = make_float4(vc[e], vc[e + 1], vc[e + 2], vc[e + 3]);
       }
     }
-    // the block pairs' decay factors, exp(G[n_i] - G[m_j]) from the
-    // block-local sums: g[16i] - tot[i] on the diagonal, g[16i] plus the
-    // totals of the blocks between j and i below it
+    // the block pairs' decay factors exp(G[n_i] - G[m_j]) from the
+    // block-local sums: the exponent is g[16i] - tot[i] on the diagonal
+    // (j = i), and g[16i] plus the totals of the blocks strictly between j
+    // and i below it (j < i)
     auto pair_decay = [&](int idx) {
       const int pr = idx >> 5, c = idx & 31;
       const int i = pr >= 6 ? 3 : pr >= 3 ? 2 : pr >= 1 ? 1 : 0;
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 3 : 3) void kda_intra_kernel(
 
     // ---- block pairs (w, jb), jb <= w, over the slab's channels: fp16 (fp32
     // for fp32 io) MFMA.  The diagonal pair's operands decide first whether
-    // its decay or size leaves the fast path's range; then this slab's part
+    // its decay or size leaves the fast path's range; if so, this slab's part
     // of the diagonal block is computed exactly, pair by pair, in fp32.
     bool exact;
     {
