@@ -138,13 +138,20 @@ def stage_times(binding, torch, step, steps):
 
 # --------------------------------------------------------------- counters
 def source_hash() -> str:
-    """Hash of the kernel sources (the same hash the profile summaries record)."""
+    """Hash of the kernel sources (the same hash the profile summaries record),
+    taken over the code only: comments, indentation and blank lines are
+    dropped, so that an edit of the text around a kernel does not void its
+    measured counters."""
     import glob
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_61_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        lines = (re.sub(r"//.*", "", ln).strip() for ln in text.splitlines())
+        h.update(os.path.basename(f).encode())
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 
