@@ -108,14 +108,21 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   const int n = lane & 15, g = lane >> 4;
   const int NVT = V / BV;
 
-  // ---- work-group -> (sequence, head, V-tile): the NVT tiles of a (sequence,
-  // head) stay on one XCD, groups in order of decreasing sequence length
+  // ---- work-group -> (sequence, head, V-tile).  Work-group ids are dealt
+  // round-robin to the 8 XCDs.  The unit is a (sequence, q / k head): its
+  // HV / Hk v-heads and their NVT tiles run next to each other on one XCD, so
+  // that they share the q / k rows in that XCD's L2 (KDA: one v-head per
+  // unit).  Units go in order of decreasing sequence length.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, pos = bid >> 3;
-  const int vt = pos % NVT;
-  const int grpi = (pos / NVT) * 8 + xcd;
-  if (grpi >= N * HV) return;
-  const int rank = grpi / HV, j = grpi - rank * HV;
+  const int G = KDA ? 1 : HV / Hk;            // v-heads per unit
+  const int per = G * NVT;                    // work-groups per unit
+  const int unit = (pos / per) * 8 + xcd;
+  const int rem = pos - (pos / per) * per;
+  const int vt = rem % NVT;
+  const int HU = HV / G;                      // units per sequence
+  if (unit >= N * HU) return;
+  const int rank = unit / HU, j = (unit - rank * HU) * G + rem / NVT;
   const int ns = order ? order[rank] : rank;
   int bos, eos;
   if (cu) {
@@ -582,8 +589,9 @@ template <int DK, bool KDA>
 hipError_t launch_dk(const ChunkArgs& a, const void* qop, const void* kop, const void* ktop,
                      const float* dg, hipStream_t s) {
   const int nvt = a.V / BV;
-  const int groups = a.N * a.HV;
-  const int nblk = ((groups + 7) / 8) * 8 * nvt;
+  const int G = KDA ? 1 : a.HV / a.Hk;        // v-heads per (sequence, q / k head) unit
+  const int units = a.N * (a.HV / G);
+  const int nblk = ((units + 7) / 8) * 8 * G * nvt;
   hipLaunchKernelGGL((gdn_scan_bf16_kernel<DK, KDA>), dim3((unsigned)nblk), dim3(NTHR), 0, s, qop, kop,
                      (const f16_t*)ktop, (const bf16_t*)a.v, (const float*)a.GF, dg,
                      (const f16_t*)a.Ainv, (const f16_t*)a.Aqk, a.scale, a.h0, a.ht, a.hs, a.split_chunks,
