@@ -86,6 +86,18 @@ def test_gdn_varlen_bf16_k128():
     _compare(inp)
 
 
+@pytest.mark.parametrize("Hk,HV,lens", [(1, 4, [130, 1, 77]), (1, 8, [64, 200]), (2, 8, None)],
+                         ids=["gqa4_varlen3", "gqa8_varlen2", "gqa4_dense"])
+def test_gdn_bf16_wide_gqa_groups(Hk, HV, lens):
+    # the bf16 scan runs the v-heads of a (sequence, q/k head) next to each other on one XCD;
+    # 4 and 8 v-heads per q/k head, with unit counts that leave padding work-groups
+    T = sum(lens) if lens else 150
+    B = 1 if lens else 3
+    inp = workloads.make_prefill(B, T, Hk, HV, 128, 128, dtype=torch.bfloat16, seed=11 + HV, h0=True,
+                                 seqlens=lens, name=f"bf16_gqa{HV // Hk}")
+    _compare(inp)
+
+
 def test_gdn_no_final_state_and_empty():
     inp = workloads.make_prefill(1, 70, 1, 1, 64, 64, dtype=torch.float32, seed=9)
     o, ht = _gpu(inp, output_final_state=False)
