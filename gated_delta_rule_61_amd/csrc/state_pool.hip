@@ -10,6 +10,7 @@
 // (sequence, head) state; per 8 elements a thread reads two 16-byte fp32
 // vectors and writes one 16-byte bf16 vector (each wave instruction touches
 // 1 KiB of contiguous memory), all of its loads issued before its stores.
+// Both directions are streaming accesses (each byte is touched once).
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -39,8 +40,12 @@ __global__ __launch_bounds__(256) void state_to_pool_kernel(
   for (int i = 0; i < ITEMS; ++i) {
     const long long e0 = (long long)part * PER_BLOCK + 2048 * i + 8 * threadIdx.x;
     if (e0 < VK) {
-      a[i] = *reinterpret_cast<const float4*>(src + e0);
-      b[i] = *reinterpret_cast<const float4*>(src + e0 + 4);
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      // read once: streaming (nontemporal) loads
+      const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + e0));
+      const f4 y = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + e0 + 4));
+      a[i] = make_float4(x[0], x[1], x[2], x[3]);
+      b[i] = make_float4(y[0], y[1], y[2], y[3]);
     }
   }
 #pragma unroll
