@@ -87,6 +87,37 @@ def test_kda_strong_gate_bf16_exact_diagonal(K):
     _compare(inp)
 
 
+def _exact_fraction(inp):
+    # share of (chunk, 16-token block, 32-channel slab, head) units whose decay inside the
+    # block exceeds the 10 nats the intra kernel's fast path accepts (those take the exact path)
+    gk = inp.gk[0].double().numpy()
+    K = gk.shape[-1]
+    cu = inp.cu_seqlens.tolist()
+    hits = units = 0
+    for c0, c1 in ((c, min(c + 64, e)) for b, e in zip(cu[:-1], cu[1:]) for c in range(b, e, 64)):
+        G = np.cumsum(gk[c0:c1], axis=0)
+        for w in range(0, G.shape[0], 16):
+            d = G[w] - G[min(w + 15, G.shape[0] - 1)]
+            for s in range(K // 32):
+                m = d[:, 32 * s:32 * s + 32].max(axis=1)
+                hits += int((m > 10).sum())
+                units += m.size
+    return hits / units
+
+
+@pytest.mark.parametrize("K", [64, 128])
+def test_kda_bf16_mixed_exact_and_fast_slabs(K):
+    """gk = -softplus(N(0, 1)) * 0.6: about a third of the (block, slab) units exceed the fast
+    path's decay limit, so one call mixes exactly computed and factorised slabs of the same
+    diagonal blocks; o, ht, Aqk and Akk_inv element-wise against the oracle."""
+    inp = workloads.make_prefill(1, 256, 2, 2, K, K, dtype=torch.bfloat16, seed=160 + K, gate="kda",
+                                 g_scale=0.6, h0=True, seqlens=[190, 66], name=f"kda_bf16_mixed_K{K}")
+    f = _exact_fraction(inp)
+    print(f"exact-path share of (block, slab) units: {f:.3f}", flush=True)
+    assert 0.1 < f < 0.9
+    _compare(inp)
+
+
 def test_kda_varlen_bf16():
     lens = [70, 1, 64, 129, 0, 33]
     inp = workloads.make_prefill(1, sum(lens), 2, 4, 128, 128, dtype=torch.bfloat16, seed=150,
