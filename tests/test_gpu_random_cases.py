@@ -1,9 +1,13 @@
-"""GPU parity over seeded random problem shapes (GDN and KDA prefill, C ABI)
-against the fp64 oracle.  Each case draws, from its own seed: q/k heads and
-v-heads per q/k head (1, 2 or 4), K = V in {64, 128}, the io dtype, the gate
-form, a dense batch or packed sequences (lengths 0..200, empty and one-token
-sequences included), h0 or none, and a gate strength.  The draws are fixed by
-the seed list, so the cases are the same on every run."""
+"""GPU parity over seeded random problem shapes against the fp64 oracle (C ABI):
+GDN and KDA prefill, decode, and both state scans.  Each prefill case draws,
+from its own seed: q/k heads and v-heads per q/k head (1, 2 or 4), K = V in
+{64, 128}, the io dtype, the gate form, a dense batch or packed sequences
+(lengths 0..200, empty and one-token sequences included), h0 or none, and a
+gate strength; decode cases draw the batch, T, head counts, a pool larger
+than the batch with shuffled slots, the normalisation switch and the softplus
+parameters; state-scan cases draw heads, K, the gate form, the split size and
+the stored-state dtype.  The draws are fixed by the seed lists, so the cases
+are the same on every run."""
 
 import numpy as np
 import pytest
@@ -77,3 +81,67 @@ def test_gdn_random_case(seed):
 @pytest.mark.parametrize("seed", range(12))
 def test_kda_random_case(seed):
     _run(seed, kda=True)
+
+
+# ---------------------------------------------------------------------------
+# decode and the two state scans over seeded random shapes, through the
+# helpers of their own GPU test modules
+# ---------------------------------------------------------------------------
+from tests.test_gpu_decode import _run as _decode_run, _ulp_consistent        # noqa: E402
+from tests.test_gpu_fwd_h import _case as _fwd_h_case                          # noqa: E402
+from tests.test_gpu_bwd_dh import _case as _bwd_dh_case                        # noqa: E402
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_random_case(seed):
+    r = np.random.default_rng(30_000 + seed)
+    B, T = int(r.integers(1, 41)), int(r.integers(1, 5))
+    H = int(r.choice([1, 2, 4]))
+    HV = min(32, H * int(r.choice([1, 2, 4, 8])))
+    pool = B + int(r.integers(0, 9))
+    idx = [int(x) for x in r.permutation(pool)[:B]]
+    use_norm = bool(r.random() < 0.8)
+    sp_beta = float(r.choice([1.0, 1.0, 2.0]))
+    sp_thr = float(r.choice([20.0, 20.0, 1.0]))
+    print(f"decode random seed={seed} B={B} T={T} H={H} HV={HV} pool={pool} norm={use_norm} "
+          f"softplus beta={sp_beta} threshold={sp_thr}", flush=True)
+    inp = workloads.make_decode(B, T, H, HV, 128, 128, seed=31_000 + seed, pool=pool, indices=idx)
+    o, s, o_ref, s_ref = _decode_run(inp, use_norm=use_norm, sp_beta=sp_beta, sp_thr=sp_thr)
+    check("o", o, o_ref, torch.bfloat16)
+    check("state", s, s_ref, torch.bfloat16)
+    _ulp_consistent(s, s_ref)
+    untouched = sorted(set(range(pool)) - set(idx))
+    assert torch.equal(s[untouched], inp.state[untouched])
+
+
+def _state_scan_draw(seed):
+    r = np.random.default_rng(40_000 + seed)
+    Hk = int(r.choice([1, 2]))
+    HV = Hk * int(r.choice([1, 2]))
+    K = int(r.choice([64, 128]))
+    gate = str(r.choice(["gdn", "gamma", "none", "gv", "gdn+gv", "kda"]))
+    S = int(r.choice([64, 128, 256]))
+    fp32_states = bool(r.random() < 0.5)
+    if r.random() < 0.5:
+        lens = [int(x) for x in r.choice([0, 1, 64, 65, 127, 200, 300], size=int(r.integers(1, 4)))]
+        if sum(lens) == 0:
+            lens[0] = 90
+        B, T = 1, sum(lens)
+    else:
+        lens, B, T = None, int(r.integers(1, 3)), int(r.integers(1, 300))
+    inp = workloads.make_prefill(B, T, Hk, HV, K, K, dtype=torch.bfloat16, seed=41_000 + seed,
+                                 gate="kda" if gate == "kda" else "gdn", h0=bool(r.random() < 0.5),
+                                 seqlens=lens, name=f"scan_random{seed}")
+    return inp, (None if gate == "none" else gate), S, fp32_states
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fwd_h_random_case(seed):
+    inp, gate, S, fp32_states = _state_scan_draw(seed)
+    _fwd_h_case(inp, gate, S, seed=seed, fp32_states=fp32_states)
+
+
+@pytest.mark.parametrize("seed", range(8, 16))
+def test_bwd_dh_random_case(seed):
+    inp, gate, S, fp32_states = _state_scan_draw(seed)
+    _bwd_dh_case(inp, gate, S, seed=seed, fp32_states=fp32_states)
