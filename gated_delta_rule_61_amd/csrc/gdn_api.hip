@@ -140,6 +140,14 @@ int check_chunk(const void* q, const void* k, const void* v, const float* gate,
   } else {
     P.N = B;
   }
+  {
+    // the launches index chunk slots, (sequence, head) pairs and their
+    // tiles (at most 8 per pair) with 32-bit integers
+    const long long slots = cu ? (long long)(T + 63) / 64 + P.N : (long long)B * ((T + 63) / 64);
+    if ((slots + 8) * HV * 8 >= (1LL << 31) || ((long long)P.N * HV + 8) * 8 >= (1LL << 31))
+      return fail(GDN_ERR_UNSUPPORTED, "too many chunks or sequences x heads for one launch (N=%d HV=%d)", P.N,
+                  HV);
+  }
   const bool work = (long long)B * T > 0;
   if (work && (!q || !k || !v || !beta || !o))
     return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, beta and o are required");
@@ -487,6 +495,9 @@ int gdn_decode(const void* q, const void* k, const void* v, const void* a, const
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, state and o must be 16-byte aligned");
   if ((long long)pool * HV * V * K >= (1LL << 40)) return fail(GDN_ERR_UNSUPPORTED, "state pool too large");
+  // up to four work-groups per (batch row, v-head), indexed with 32-bit integers
+  if ((long long)B * HV * 4 >= (1LL << 31))
+    return fail(GDN_ERR_UNSUPPORTED, "too many batch rows x heads for one launch (B=%d HV=%d)", B, HV);
   DecodeArgs d;
   d.q = q; d.k = k; d.v = v; d.a = a; d.b = b; d.A_log = A_log; d.dt_bias = dt_bias;
   d.state = state; d.idx = state_indices; d.o = o;
@@ -537,6 +548,10 @@ static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, c
     if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", num_seqs);
     N = num_seqs;
   }
+  // the launch indexes (sequence, head) pairs and their tiles (at most 8 per
+  // pair) with 32-bit integers
+  if (((long long)N * HV + 8) * 8 >= (1LL << 31))
+    return fail(GDN_ERR_UNSUPPORTED, "too many sequences x heads for one launch (N=%d HV=%d)", N, HV);
   if ((long long)B * T > 0 && (!a_op || !b_op))
     return fail(GDN_ERR_INVALID_ARGUMENT, "%s and %s are required", an, bn);
   const void* ptrs[] = {a_op, b_op, g, g_gamma, gk, gv, init, snaps, fin};

@@ -40,6 +40,11 @@
  *     missing or too small workspace GDN_ERR_WORKSPACE (the one code added
  *     to the four of the plan: it tells the caller to query the size).
  *   - io dtype codes: GDN_DTYPE_F32 (0) or GDN_DTYPE_BF16 (1).
+ *   - Size limits (GDN_ERR_UNSUPPORTED beyond them): B * T below 2^25
+ *     tokens; the kernels index work-groups with 32-bit integers, so
+ *     (sequences x v-heads + 8) x 8 and, for the prefill, (chunk slots + 8)
+ *     x v-heads x 8 stay below 2^31 (decode: B x HV x 4); tensor offsets
+ *     are 64-bit.
  *   - Stored states (prefill snapshots, the state scans' h / dh) are kept in
  *     fp32 or bf16 as the caller chooses (state_dtype; "fla ops/common/
  *     chunk_h.py", chunk_fwd_h / chunk_bwd_dh: states in the input dtype

@@ -107,6 +107,24 @@ def test_kda_rejects_planes_past_32_bit_offsets(L):
     assert r == 2 and b"too large for KDA" in L.gdn_last_error()
 
 
+def test_launch_index_range_is_checked(L):
+    """Grids are indexed with 32-bit integers: shapes whose work-group count
+    would pass 2^31 are refused before any launch."""
+    # 2^28 packed sequences x 8 heads
+    assert _chunk(L, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, cu=FAKE, ns=1 << 28, HV=8, Hk=8,
+                  ws=FAKE, wsb=1 << 60) == 2
+    assert b"for one launch" in L.gdn_last_error()
+    # 2^24 dense sequences of one token x 32 heads
+    assert _chunk(L, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, o=FAKE, B=1 << 24, T=1, HV=32, Hk=32,
+                  ws=FAKE, wsb=1 << 60) == 2
+    assert b"for one launch" in L.gdn_last_error()
+    for fwd in (False, True):
+        assert _bwd(L, fwd=fwd, cu=FAKE, ns=1 << 27, HV=4, Hk=4) == 2
+        assert b"for one launch" in L.gdn_last_error()
+    assert _dec(L, B=1 << 25, HV=16, H=16, idx=FAKE) == 2
+    assert b"for one launch" in L.gdn_last_error()
+
+
 def test_kda_rejects_undersized_snapshots(L):
     r = L.kda_chunk_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, None, None, FAKE, 128, 1, 0, None, 0, 2, 64, 1, 1, 64, 64,
                         64, 1, FAKE, None, None, FAKE, 1 << 40, None)
