@@ -54,12 +54,12 @@ _SIGNATURES = {
                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_float, _c_float, _c_float, _c_int, _c_float, _c_void_p]),
     "gdn_chunk_bwd_dh": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
-                                  _c_float, _c_void_p, _c_void_p, _c_int, _c_ll, _c_int, _c_void_p,
+                                  _c_float, _c_void_p, _c_void_p, _c_int, _c_ll, _c_int, _c_int, _c_void_p,
                                   _c_void_p, _c_int,
                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                   _c_void_p]),
     "gdn_chunk_fwd_h": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
-                                 _c_void_p, _c_void_p, _c_int, _c_ll, _c_int, _c_void_p, _c_void_p, _c_int,
+                                 _c_void_p, _c_void_p, _c_int, _c_ll, _c_int, _c_int, _c_void_p, _c_void_p, _c_int,
                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_void_p]),
     "gdn_state_to_pool": (_c_int, [_c_void_p, _c_void_p, _c_void_p,
@@ -426,13 +426,15 @@ def chunk_bwd_dh(q: torch.Tensor, dout: torch.Tensor, g: Optional[torch.Tensor] 
                  cu_seqlens: Optional[torch.Tensor] = None, split_size: Optional[int] = 64,
                  output_dh0: bool = True, chunk_size: int = 64, gv: Optional[torch.Tensor] = None,
                  states_in_fp32: bool = False, dh: Optional[torch.Tensor] = None,
-                 cu_seqlens_cpu=None):
+                 cu_seqlens_cpu=None, state_v_first: bool = True):
     """Backward state-gradient scan (bf16 q / dout).  Returns (dh [S,HV,V,K]
     -- bf16, or fp32 with ``states_in_fp32``; None when ``split_size`` is
     None -- and dh0 [N,HV,V,K] fp32 or None).  The gates may have fewer heads
     than dout (Hg, a divisor of HV: v-head j takes gate head j / (HV / Hg)).
     ``dh`` may be passed preallocated (any capacity; entries past it are not
-    written); a varlen call without it needs ``cu_seqlens_cpu``."""
+    written); a varlen call without it needs ``cu_seqlens_cpu``.  With
+    ``state_v_first=False`` dht, dh and dh0 are [*, HV, K, V] (V contiguous)
+    instead."""
     B, T, Hk, HV, K, V, N, dev, Hg = _state_scan_args(q, dout, "q", "dout", g, g_gamma, gk, gv, dht, "dht",
                                                       cu_seqlens)
     if scale is None:
@@ -442,7 +444,8 @@ def chunk_bwd_dh(q: torch.Tensor, dout: torch.Tensor, g: Optional[torch.Tensor] 
     dh0 = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if output_dh0 else None
     _check(lib().gdn_chunk_bwd_dh(_ptr(q), _ptr(dout), _ptr(g), _ptr(g_gamma), _ptr(gk), _ptr(gv), Hg,
                                   float(scale), _ptr(dht), _ptr(dh), split_size or 0,
-                                  0 if dh is None else dh.shape[0], _dtype_code(sdt), _ptr(dh0),
+                                  0 if dh is None else dh.shape[0], _dtype_code(sdt), int(bool(state_v_first)),
+                                  _ptr(dh0),
                                   _ptr(cu_seqlens), N, B, T, Hk, HV, K, V, chunk_size,
                                   _io_code(torch.bfloat16), _stream(dev)))
     return dh, dh0
@@ -453,17 +456,18 @@ def chunk_fwd_h(k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor] = No
                 gv: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None,
                 cu_seqlens: Optional[torch.Tensor] = None, split_size: Optional[int] = 64,
                 output_final_state: bool = True, chunk_size: int = 64, states_in_fp32: bool = False,
-                h: Optional[torch.Tensor] = None, cu_seqlens_cpu=None):
+                h: Optional[torch.Tensor] = None, cu_seqlens_cpu=None, state_v_first: bool = True):
     """Forward decay-only chunk-state scan (bf16 k / v).  Returns (h
     [S,HV,V,K], the state at the start of every split -- bf16, or fp32 with
     ``states_in_fp32``; None when ``split_size`` is None -- and ht [N,HV,V,K]
-    fp32 or None).  Gate heads and the ``h`` buffer as in ``chunk_bwd_dh``."""
+    fp32 or None).  Gate heads, the ``h`` buffer and ``state_v_first`` (h0,
+    h, ht as [*, HV, K, V] when False) as in ``chunk_bwd_dh``."""
     B, T, Hk, HV, K, V, N, dev, Hg = _state_scan_args(k, v, "k", "v", g, g_gamma, gk, gv, h0, "h0", cu_seqlens)
     sdt = _state_dtype(torch.bfloat16, states_in_fp32)
     h = _states(B, T, HV, V, K, N, dev, split_size, h, "h", cu_seqlens is not None, cu_seqlens_cpu, sdt)
     ht = torch.empty((N, HV, V, K), dtype=torch.float32, device=dev) if output_final_state else None
     _check(lib().gdn_chunk_fwd_h(_ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma), _ptr(gk), _ptr(gv), Hg,
                                  _ptr(h0), _ptr(h), split_size or 0, 0 if h is None else h.shape[0],
-                                 _dtype_code(sdt), _ptr(ht), _ptr(cu_seqlens), N,
+                                 _dtype_code(sdt), int(bool(state_v_first)), _ptr(ht), _ptr(cu_seqlens), N,
                                  B, T, Hk, HV, K, V, chunk_size, _io_code(torch.bfloat16), _stream(dev)))
     return h, ht

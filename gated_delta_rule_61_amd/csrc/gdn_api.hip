@@ -516,7 +516,7 @@ int gdn_decode(const void* q, const void* k, const void* v, const void* a, const
 static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, const float* g,
                       const float* g_gamma, const float* gk, const float* gv, int num_gate_heads,
                       float scale, const float* init, void* snaps, int split_size, long long entries,
-                      int state_dtype, float* fin,
+                      int state_dtype, int state_v_first, float* fin,
                       const int64_t* cu_seqlens, int num_seqs, int B, int T, int Hk, int HV, int K, int V,
                       int chunk_size, int dtype, void* stream) {
   const char* an = fwd ? "k" : "q";
@@ -535,6 +535,8 @@ static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, c
   if ((g != nullptr) + (g_gamma != nullptr) + (gk != nullptr) > 1)
     return fail(GDN_ERR_INVALID_ARGUMENT, "pass at most one of g, g_gamma and gk");
   if (gk && gv) return fail(GDN_ERR_UNSUPPORTED, "gk together with gv is not supported");
+  if (state_v_first != 0 && state_v_first != 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "state_v_first must be 0 or 1 (got %d)", state_v_first);
   if ((long long)B * T >= (1LL << 31) / 64)
     return fail(GDN_ERR_UNSUPPORTED, "B*T too large (got %lld tokens)", (long long)B * T);
   {
@@ -565,6 +567,7 @@ static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, c
   a.dh_cap = snaps ? entries : 0;
   a.cu_seqlens = cu_seqlens; a.N = N; a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
   a.Hg = Hg;
+  a.v_first = state_v_first != 0;
   prof_begin(stage, (hipStream_t)stream);
   const hipError_t e = launch_bwd_dh(a, (hipStream_t)stream);
   prof_end(stage, (hipStream_t)stream);
@@ -575,21 +578,21 @@ static int state_scan(bool fwd, int stage, const void* a_op, const void* b_op, c
 int gdn_chunk_bwd_dh(const void* q, const void* dout, const float* g, const float* g_gamma,
                      const float* gk, const float* gv, int num_gate_heads, float scale,
                      const float* dht, void* dh, int split_size, long long dh_entries, int state_dtype,
-                     float* dh0, const int64_t* cu_seqlens, int num_seqs, int B, int T,
+                     int state_v_first, float* dh0, const int64_t* cu_seqlens, int num_seqs, int B, int T,
                      int Hk, int HV, int K, int V, int chunk_size, int dtype, void* stream) {
   return state_scan(false, GDN_STAGE_BWD_DH, q, dout, g, g_gamma, gk, gv, num_gate_heads, scale, dht, dh,
-                    split_size, dh_entries, state_dtype, dh0, cu_seqlens, num_seqs, B, T, Hk, HV, K, V,
-                    chunk_size, dtype, stream);
+                    split_size, dh_entries, state_dtype, state_v_first, dh0, cu_seqlens, num_seqs, B, T, Hk,
+                    HV, K, V, chunk_size, dtype, stream);
 }
 
 int gdn_chunk_fwd_h(const void* k, const void* v, const float* g, const float* g_gamma,
                     const float* gk, const float* gv, int num_gate_heads, const float* h0, void* h,
-                    int split_size, long long h_entries, int state_dtype, float* ht,
+                    int split_size, long long h_entries, int state_dtype, int state_v_first, float* ht,
                     const int64_t* cu_seqlens, int num_seqs, int B, int T, int Hk, int HV,
                     int K, int V, int chunk_size, int dtype, void* stream) {
   return state_scan(true, GDN_STAGE_FWD_H, k, v, g, g_gamma, gk, gv, num_gate_heads, 1.f, h0, h, split_size,
-                    h_entries, state_dtype, ht, cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size, dtype,
-                    stream);
+                    h_entries, state_dtype, state_v_first, ht, cu_seqlens, num_seqs, B, T, Hk, HV, K, V,
+                    chunk_size, dtype, stream);
 }
 
 int gdn_state_to_pool(const float* ht, const int32_t* indices, void* pool_state, int N, int HV,

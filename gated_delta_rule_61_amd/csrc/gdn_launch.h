@@ -33,12 +33,13 @@ struct BwdDhArgs {
   const float* gv;                 // [B*T, Hg, V] or nullptr; not with gk
   bool fwd;
   float scale;
-  const float* dht;                // [N, HV, V, K] or nullptr
-  void* dh;                        // [splits, HV, V, K] fp32 or bf16 (dh_bf16), or nullptr
+  const float* dht;                // [N, HV, V, K] (v_first) or [N, HV, K, V], or nullptr
+  void* dh;                        // [splits, HV, V, K] or [splits, HV, K, V], fp32 or bf16 (dh_bf16), or nullptr
   bool dh_bf16;
   long long dh_cap;                // entries of dh; later entries are not written
   int split_chunks;
-  float* dh0;                      // [N, HV, V, K] or nullptr
+  float* dh0;                      // [N, HV, V, K] or [N, HV, K, V], or nullptr
+  bool v_first;                    // state layout: V-first (K contiguous) or key-first (V contiguous)
   const int64_t* cu_seqlens;
   int N, B, T, Hk, HV, K, V;
   int Hg;                          // gate heads (HV % Hg == 0)

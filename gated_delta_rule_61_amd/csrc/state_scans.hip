@@ -126,6 +126,62 @@ __device__ __forceinline__ void store_tile(void* dst, size_t base, const f32x4 (
   }
 }
 
+// The same accumulators into a key-first [*, HV, K, V] array (V contiguous:
+// the state scans' layout without state_v_first): `eb` is the entry's first
+// element, key0 the wave's first key, col the lane's first column.  One 4- or
+// 2-byte store per element; the 16 lanes of a key row cover 16 consecutive
+// columns.
+template <int DK, int RB, int CBN>
+__device__ __forceinline__ void store_tile_kfirst(void* dst, size_t eb, int key0, int col,
+                                                  const f32x4 (&acc)[RB][CBN], int gq, bool bf) {
+  constexpr int DV = DK;
+#pragma unroll
+  for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t off = eb + (size_t)(key0 + 16 * rb + 4 * gq + i) * DV + col + 16 * cb;
+        if (bf)
+          reinterpret_cast<bf16_t*>(dst)[off] = f2bf(acc[rb][cb][i]);
+        else
+          reinterpret_cast<float*>(dst)[off] = acc[rb][cb][i];
+      }
+}
+
+// A work-group's accumulators into entry e of a state array, V-first
+// ([*, HV, V, K]) or key-first ([*, HV, K, V]).
+template <int DK, int RB, int CBN>
+__device__ __forceinline__ void store_state_tile(void* dst, size_t e, int HV, int j, int key0, int col,
+                                                 const f32x4 (&acc)[RB][CBN], int gq, bool bf, bool vfirst) {
+  const size_t eb = (e * HV + j) * (size_t)DK * DK;
+  if (vfirst)
+    store_tile<DK, RB, CBN>(dst, eb + (size_t)col * DK + key0, acc, gq, bf);
+  else
+    store_tile_kfirst<DK, RB, CBN>(dst, eb, key0, col, acc, gq, bf);
+}
+
+// The initial state of the accumulators (same lane layout) from entry `sh`
+// of a fp32 state array, V-first or key-first.
+template <int DK, int RB, int CBN>
+__device__ __forceinline__ void load_state_tile(const float* src, size_t sh, int key0, int col,
+                                                f32x4 (&acc)[RB][CBN], int gq, bool vfirst) {
+  const size_t eb = sh * (size_t)DK * DK;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) {
+      if (vfirst) {
+        const float4 x = *reinterpret_cast<const float4*>(src + eb + (size_t)(col + 16 * cb) * DK + key0 + 16 * rb +
+                                                          4 * gq);
+        acc[rb][cb] = f32x4{x.x, x.y, x.z, x.w};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rb][cb][i] = src[eb + (size_t)(key0 + 16 * rb + 4 * gq + i) * DK + col + 16 * cb];
+      }
+    }
+}
+
 // Per-key-channel gate (gk): the gated operand is the A side (q / k), one
 // thread per key channel forms the chunk-local cumulative gates in LDS, the
 // value side transposes raw; three barriers per chunk.
@@ -133,7 +189,8 @@ template <int DK, bool FWD>
 __global__ __launch_bounds__(256) void state_scan_gk_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ gk, float scale,
     const float* __restrict__ dht, void* __restrict__ dh, int nts, int sbf16, long long scap,
-    float* __restrict__ dh0, const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV, int Hg) {
+    float* __restrict__ dh0, const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV, int Hg,
+    int vfirst) {
   constexpr int DV = DK;
   constexpr int BVT = BVK, CBN = BVT / 16;
   constexpr int RW = DK / 4;          // key rows per wave
@@ -174,26 +231,21 @@ __global__ __launch_bounds__(256) void state_scan_gk_kernel(
     eos = bos + Tlen;
   }
   const int NC = (eos - bos + BT - 1) / BT;
-  const size_t hbase = (size_t)sh * DV * DK;   // [N, HV, V, K] arrays
   const size_t sbase = dh ? (size_t)snapshot_offset(cu, sq, Tlen, nts * BT) : 0;
 
   // accumulators: block (rb, cb), lane (n, gq): key row RW w + 16 rb + 4 gq + i, column v0 + 16 cb + n
   f32x4 acc[RB][CBN];
+  if (dht) {
+    load_state_tile<DK, RB, CBN>(dht, sh, RW * w, v0 + n, acc, gq, vfirst != 0);
+  } else {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb) {
-      if (dht) {
-        const float4 x = *reinterpret_cast<const float4*>(
-            dht + hbase + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq);
-        acc[rb][cb] = f32x4{x.x, x.y, x.z, x.w};
-      } else {
-        acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  // the state into a [*, HV, V, K] array at entry `e` (fp32, or bf16 when `bf`)
+      for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // the state into entry `e` of a state array (fp32, or bf16 when `bf`)
   auto store_state = [&](void* dst, size_t e, bool bf) {
-    store_tile<DK, RB, CBN>(dst, (e * HV + j) * (size_t)DV * DK + (size_t)(v0 + n) * DK + RW * w, acc, gq, bf);
+    store_state_tile<DK, RB, CBN>(dst, e, HV, j, RW * w, v0 + n, acc, gq, bf, vfirst != 0);
   };
 
   // this thread's 8 x 8 block: q (waves 0 .. NQB / 64 - 1) or dO (the next
@@ -352,7 +404,8 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ g,
     const float* __restrict__ gamma, const float* __restrict__ gvp, float scale,
     const float* __restrict__ dht, void* __restrict__ dh, int nts, int sbf16, long long scap,
-    float* __restrict__ dh0, const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV, int Hg) {
+    float* __restrict__ dh0, const int64_t* __restrict__ cu, int Tlen, int N, int Hk, int HV, int Hg,
+    int vfirst) {
   constexpr int DV = DK;
   constexpr int BVT = BVS, CBN = BVT / 16;
   constexpr int RW = DK / 4;
@@ -392,25 +445,20 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
     eos = bos + Tlen;
   }
   const int NC = (eos - bos + BT - 1) / BT;
-  const size_t hbase = (size_t)sh * DV * DK;
   const size_t sbase = dh ? (size_t)snapshot_offset(cu, sq, Tlen, nts * BT) : 0;
 
   f32x4 acc[RB][CBN];
+  if (dht) {
+    load_state_tile<DK, RB, CBN>(dht, sh, RW * w, v0 + n, acc, gq, vfirst != 0);
+  } else {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb) {
-      if (dht) {
-        const float4 x = *reinterpret_cast<const float4*>(
-            dht + hbase + (size_t)(v0 + 16 * cb + n) * DK + RW * w + 16 * rb + 4 * gq);
-        acc[rb][cb] = f32x4{x.x, x.y, x.z, x.w};
-      } else {
-        acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  // the state into a [*, HV, V, K] array at entry `e` (fp32, or bf16 when `bf`)
+      for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // the state into entry `e` of a state array (fp32, or bf16 when `bf`)
   auto store_state = [&](void* dst, size_t e, bool bf) {
-    store_tile<DK, RB, CBN>(dst, (e * HV + j) * (size_t)DV * DK + (size_t)(v0 + n) * DK + RW * w, acc, gq, bf);
+    store_state_tile<DK, RB, CBN>(dst, e, HV, j, RW * w, v0 + n, acc, gq, bf, vfirst != 0);
   };
 
   // roles: the first QB / 64 waves -> q blocks; waves 2, 3 -> dO (columns
@@ -628,7 +676,7 @@ __global__ __launch_bounds__(320) void state_scan_ring_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ dout, const float* __restrict__ g,
     const float* __restrict__ gamma, float scale, const float* __restrict__ dht, void* __restrict__ dh,
     int nts, int sbf16, long long scap, float* __restrict__ dh0, const int64_t* __restrict__ cu, int Tlen,
-    int N, int Hk, int HV, int Hg) {
+    int N, int Hk, int HV, int Hg, int vfirst) {
   constexpr int DV = DK, BV = BVS, CBN = 1;
   constexpr int RW = DK / 4, RB = RW / 16;
   constexpr int NSL = 4, LEAD = NSL - 1;  // LDS slots; chunks loaded ahead of their use
@@ -747,22 +795,18 @@ __global__ __launch_bounds__(320) void state_scan_ring_kernel(
   }
 
   // =================== compute waves
-  const size_t hbase = (size_t)sh * DV * DK;
   const size_t sbase = ST ? (size_t)snapshot_offset(cu, sq, Tlen, nts * BT) : 0;
   // accumulators: lane (n, gq) of block rb holds keys DK/4 w + 16 rb + 4 gq + i, column v0 + n
   f32x4 acc[RB][CBN];
+  if (dht) {
+    load_state_tile<DK, RB, CBN>(dht, sh, RW * w, v0 + n, acc, gq, vfirst != 0);
+  } else {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if (dht) {
-      const float4 x = *reinterpret_cast<const float4*>(dht + hbase + (size_t)(v0 + n) * DK + RW * w + 16 * rb + 4 * gq);
-      acc[rb][0] = f32x4{x.x, x.y, x.z, x.w};
-    } else {
-      acc[rb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int rb = 0; rb < RB; ++rb) acc[rb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float gam = (!g && gamma) ? gamma[jg] : 0.f;
   auto store_state = [&](void* dst, size_t e, bool bf) {
-    store_tile<DK, RB, CBN>(dst, (e * HV + j) * (size_t)DV * DK + (size_t)(v0 + n) * DK + RW * w, acc, gq, bf);
+    store_state_tile<DK, RB, CBN>(dst, e, HV, j, RW * w, v0 + n, acc, gq, bf, vfirst != 0);
   };
   // A-fragment byte offsets within a q tile: block rb, slab s, token half h
   int o_a[RB][2][2];
@@ -846,8 +890,8 @@ __global__ __launch_bounds__(320) void state_scan_ring_kernel(
     for (int rb = 0; rb < RB; ++rb) acc[rb][0] = mma_bf(a[rb][0], Bl[0], acc[rb][0]);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) p1[rb] = mma_bf(a[rb][1], Bl[1], p1[rb]);
-    if (st) store_tile<DK, RB, CBN>(dh, ((sbase + ic / nts) * HV + j) * (size_t)DV * DK + (size_t)(v0 + n) * DK + RW * w,
-                                    prev, gq, sbf16 != 0);
+    if (st) store_state_tile<DK, RB, CBN>(dh, sbase + ic / nts, HV, j, RW * w, v0 + n, prev, gq, sbf16 != 0,
+                                          vfirst != 0);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[rb][0] += p1[rb];
   };
@@ -867,7 +911,7 @@ hipError_t launch_k(const BwdDhArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((state_scan_gk_kernel<DK, FWD>), dim3((unsigned)blocks), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.dout, a.gk, a.scale, a.dht, a.dh,
                      a.split_chunks, a.dh_bf16 ? 1 : 0, a.dh_cap, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV,
-                     a.Hg);
+                     a.Hg, a.v_first ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -881,7 +925,7 @@ hipError_t launch_gdn(const BwdDhArgs& a, hipStream_t s) {
     auto ring = a.dh ? state_scan_ring_kernel<DK, FWD, true> : state_scan_ring_kernel<DK, FWD, false>;
     hipLaunchKernelGGL(ring, dim3((unsigned)blocks), dim3(320), 0, s, (const bf16_t*)a.q, (const bf16_t*)a.dout,
                        a.g, a.g_gamma, a.scale, a.dht, a.dh, a.split_chunks, a.dh_bf16 ? 1 : 0, a.dh_cap, a.dh0,
-                       a.cu_seqlens, a.T, a.N, a.Hk, a.HV, a.Hg);
+                       a.cu_seqlens, a.T, a.N, a.Hk, a.HV, a.Hg, a.v_first ? 1 : 0);
     return hipGetLastError();
   }
   // without stored states the loop issues no stores, so the waits for the
@@ -891,7 +935,7 @@ hipError_t launch_gdn(const BwdDhArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s,
                      (const bf16_t*)a.q, (const bf16_t*)a.dout, a.g, a.g_gamma, a.gv, a.scale, a.dht, a.dh,
                      a.split_chunks, a.dh_bf16 ? 1 : 0, a.dh_cap, a.dh0, a.cu_seqlens, a.T, a.N, a.Hk, a.HV,
-                     a.Hg);
+                     a.Hg, a.v_first ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -290,6 +290,10 @@ int gdn_decode(const void* q, const void* k, const void* v,
  *   split_size   a positive multiple of 64, read when dh is not NULL
  *   dh_entries   capacity of dh in [HV, V, K] entries (see the conventions)
  *   state_dtype  GDN_DTYPE_F32 or GDN_DTYPE_BF16: dtype of dh
+ *   state_v_first  layout of dht, dh and dh0 (the page's state_v_first):
+ *                1 = [*, HV, V, K] (K contiguous, as documented here and as
+ *                the prefill and decode keep their states; the fast layout),
+ *                0 = [*, HV, K, V] (V contiguous, the page's default)
  *   dh0          [N, HV, V, K]  fp32 out (gradient of the initial state), or NULL
  *   cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size  as in gdn_chunk_fwd
  * Supported: dtype = GDN_DTYPE_BF16, K = V in {64, 128}, chunk_size = 64.
@@ -299,14 +303,15 @@ int gdn_chunk_bwd_dh(const void* q, const void* dout,
                      const float* g, const float* g_gamma, const float* gk,
                      const float* gv, int num_gate_heads, float scale,
                      const float* dht, void* dh, int split_size,
-                     long long dh_entries, int state_dtype, float* dh0,
+                     long long dh_entries, int state_dtype,
+                     int state_v_first, float* dh0,
                      const int64_t* cu_seqlens, int num_seqs,
                      int B, int T, int Hk, int HV, int K, int V,
                      int chunk_size, int dtype, void* stream);
 
 /*
  * Forward decay-only chunk-state scan ("fla ops/common/chunk_h.py",
- * chunk_fwd_kernel_h, with the state-V-first layout), bf16 io.  Per sequence
+ * chunk_fwd_kernel_h, either state layout), bf16 io.  Per sequence
  * and v-head, over the chunks of 64 tokens in order, with h [V, K] the state
  * at the start of the current chunk:
  *   start:       h = h0 (or zeros)
@@ -331,6 +336,8 @@ int gdn_chunk_bwd_dh(const void* q, const void* dout,
  *   split_size   a positive multiple of 64, read when h is not NULL
  *   h_entries    capacity of h in [HV, V, K] entries (see the conventions)
  *   state_dtype  GDN_DTYPE_F32 or GDN_DTYPE_BF16: dtype of h
+ *   state_v_first  layout of h0, h and ht, as in gdn_chunk_bwd_dh (1 =
+ *                [*, HV, V, K] as documented here, 0 = [*, HV, K, V])
  *   ht           [N, HV, V, K]  fp32 out (final state), or NULL
  *   cu_seqlens, num_seqs, B, T, Hk, HV, K, V, chunk_size  as in gdn_chunk_fwd
  * Supported: dtype = GDN_DTYPE_BF16, K = V in {64, 128}, chunk_size = 64.
@@ -341,7 +348,7 @@ int gdn_chunk_fwd_h(const void* k, const void* v,
                     const float* g, const float* g_gamma, const float* gk,
                     const float* gv, int num_gate_heads, const float* h0,
                     void* h, int split_size, long long h_entries,
-                    int state_dtype, float* ht,
+                    int state_dtype, int state_v_first, float* ht,
                     const int64_t* cu_seqlens, int num_seqs,
                     int B, int T, int Hk, int HV, int K, int V,
                     int chunk_size, int dtype, void* stream);

@@ -191,11 +191,11 @@ def test_state_to_pool_empty_is_a_no_op(L):
 
 
 def _bwd(L, q=FAKE, do=FAKE, g=None, gg=None, gk=None, gv=None, hg=0, dht=None, dh=None, ss=64, se=1 << 30, sdt=0,
-         dh0=FAKE, cu=None, ns=0, B=1, T=64, Hk=1, HV=1, K=64, V=64, cs=64, dt=1, fwd=False):
+         vf=1, dh0=FAKE, cu=None, ns=0, B=1, T=64, Hk=1, HV=1, K=64, V=64, cs=64, dt=1, fwd=False):
     f = L.gdn_chunk_fwd_h if fwd else L.gdn_chunk_bwd_dh
     if fwd:
-        return f(q, do, g, gg, gk, gv, hg, dht, dh, ss, se, sdt, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
-    return f(q, do, g, gg, gk, gv, hg, 1.0, dht, dh, ss, se, sdt, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
+        return f(q, do, g, gg, gk, gv, hg, dht, dh, ss, se, sdt, vf, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
+    return f(q, do, g, gg, gk, gv, hg, 1.0, dht, dh, ss, se, sdt, vf, dh0, cu, ns, B, T, Hk, HV, K, V, cs, dt, None)
 
 
 @pytest.mark.parametrize("fwd", [False, True])
@@ -212,6 +212,7 @@ def _bwd(L, q=FAKE, do=FAKE, g=None, gg=None, gk=None, gv=None, hg=0, dht=None, 
     (dict(HV=4, Hk=4, hg=3), 1, b"gate heads"),
     (dict(dh=FAKE, B=3, T=100, se=5), 1, b"6 needed"),
     (dict(dh=FAKE, sdt=2), 1, b"state dtype"),
+    (dict(vf=2), 1, b"state_v_first"),
 ])
 def test_state_scans_reject(L, kw, status, msg, fwd):
     assert _bwd(L, fwd=fwd, **kw) == status

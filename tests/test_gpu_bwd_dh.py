@@ -16,7 +16,9 @@ DEV = "cuda:0"
 dv = lambda t: None if t is None else t.to(DEV)
 
 
-def _case(inp, gate, S, dht_std=0.1, seed=0, fp32_states=False, gate_heads=None):
+def _case(inp, gate, S, dht_std=0.1, seed=0, fp32_states=False, gate_heads=None, v_first=True):
+    """``v_first=False``: dht goes in, and dh / dh0 come out, as
+    [*, HV, K, V]; they are transposed back for the comparison."""
     B, T, Hk, HV, K, V = inp.dims
     rng = np.random.default_rng(seed)
     do = torch.from_numpy(rng.standard_normal((B, T, HV, V)).astype(np.float32)).to(torch.bfloat16)
@@ -33,11 +35,14 @@ def _case(inp, gate, S, dht_std=0.1, seed=0, fp32_states=False, gate_heads=None)
         cut = lambda x, ax: None if x is None else x.narrow(ax, 0, gate_heads).contiguous()
         g, gk, gv, gamma = cut(g, 2), cut(gk, 2), cut(gv, 2), cut(gamma, 0)
     print(f"bwd dh {inp.name} gate={gate} split={S} dims={inp.dims} fp32 states={fp32_states} "
-          f"gate heads={gate_heads}", flush=True)
+          f"gate heads={gate_heads} v_first={v_first}", flush=True)
+    lay = (lambda x: x) if v_first else (lambda x: None if x is None else x.transpose(-1, -2).contiguous())
     dh, dh0 = binding.chunk_bwd_dh(dv(inp.q), dv(do), g=dv(g), g_gamma=dv(gamma), gk=dv(gk), gv=dv(gv),
-                                   scale=inp.scale, dht=dv(dht), cu_seqlens=dv(inp.cu_seqlens), split_size=S,
-                                   states_in_fp32=fp32_states, cu_seqlens_cpu=inp.cu_seqlens)
+                                   scale=inp.scale, dht=dv(lay(dht)), cu_seqlens=dv(inp.cu_seqlens), split_size=S,
+                                   states_in_fp32=fp32_states, cu_seqlens_cpu=inp.cu_seqlens,
+                                   state_v_first=v_first)
     torch.cuda.synchronize()
+    dh, dh0 = lay(dh), lay(dh0)
     assert dh.dtype == (torch.float32 if fp32_states else torch.bfloat16)
     dh_ref, dh0_ref = oracle.state_grad_scan(inp.q, do, inp.scale, g=g, g_gamma=gamma, gk=gk, gv=gv, dht=dht,
                                              cu_seqlens=inp.cu_seqlens, split_size=S)
@@ -53,6 +58,24 @@ def test_bwd_dh_scalar_gate_varlen(gate, fp32_states):
     inp = workloads.make_prefill(1, 330, 2, 4, 128, 128, dtype=torch.bfloat16, seed=60, h0=True,
                                  seqlens=[200, 1, 129], name="bwd_varlen")
     _case(inp, gate, 64, seed=61, fp32_states=fp32_states)
+
+
+@pytest.mark.parametrize("fp32_states", [False, True])
+@pytest.mark.parametrize("gate", ["gdn", "gamma", None, "gv", "gamma+gv", "kda"])
+def test_bwd_dh_key_first_layout(gate, fp32_states):
+    """The page's default state layout ([*, HV, K, V], V contiguous) for
+    dht, dh and dh0, in each of the three kernels (scalar / no gate, gv, gk)."""
+    inp = workloads.make_prefill(1, 330, 2, 4, 128, 128, dtype=torch.bfloat16, seed=68, h0=True,
+                                 gate="kda" if gate == "kda" else "gdn", seqlens=[200, 1, 129],
+                                 name="bwd_kfirst")
+    _case(inp, gate, 64, seed=69, fp32_states=fp32_states, v_first=False)
+
+
+@pytest.mark.parametrize("gate", ["gamma", "gdn+gv", "kda"])
+def test_bwd_dh_key_first_k64(gate):
+    inp = workloads.make_prefill(2, 150, 1, 2, 64, 64, dtype=torch.bfloat16, seed=87,
+                                 gate="kda" if gate == "kda" else "gdn", name="bwd_kfirst_K64")
+    _case(inp, gate, 128, seed=88, v_first=False)
 
 
 @pytest.mark.parametrize("gate", ["gv", "gdn+gv"])

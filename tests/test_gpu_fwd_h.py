@@ -34,15 +34,19 @@ def _rel(t):
     return STATE_SCAN_REL if t.dtype == torch.float32 else None
 
 
-def _case(inp, gate, S, seed=0, fp32_states=False):
+def _case(inp, gate, S, seed=0, fp32_states=False, v_first=True):
+    """``v_first=False``: h0 goes in, and h / ht come out, as [*, HV, K, V];
+    they are transposed back for the comparison."""
     rng = np.random.default_rng(seed)
     g, gamma, gk, gv = _gates(inp, gate, rng)
     print(f"fwd h {inp.name} gate={gate} split={S} dims={inp.dims} h0={inp.h0 is not None} "
-          f"fp32 states={fp32_states}", flush=True)
+          f"fp32 states={fp32_states} v_first={v_first}", flush=True)
+    lay = (lambda x: x) if v_first else (lambda x: None if x is None else x.transpose(-1, -2).contiguous())
     h, ht = binding.chunk_fwd_h(dv(inp.k), dv(inp.v), g=dv(g), g_gamma=dv(gamma), gk=dv(gk), gv=dv(gv),
-                                h0=dv(inp.h0), cu_seqlens=dv(inp.cu_seqlens), split_size=S,
-                                states_in_fp32=fp32_states, cu_seqlens_cpu=inp.cu_seqlens)
+                                h0=dv(lay(inp.h0)), cu_seqlens=dv(inp.cu_seqlens), split_size=S,
+                                states_in_fp32=fp32_states, cu_seqlens_cpu=inp.cu_seqlens, state_v_first=v_first)
     torch.cuda.synchronize()
+    h, ht = lay(h), lay(ht)
     assert h.dtype == (torch.float32 if fp32_states else torch.bfloat16)
     h_ref, ht_ref = oracle.state_scan(inp.k, inp.v, g=g, g_gamma=gamma, gk=gk, gv=gv, h0=inp.h0,
                                       cu_seqlens=inp.cu_seqlens, split_size=S)
@@ -58,6 +62,24 @@ def test_fwd_h_varlen_gqa(gate, fp32_states):
     inp = workloads.make_prefill(1, 331, 2, 4, 128, 128, dtype=torch.bfloat16, seed=70, h0=True,
                                  seqlens=[200, 1, 0, 130], name="fwd_h_varlen")
     _case(inp, gate, 64, seed=71, fp32_states=fp32_states)
+
+
+@pytest.mark.parametrize("fp32_states", [False, True])
+@pytest.mark.parametrize("gate", ["gdn", "gamma", None, "gv", "gdn+gv", "kda"])
+def test_fwd_h_key_first_layout(gate, fp32_states):
+    """The page's default state layout ([*, HV, K, V], V contiguous) for h0,
+    h and ht, in each of the three kernels (scalar / no gate, gv, gk)."""
+    inp = workloads.make_prefill(1, 331, 2, 4, 128, 128, dtype=torch.bfloat16, seed=83, h0=True,
+                                 gate="kda" if gate == "kda" else "gdn", seqlens=[200, 1, 0, 130],
+                                 name="fwd_h_kfirst")
+    _case(inp, gate, 64, seed=84, fp32_states=fp32_states, v_first=False)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "gv", "kda"])
+def test_fwd_h_key_first_k64(gate):
+    inp = workloads.make_prefill(2, 150, 1, 2, 64, 64, dtype=torch.bfloat16, seed=85, h0=True,
+                                 gate="kda" if gate == "kda" else "gdn", name="fwd_h_kfirst_K64")
+    _case(inp, gate, 128, seed=86, v_first=False)
 
 
 @pytest.mark.parametrize("gate", ["gdn", "gv", "gdn+gv", "kda"])

@@ -92,9 +92,10 @@ def test_prefill_invalid_boundaries_stay_in_bounds(kda):
         assert torch.equal(ht[n], h0[n]), f"empty sequence {n}: ht differs from h0"
 
 
+@pytest.mark.parametrize("vf", [1, 0], ids=["v_first", "k_first"])
 @pytest.mark.parametrize("fwd", [False, True], ids=["bwd_dh", "fwd_h"])
-def test_state_scan_invalid_boundaries_stay_in_bounds(fwd):
-    print(f"state scan with invalid cu_seqlens {CU}, forward={fwd}", flush=True)
+def test_state_scan_invalid_boundaries_stay_in_bounds(fwd, vf):
+    print(f"state scan with invalid cu_seqlens {CU}, forward={fwd}, state_v_first={vf}", flush=True)
     q, k, v, g, gk, beta, h0, cu = _inputs(310 + fwd)
     L = binding.lib()
     sb, hs = _guarded((8, HV, K, K), torch.bfloat16)
@@ -102,11 +103,11 @@ def test_state_scan_invalid_boundaries_stay_in_bounds(fwd):
     a, b = (k, v) if fwd else (q, v)
     if fwd:
         st = L.gdn_chunk_fwd_h(_p(a), _p(b), _p(g), None, None, None, HV, _p(h0), _p(hs), 64, hs.shape[0],
-                               binding.GDN_DTYPE_BF16, _p(fin), _p(cu), N, 1, T, HK, HV, K, K, 64,
+                               binding.GDN_DTYPE_BF16, vf, _p(fin), _p(cu), N, 1, T, HK, HV, K, K, 64,
                                binding.GDN_DTYPE_BF16, _stream())
     else:
         st = L.gdn_chunk_bwd_dh(_p(a), _p(b), _p(g), None, None, None, HV, ctypes.c_float(K ** -0.5), _p(h0),
-                                _p(hs), 64, hs.shape[0], binding.GDN_DTYPE_BF16, _p(fin), _p(cu), N, 1, T, HK, HV,
+                                _p(hs), 64, hs.shape[0], binding.GDN_DTYPE_BF16, vf, _p(fin), _p(cu), N, 1, T, HK, HV,
                                 K, K, 64, binding.GDN_DTYPE_BF16, _stream())
     assert st == 0, L.gdn_last_error()
     torch.cuda.synchronize()
