@@ -123,6 +123,31 @@ def timed(fn, steps, warmup):
     return ev0.elapsed_time(ev1) / steps
 
 
+def graph_ms_per_call(torch, step, replays, per=8):
+    """Milliseconds per call when `per` back-to-back calls are captured in a
+    HIP graph and the graph is replayed: the launch cost a serving loop pays
+    once per replay instead of once per call."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per):
+            step()
+    settle(g.replay)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(replays):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / (replays * per)
+
+
 def stage_times(binding, torch, step, steps):
     """Average duration of each library stage over `steps` calls: HIP events
     recorded by the library on the launch stream around every kernel."""
@@ -322,6 +347,7 @@ def bench_decode(args, binding, workloads, torch, T, B=256):
 
     ms = timed(step, args.steps, args.warmup)
     kms = stage_times(binding, torch, step, args.steps)["decode"]
+    gms = graph_ms_per_call(torch, step, max(args.steps, 4))
     state_bytes = 2 * B * HV * V * K * 2
     other = (2 * B * T * H * K + 2 * B * T * HV * V + 2 * B * T * HV) * 2 + 2 * HV * 4
     # One kernel per call: the back-to-back loop time per call bounds the
@@ -337,6 +363,8 @@ def bench_decode(args, binding, workloads, torch, T, B=256):
         "total_GBps": round((state_bytes + other) / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round((state_bytes + other) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_ms_bracketed": round(kms, 5),
+        "graph_ms_per_call": round(gms, 5),
+        "graph_tokens_per_s": round(B * T / (gms * 1e-3), 1),
         "method_bytes": state_bytes + other,
         "measured_bytes": meas,
         "traffic_GBps": None if meas is None else round(meas / (ms * 1e-3) / 1e9, 1),
