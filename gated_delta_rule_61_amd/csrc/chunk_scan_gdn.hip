@@ -1,7 +1,8 @@
 // Sequential part of the chunked prefill for bf16 io with the scalar gate,
 // gfx950.  The mathematics is the one of the generic scan: per (sequence,
-// v-head, V-tile), over the chunks in order, with S^T (K x BV, fp32) the state
-// at the chunk start and Ainv, Aqk, G from the intra kernel,
+// v-head, V-tile), over the chunks in order, with S^T (K x BV, fp32; BV the
+// tile's columns) the state at the chunk start and Ainv, Aqk, G from the
+// intra kernel,
 //
 //   X     = diag(e^G) K S^T
 //   R     = beta * (V - X)
@@ -15,7 +16,7 @@
 // recompute_w_u and the output step.)
 //
 // gfx950 design.  Work-group = one (sequence, v-head, 32-column V tile), eight
-// waves, two per SIMD:
+// waves, two per SIMD (the 64-column form is described at the end):
 //   * two state waves, one per 16-column block, keep their S^T (K x 16) in
 //     fp32 MFMA accumulators and run the chain of a chunk,
 //       X = K S^T  ->  R  ->  Vn = Ainv R  ->  S^T update,
@@ -50,6 +51,14 @@
 //     first product, so the chain waits out the LDS latency once;
 //   * two barriers per chunk; the work-groups of one (sequence, head) share an
 //     XCD (its L2), sequences are issued longest first.
+// A CU holds one such work-group at a time (LDS, and two 247-VGPR waves per
+// SIMD).  When the 32-column work-groups would not all run at once, the
+// scalar-gate scan (K = 128) uses 64-column ones instead: four state waves
+// (one per SIMD), two helper waves of two 16-column blocks each, and two
+// movers taking load sets {k, Ainv, v} and {q, Aqk, gate rows}.  The o tile
+// then lives in the v buffer of the chunk's stage, which the state waves have
+// read before the mid-chunk barrier and the movers refill only after the
+// mover that loads v has stored o from it.
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -65,7 +74,7 @@ using namespace tiles;
 // third tile holds K o e^{G_last - G} for the state update, the scalar
 // gate factors are 1 except beta, and S^T decays row by row by the chunk's
 // e^{G_last} (one value per key channel).
-template <int DK, bool KDA>
+template <int DK, bool KDA, int NB>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_scan_bf16_kernel(
     const void* __restrict__ qop, const void* __restrict__ kop, const f16_t* __restrict__ ktop,
     const bf16_t* __restrict__ v, const float* __restrict__ GF, const float* __restrict__ DG,
@@ -76,6 +85,14 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     int Tlen, int ttot, int NT, int N, int Hk, int HV, int V, int dg_rows) {
   typedef Lds<DK> L;
   constexpr int KS = L::KS, KB = L::KB, NQK = L::NQK;
+  // NB 16-column blocks per work-group, one state wave each; two helper
+  // waves of NB / 2 blocks each; the other 6 - NB waves move data
+  static_assert(NB == 2 || (NB == 4 && !KDA), "32 columns, or 64 for the scalar gate");
+  constexpr int BVW = 16 * NB;                 // V columns per work-group
+  constexpr int NHB = NB / 2;                  // column blocks per helper wave
+  constexpr int NMW = 6 - NB;                  // mover waves
+  constexpr int VTB = BT * BVW * 2;            // v tile bytes
+  constexpr int OROW = BVW * 2 + 16;           // padded o row (bytes) of sO
   // q / k tile sources (GDN: the raw bf16 inputs, one row per q / k head;
   // KDA: the gated fp16 operands, head- and slab-major: [HV][DK / 32][tokens][32])
   const char* const qsrc = reinterpret_cast<const char*>(qop);
@@ -84,16 +101,18 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   // tell the stage being filled from the one being read
   __shared__ __attribute__((aligned(16))) char sK0[L::QK], sK1[L::QK], sQ0[L::QK], sQ1[L::QK];
   __shared__ __attribute__((aligned(16))) char sAi0[L::AT], sAi1[L::AT], sAq0[L::AT], sAq1[L::AT];
-  __shared__ __attribute__((aligned(16))) char sV0[L::VT], sV1[L::VT];
+  __shared__ __attribute__((aligned(16))) char sV0[VTB], sV1[VTB];
   __shared__ __attribute__((aligned(16))) float sG0[4][BT], sG1[4][BT];  // gate-factor planes
   // KDA: K o e^{G_last - G} tiles and the chunk's decay row e^{G_last}
   __shared__ __attribute__((aligned(16))) char sT0[KDA ? L::QK : 16], sT1[KDA ? L::QK : 16];
   __shared__ __attribute__((aligned(16))) float sD0[KDA ? DK : 4], sD1[KDA ? DK : 4];
   // S fragments for the output: GDN fp32 (split there into bf16 hi + lo),
   // KDA fp16 (the B operand itself)
-  __shared__ __attribute__((aligned(16))) u32x4 sSF[NSW][KS][KDA ? 1 : 2][64];
-  __shared__ __attribute__((aligned(16))) u32x4 sVnF[NSW][2][64];     // Vn fragments (fp16)
-  __shared__ __attribute__((aligned(16))) char sO[BT * L::OROW];       // o tile
+  __shared__ __attribute__((aligned(16))) u32x4 sSF[NB][KS][KDA ? 1 : 2][64];
+  __shared__ __attribute__((aligned(16))) u32x4 sVnF[NB][2][64];      // Vn fragments (fp16)
+  // o tile; with 64 columns it lives in the v buffer of the chunk's stage
+  // (free after the mid-chunk barrier, refilled only after o has left)
+  __shared__ __attribute__((aligned(16))) char sO[NB == 2 ? BT * OROW : 16];
   __shared__ __attribute__((aligned(16))) uint32_t sSink[64];          // L2-prefetch landing words
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -101,12 +120,12 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   // wave roles; wave w runs on SIMD w % 4: state waves on SIMDs 0 and 1,
   // helpers on 2 and 3, one mover on each SIMD (placing both state waves
   // on one SIMD, or a state wave beside the other block's helper, was slower)
-  const int role = w < 2 ? 0 : w < 4 ? 1 : 2;
-  const int ridx = w < 4 ? (w & 1) : w - 4;
+  const int role = w < NB ? 0 : w < NB + 2 ? 1 : 2;
+  const int ridx = NB == 2 ? (w < 4 ? (w & 1) : w - 4) : (w < NB ? w : w < NB + 2 ? w - NB : w - NB - 2);
   const bool is_state = role == 0;
   const int cb = ridx;                    // 16-column block (state, helper) / mover index
   const int n = lane & 15, g = lane >> 4;
-  const int NVT = V / BV;
+  const int NVT = V / BVW;
 
   // ---- work-group -> (sequence, head, V-tile).  Work-group ids are dealt
   // round-robin to the 8 XCDs.  The unit is a (sequence, q / k head): its
@@ -136,7 +155,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     eos = bos + Tlen;
   }
   const int jo = KDA ? j : j / (HV / Hk);   // row of the q / k tile sources
-  const int v0 = vt * BV;
+  const int v0 = vt * BVW;
   int NC = (eos - bos + BT - 1) / BT;
   // KDA: global index of the sequence's first chunk (row of the decay rows);
   // only non-monotone (invalid) varlen boundaries can reach past their end
@@ -246,7 +265,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         const int t0 = perm_row(tb, 4 * g);
         ex[tb] = KDA ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&sG[0][t0]);
         bz[tb] = *reinterpret_cast<const f32x4*>(&sG[2][t0]);
-        vr[tb] = ld_tr(sV + (perm_row(tb, 4 * g + (n >> 2)) * BV + 16 * cb + 4 * (n & 3)) * 2);
+        vr[tb] = ld_tr(sV + (perm_row(tb, 4 * g + (n >> 2)) * BVW + 16 * cb + 4 * (n & 3)) * 2);
       }
       u32x4 Ai[6];
 #pragma unroll
@@ -361,62 +380,84 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         store_nt16(ht + hbase + (size_t)(v0 + 16 * cb + n) * DK + perm_row(kb, 4 * g), St[kb]);
     }
   } else if (role == 1) {
-    // =================== helper wave: the output of 16 columns
+    // =================== helper wave: the output of NB / 2 16-column blocks
     __syncthreads();
     auto chunk = [&](auto stg, int c) __attribute__((always_inline)) {
       constexpr bool S1 = decltype(stg)::value;
       const char* sQ = S1 ? sQ1 : sQ0;
       const char* sAq = S1 ? sAq1 : sAq0;
       const float (*sG)[BT] = S1 ? sG1 : sG0;
+      // the o tile: sO, or (64 columns) this stage's v buffer, whose 128-byte
+      // rows take a 16-byte-unit XOR swizzle by row / 8
+      char* oT = NB == 2 ? sO : const_cast<char*>(S1 ? sV1 : sV0);
       // the state waves' reads at the start of a chunk head the chain; the
       // helpers (which have slack) and the movers stay off the LDS meanwhile
       // (about 500 and 250 cycles; measured at DK = 128)
       if constexpr (DK == 128) __builtin_amdgcn_s_sleep(8);
       // ---- Oi = Q S^T from the published fp32 S (split into bf16 hi + lo);
       // KDA: (Q o e^G) S^T with the published fp16 S
-      f32x4 Oi[4];
+      f32x4 Oi[NHB][4];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) Oi[tb] = zero4();
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) Oi[hb][tb] = zero4();
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         u32x4 A[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) A[tb] = ld16(sQ + qk_off<DK>(perm_row(tb, n), 4 * s + g));
-        if constexpr (KDA) {
-          const u32x4 bs = sSF[cb][s][0][lane];
 #pragma unroll
-          for (int tb = 0; tb < 4; ++tb) Oi[tb] = mma_h(A[tb], bs, Oi[tb]);
-        } else {
-          u32x4 bh, bl;
-          split_bf(__builtin_bit_cast(f32x4, sSF[cb][s][0][lane]),
-                   __builtin_bit_cast(f32x4, sSF[cb][s][KDA ? 0 : 1][lane]), bh, bl);
+        for (int hb = 0; hb < NHB; ++hb) {
+          const int cbh = cb * NHB + hb;
+          if constexpr (KDA) {
+            const u32x4 bs = sSF[cbh][s][0][lane];
 #pragma unroll
-          for (int tb = 0; tb < 4; ++tb) Oi[tb] = mma_bf(A[tb], bh, Oi[tb]);
+            for (int tb = 0; tb < 4; ++tb) Oi[hb][tb] = mma_h(A[tb], bs, Oi[hb][tb]);
+          } else {
+            u32x4 bh, bl;
+            split_bf(__builtin_bit_cast(f32x4, sSF[cbh][s][0][lane]),
+                     __builtin_bit_cast(f32x4, sSF[cbh][s][KDA ? 0 : 1][lane]), bh, bl);
 #pragma unroll
-          for (int tb = 0; tb < 4; ++tb) Oi[tb] = mma_bf(A[tb], bl, Oi[tb]);
+            for (int tb = 0; tb < 4; ++tb) Oi[hb][tb] = mma_bf(A[tb], bh, Oi[hb][tb]);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) Oi[hb][tb] = mma_bf(A[tb], bl, Oi[hb][tb]);
+          }
         }
       }
       lds_barrier();
 
       // ---- O = scale e^G Oi + Aqk Vn -> LDS tile
-      const u32x4 vf0 = sVnF[cb][0][lane], vf1 = sVnF[cb][1][lane];
+      u32x4 vf[NHB][2];
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        vf[hb][0] = sVnF[cb * NHB + hb][0][lane];
+        vf[hb][1] = sVnF[cb * NHB + hb][1][lane];
+      }
       u32x4 Aq[6];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) Aq[tb] = ld16(sAq + a_off(perm_row(tb, n), g));
       Aq[4] = ld16(sAq + a_off(perm_row(2, n), 4 + g));
       Aq[5] = ld16(sAq + a_off(perm_row(3, n), 4 + g));
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const f32x4 ex = KDA ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&sG[0][perm_row(tb, 4 * g)]);
-        f32x4 acc;
+      for (int hb = 0; hb < NHB; ++hb) {
+        const int cbh = cb * NHB + hb;
+        const u32x4 vf0 = vf[hb][0], vf1 = vf[hb][1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = Oi[tb][i] * (scale * ex[i]);
-        acc = mma_h(Aq[tb], vf0, acc);
-        if (tb >= 2) acc = mma_h(Aq[tb + 2], vf1, acc);
+        for (int tb = 0; tb < 4; ++tb) {
+          const f32x4 ex = KDA ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&sG[0][perm_row(tb, 4 * g)]);
+          f32x4 acc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<bf16_t*>(sO + perm_row(tb, 4 * g + i) * L::OROW + 2 * (16 * cb + n)) =
-              f2bf(acc[i]);
+          for (int i = 0; i < 4; ++i) acc[i] = Oi[hb][tb][i] * (scale * ex[i]);
+          acc = mma_h(Aq[tb], vf0, acc);
+          if (tb >= 2) acc = mma_h(Aq[tb + 2], vf1, acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = perm_row(tb, 4 * g + i), col = 16 * cbh + n;
+            const int ob = NB == 2 ? row * OROW + 2 * col
+                                   : row * (2 * BVW) + (((col >> 3) ^ ((row >> 3) & 7)) << 4) + 2 * (col & 7);
+            *reinterpret_cast<bf16_t*>(oT + ob) = f2bf(acc[i]);
+          }
+        }
       }
       lds_barrier();
     };
@@ -426,19 +467,22 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     }
   } else {
     // =================== mover wave: global <-> LDS traffic
-    // Direct-to-LDS loads of the next chunk into the other stage; each mover
-    // also stores a quarter of the o tile.  Load sets (mr): GDN: 0 k, 1 q,
-    // 2 Ainv and v, 3 Aqk and the gate rows.  KDA: 0 K o e^G and v,
-    // 1 Q o e^G, the beta row and the decay row, 2 K o e^{G_last - G},
-    // 3 Ainv and Aqk.
+    // Direct-to-LDS loads of the next chunk into the other stage; with 32
+    // columns each of the four movers also stores a quarter of the o tile.
+    // Load sets (mr): GDN: 0 k, 1 q, 2 Ainv and v, 3 Aqk and the gate rows.
+    // KDA: 0 K o e^G and v, 1 Q o e^G, the beta row and the decay row,
+    // 2 K o e^{G_last - G}, 3 Ainv and Aqk.  With 64 columns two movers
+    // take sets {0, 2} and {1, 3}; the one that loads v also stores the
+    // whole o tile, which sits in the v buffer its next loads refill.
     const int mv = ridx;
     // load set of this mover: movers 0 and 1 share SIMDs with the state
     // waves, which leave them fewer issue slots, so they take the lighter
     // sets (GDN: Ainv + v, Aqk + gates; KDA: K o e^{G_last - G}, Ainv + Aqk)
-    const int mr = (mv + 2) & 3;
+    const int mr = NB == 2 ? (mv + 2) & 3 : mv + 2;
+    constexpr int NVL = VTB / 1024;              // 1 KB loads per v tile
     // per-lane byte offsets within a full chunk: LDS slot (row, unit')
     // receives global unit unit' ^ swizzle(row)
-    uint32_t o_qk[NQK], o_a[8], o_v[4];
+    uint32_t o_qk[NQK], o_a[8], o_v[NVL];
     // KDA's gated planes are head- and slab-major (a chunk's 32-channel slab
     // is one 4 KB block, the slabs of a head ttot * 64 bytes apart)
     const uint32_t slab_bytes = (uint32_t)ttot * 64u;
@@ -454,7 +498,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       o_a[i] = (uint32_t)row * a_row + 16 * ((lane % 8) ^ a_swz(row));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o_v[i] = (uint32_t)(16 * i + lane / 4) * v_row + 16 * (lane % 4);
+    for (int i = 0; i < NVL; ++i)
+      o_v[i] = (uint32_t)((64 / (BVW / 8)) * i + lane / (BVW / 8)) * v_row + 16 * (lane % (BVW / 8));
 
     // loads of the chunk at token c0 into the given stage
     auto dma_chunk = [&](int c0, lchar* dK, lchar* dQ, lchar* dT, lchar* dAi, lchar* dAq, lchar* dV,
@@ -483,6 +528,17 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
           dma_a_tile(ac0, o_a, nr, a_row, dAi, lane);
           dma_a_tile(ac1, o_a, nr, a_row, dAq, lane);
         }
+      } else if constexpr (NB == 4) {
+        if (mr == 2) {
+          dma_qk_tile<DK>(ksrc + xo, o_qk, nr, qk_row, dK, lane);
+          dma_a_tile(ac0, o_a, nr, a_row, dAi, lane);
+          dma_v_tile<BVW>(vc, o_v, nr, v_row, dV, lane);
+        } else {
+          dma_qk_tile<DK>(qsrc + xo, o_qk, nr, qk_row, dQ, lane);
+          dma_a_tile(ac1, o_a, nr, a_row, dAq, lane);
+#pragma unroll
+          for (int pl = 0; pl < 4; ++pl) dma4(gp + pl * gs, dG + 256 * pl);
+        }
       } else {
         if (mr < 2) {
           dma_qk_tile<DK>(pick(mr == 0, ksrc, qsrc) + xo, o_qk, nr, qk_row, mr == 0 ? dK : dQ, lane);
@@ -508,7 +564,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       lchar* sink = (lchar*)sSink;
       constexpr int QKP = DK / 64;               // 64-line pieces per q or k tile
       constexpr int NXT = KDA ? 3 : 2;           // q / k-like tiles of a chunk
-      const int piece = (NMV * vt + mv) % (NXT * QKP + 2);
+      // 64 columns: fewer work-groups per head, so every one of a unit's
+      // work-groups takes its own pieces
+      const int piece = (NMW * (NB == 2 ? vt : rem) + mv) % (NXT * QKP + 2);
       const char* p;
       if (piece < NXT * QKP) {
         const int t = piece / QKP;
@@ -535,14 +593,27 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       else touch4(GF + (size_t)j * 4 * gs + (lane >> 1 & 3) * gs + c0 + (nr > 32 ? 32 * (lane & 1) : 0), sink);
     };
 
-    // a quarter of the o rows of the chunk at token c0, from the LDS tile
-    auto store_o = [&](int c0) __attribute__((always_inline)) {
+    // the o rows of the chunk at token c0 from its LDS tile (oT): with 32
+    // columns a quarter per mover; with 64 columns all of them, by the mover
+    // that loads v (mr 2)
+    auto store_o = [&](int c0, const char* oT) __attribute__((always_inline)) {
       const int nr = eos - c0 < BT ? eos - c0 : BT;
-      const int qq = mv * 64 + lane;
-      const int row = qq / (BV / 8), u = qq % (BV / 8);
-      if (row < nr)
-        store_nt16(o + ((size_t)(c0 + row) * HV + j) * V + v0 + 8 * u,
-                   *reinterpret_cast<const uint4*>(sO + row * L::OROW + 16 * u));
+      if constexpr (NB == 2) {
+        const int qq = mv * 64 + lane;
+        const int row = qq / (BVW / 8), u = qq % (BVW / 8);
+        if (row < nr)
+          store_nt16(o + ((size_t)(c0 + row) * HV + j) * V + v0 + 8 * u,
+                     *reinterpret_cast<const uint4*>(oT + row * OROW + 16 * u));
+      } else {
+        if (mr != 2) return;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int row = 8 * p + (lane >> 3), u = lane & 7;
+          if (row < nr)
+            store_nt16(o + ((size_t)(c0 + row) * HV + j) * V + v0 + 8 * u,
+                       *reinterpret_cast<const uint4*>(oT + row * (2 * BVW) + ((u ^ ((row >> 3) & 7)) << 4)));
+        }
+      }
     };
 
     if (NC > 0) {
@@ -555,7 +626,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       constexpr bool S1 = decltype(stg)::value;
       const int c0 = bos + c * BT;
       if constexpr (DK == 128) __builtin_amdgcn_s_sleep(4);   // see the helper waves
-      if (c > 0) store_o(c0 - BT);
+      if (c > 0) store_o(c0 - BT, NB == 2 ? sO : (S1 ? sV0 : sV1));   // the previous chunk's tile
       if (c + 1 < NC) {
         if constexpr (S1)
           dma_chunk(c0 + BT, (lchar*)sK0, (lchar*)sQ0, (lchar*)sT0, (lchar*)sAi0, (lchar*)sAq0, (lchar*)sV0,
@@ -581,18 +652,18 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       chunk(Stage0{}, c);
       if (c + 1 < NC) chunk(Stage1{}, c + 1);
     }
-    if (NC > 0) store_o(bos + (NC - 1) * BT);
+    if (NC > 0) store_o(bos + (NC - 1) * BT, NB == 2 ? sO : (((NC - 1) & 1) ? sV1 : sV0));
   }
 }
 
-template <int DK, bool KDA>
+template <int DK, bool KDA, int NB>
 hipError_t launch_dk(const ChunkArgs& a, const void* qop, const void* kop, const void* ktop,
                      const float* dg, hipStream_t s) {
-  const int nvt = a.V / BV;
+  const int nvt = a.V / (16 * NB);
   const int G = KDA ? 1 : a.HV / a.Hk;        // v-heads per (sequence, q / k head) unit
   const int units = a.N * (a.HV / G);
   const int nblk = ((units + 7) / 8) * 8 * G * nvt;
-  hipLaunchKernelGGL((gdn_scan_bf16_kernel<DK, KDA>), dim3((unsigned)nblk), dim3(NTHR), 0, s, qop, kop,
+  hipLaunchKernelGGL((gdn_scan_bf16_kernel<DK, KDA, NB>), dim3((unsigned)nblk), dim3(NTHR), 0, s, qop, kop,
                      (const f16_t*)ktop, (const bf16_t*)a.v, (const float*)a.GF, dg,
                      (const f16_t*)a.Ainv, (const f16_t*)a.Aqk, a.scale, a.h0, a.ht, a.hs, a.split_chunks,
                      a.hs_bf16 ? 1 : 0, a.hs_cap, (bf16_t*)a.o,
@@ -601,17 +672,38 @@ hipError_t launch_dk(const ChunkArgs& a, const void* qop, const void* kop, const
   return hipGetLastError();
 }
 
+// compute units of the current device (queried once per device)
+int cu_count() {
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
 }  // namespace
 
 hipError_t launch_scan_gdn_bf16(const ChunkArgs& a, hipStream_t s) {
-  if (a.K == 128) return launch_dk<128, false>(a, a.q, a.k, nullptr, nullptr, s);
-  return launch_dk<64, false>(a, a.q, a.k, nullptr, nullptr, s);
+  if (a.K == 128) {
+    // One work-group per CU runs at a time.  When the 32-column work-groups
+    // would not all fit at once, 64-column ones (four state waves) carry
+    // twice the columns per CU through each chunk.
+    const int G = a.HV / a.Hk;
+    const long long wg32 = (long long)((a.N * (a.HV / G) + 7) / 8) * 8 * G * (a.V / 32);
+    if (wg32 > cu_count()) return launch_dk<128, false, 4>(a, a.q, a.k, nullptr, nullptr, s);
+    return launch_dk<128, false, 2>(a, a.q, a.k, nullptr, nullptr, s);
+  }
+  return launch_dk<64, false, 2>(a, a.q, a.k, nullptr, nullptr, s);
 }
 
 hipError_t launch_scan_kda_bf16(const ChunkArgs& a, const void* qg, const void* kg, const void* kt,
                                 const float* dg, hipStream_t s) {
-  if (a.K == 128) return launch_dk<128, true>(a, qg, kg, kt, dg, s);
-  return launch_dk<64, true>(a, qg, kg, kt, dg, s);
+  if (a.K == 128) return launch_dk<128, true, 2>(a, qg, kg, kt, dg, s);
+  return launch_dk<64, true, 2>(a, qg, kg, kt, dg, s);
 }
 
 }  // namespace gdn

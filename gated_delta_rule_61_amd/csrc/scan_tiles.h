@@ -17,10 +17,8 @@ namespace gdn {
 namespace tiles {
 
 constexpr int BT = 64;     // chunk length
-constexpr int BV = 32;     // V columns per work-group
-constexpr int NSW = 2;     // state waves (= helper waves)
-constexpr int NMV = 4;     // mover waves
-constexpr int NTHR = 64 * (2 * NSW + NMV);
+constexpr int BV = 32;     // V columns per work-group (the 64-column form doubles it)
+constexpr int NTHR = 512;  // eight waves per work-group
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lchar;  // LDS byte pointer
@@ -227,17 +225,20 @@ __device__ __forceinline__ void dma_a_tile(const char* ac, const uint32_t* o_a, 
     }
   }
 }
+// v tile of BVC columns: rows of 2 BVC bytes, BVC / 8 lanes per row
+template <int BVC = BV>
 __device__ __forceinline__ void dma_v_tile(const char* vc, const uint32_t* o_v, int nr, uint32_t v_row,
                                            lchar* dV, int lane) {
+  constexpr int LPR = BVC / 8, RPL = 64 / LPR, NVL = BT / RPL;
   if (nr == BT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(vc + o_v[i], dV + 1024 * i);
+    for (int i = 0; i < NVL; ++i) dma16(vc + o_v[i], dV + 1024 * i);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * i + lane / 4;
+    for (int i = 0; i < NVL; ++i) {
+      const int row = RPL * i + lane / LPR;
       const int rr = row < nr ? row : nr - 1;
-      dma16(vc + (uint32_t)rr * v_row + 16 * (lane % 4), dV + 1024 * i);
+      dma16(vc + (uint32_t)rr * v_row + 16 * (lane % LPR), dV + 1024 * i);
     }
   }
 }

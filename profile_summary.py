@@ -41,11 +41,11 @@ NUM_XCD, NUM_SIMD = 8, 1024
 # workload -> (summary file, bench.py arguments, {kernel: per-launch key})
 SPECS = [
     ("prefill", "gdn_chunk_fwd_B4_T4096_H16_K128_bf16", "--only prefill",
-     {"gdn_scan_bf16_kernel<128,false>": "prefill:scan", "gdn_intra_kernel<ushort,128,half>": "prefill:intra"}),
+     {"gdn_scan_bf16_kernel<128,false,2>": "prefill:scan", "gdn_intra_kernel<ushort,128,half>": "prefill:intra"}),
     ("varlen", "gdn_chunk_fwd_varlen8_gqa16x32_K128_bf16", "--only varlen",
-     {"gdn_scan_bf16_kernel<128,false>": "varlen:scan", "gdn_intra_kernel<ushort,128,half>": "varlen:intra"}),
+     {"gdn_scan_bf16_kernel<128,false,4>": "varlen:scan", "gdn_intra_kernel<ushort,128,half>": "varlen:intra"}),
     ("kda", "kda_chunk_fwd_B2_T8192_H32_K128_bf16", "--only kda",
-     {"kda_intra_kernel<ushort,128,half>": "kda:intra", "gdn_scan_bf16_kernel<128,true>": "kda:scan"}),
+     {"kda_intra_kernel<ushort,128,half>": "kda:intra", "gdn_scan_bf16_kernel<128,true,2>": "kda:scan"}),
     ("decode", "gdn_decode_B256_HV32_K128_T1_T4", "--only decode",
      {"gdn_decode_kernel<1,256>": "decode:T1", "gdn_decode_mfma_kernel<4,4>": "decode:T4"}),
     ("decode_b1", "gdn_decode_B1_HV32_K128_T1_T4", "--only decode --decode-batch 1",
@@ -83,7 +83,9 @@ def kernel_name(raw: str):
             return None
         ln = int(m.group(1))
         base, rest = n[m.end():m.end() + ln], n[m.end() + ln:]
-        targs = {"ILi128ELb0E": "<128,false>", "ILi128ELb1E": "<128,true>", "ItLi128E": "<ushort,128,half>"}
+        targs = {"ILi128ELb0ELi2E": "<128,false,2>", "ILi128ELb0ELi4E": "<128,false,4>",
+                 "ILi128ELb1ELi2E": "<128,true,2>", "ILi128ELb0E": "<128,false>", "ILi128ELb1E": "<128,true>",
+                 "ItLi128E": "<ushort,128,half>"}
         return base + next((v for k, v in targs.items() if rest.startswith(k)), "")
     m = re.search(r"gdn::\(anonymous namespace\)::(\w+)(<[^>]*>)?", n)
     if not m:

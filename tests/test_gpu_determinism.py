@@ -39,7 +39,8 @@ def _workspaces(nbytes):
             torch.zeros((nbytes,), dtype=torch.uint8, device=DEV))
 
 
-@pytest.mark.parametrize("case", ["gdn_dense", "gdn_varlen_gqa_snapshots", "gdn_gamma_fp32", "kda_varlen"])
+@pytest.mark.parametrize("case", ["gdn_dense", "gdn_varlen_gqa_snapshots", "gdn_gamma_fp32", "kda_varlen",
+                                  "gdn_64_column"])
 def test_prefill_bitwise_repeatable_and_workspace_independent(case):
     print(f"determinism {case}", flush=True)
     kda = case.startswith("kda")
@@ -48,6 +49,8 @@ def test_prefill_bitwise_repeatable_and_workspace_independent(case):
     elif case == "gdn_varlen_gqa_snapshots":
         inp = workloads.make_prefill(1, 900, 2, 8, 128, 128, dtype=torch.bfloat16, seed=402, h0=True,
                                      seqlens=[300, 0, 1, 535, 64])
+    elif case == "gdn_64_column":   # more 32-column work-groups than CUs
+        inp = workloads.make_prefill(3, 300, 16, 32, 128, 128, dtype=torch.bfloat16, seed=405, h0=True)
     elif case == "gdn_gamma_fp32":
         inp = workloads.make_prefill(2, 300, 1, 2, 64, 64, dtype=torch.float32, seed=403, gate="none", h0=True)
     else:

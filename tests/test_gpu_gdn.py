@@ -98,6 +98,17 @@ def test_gdn_bf16_wide_gqa_groups(Hk, HV, lens):
     _compare(inp)
 
 
+@pytest.mark.parametrize("B,T,Hk,HV,lens", [(3, 300, 16, 32, None), (1, 448, 24, 24, [257, 0, 1, 190]),
+                                              (3, 200, 8, 32, None)],
+                         ids=["gqa2_dense", "gqa1_varlen", "gqa4_dense"])
+def test_gdn_bf16_64_column_work_groups(B, T, Hk, HV, lens):
+    # more 32-column work-groups than CUs: the scan runs 64-column ones (four
+    # state waves; the o tile in the chunk's v buffer); every head checked
+    inp = workloads.make_prefill(B, T, Hk, HV, 128, 128, dtype=torch.bfloat16, seed=500 + HV + T, h0=True,
+                                 seqlens=lens, name=f"bf16_64col_{Hk}x{HV}")
+    _compare(inp)
+
+
 def test_gdn_no_final_state_and_empty():
     inp = workloads.make_prefill(1, 70, 1, 1, 64, 64, dtype=torch.float32, seed=9)
     o, ht = _gpu(inp, output_final_state=False)

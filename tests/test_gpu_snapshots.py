@@ -54,6 +54,15 @@ def test_gdn_bf16_varlen_snapshots(S, fp32_states):
     _gdn(inp, S, fp32_states)
 
 
+@pytest.mark.parametrize("fp32_states", [False, True])
+@pytest.mark.parametrize("S", [64, 128])
+def test_gdn_bf16_snapshots_64_column_work_groups(S, fp32_states):
+    # 3 x 16 (q / k head) units x 2 v-heads: the 64-column scan
+    inp = workloads.make_prefill(3, 260, 16, 32, 128, 128, dtype=torch.bfloat16, seed=510 + S, h0=True,
+                                 name="bf16_64col_snap")
+    _gdn(inp, S, fp32_states)
+
+
 def test_gdn_bf16_fixed_snapshots_every_chunk():
     inp = workloads.make_prefill(2, 200, 1, 2, 64, 64, dtype=torch.bfloat16, seed=5, h0=True,
                                  name="bf16_K64")
