@@ -50,20 +50,29 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 // Chunk tables for packed variable-length batches: chunk offsets (exclusive
 // prefix of ceil(len / 64)) and the sequence order by decreasing length.
 // One work-group; N up to any size for the offsets, the order is sorted for
-// N <= 1024 and left as the identity beyond.
+// N <= 1024 and left as the identity beyond.  For N <= 1024 the (clamped)
+// lengths are read from global memory once, one per thread, and kept in LDS,
+// so the ranking loop does not wait out a memory round trip per sequence.
 __global__ __launch_bounds__(1024) void varlen_tables_kernel(const int64_t* __restrict__ cu, int N,
                                                               int T, int32_t* __restrict__ coff,
                                                               int32_t* __restrict__ order) {
   __shared__ int32_t part[1024];
+  __shared__ int32_t slen[1024];
   const int t = threadIdx.x;
   const int per = (N + 1023) / 1024;
   const int lo = t * per, hi = lo + per < N ? lo + per : N;
-  auto len = [&](int i) {
+  auto len_g = [&](int i) {
     long long b0 = cu[i], b1 = cu[i + 1];
     b0 = b0 < 0 ? 0 : (b0 > T ? T : b0);
     b1 = b1 < b0 ? b0 : (b1 > T ? T : b1);
     return (int)(b1 - b0);
   };
+  const bool staged = N <= 1024;   // uniform
+  if (staged) {
+    if (t < N) slen[t] = len_g(t);
+    __syncthreads();
+  }
+  auto len = [&](int i) { return staged ? slen[i] : len_g(i); };
   int s = 0;
   for (int i = lo; i < hi; ++i) s += (len(i) + 63) / 64;
   part[t] = s;

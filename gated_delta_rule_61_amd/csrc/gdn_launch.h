@@ -81,16 +81,21 @@ __host__ __device__ inline long long gf_stride(long long tokens) { return tokens
 
 // First state snapshot of sequence n: a sequence of L tokens has
 // ceil(L / S) snapshots (S = split tokens), stored back to back in sequence
-// order.  Varlen boundaries are clamped as the scans clamp them.
+// order.  Varlen boundaries are clamped as the scans clamp them.  Called by
+// all 64 lanes of a wave with the same arguments: lane l sums sequences
+// l, l + 64, ..., so the loads of 64 sequences are in flight together, and
+// the partial sums are combined across the wave.
 __device__ inline long long snapshot_offset(const int64_t* cu, int n, int Tlen, int S) {
   if (!cu) return (long long)n * ((Tlen + S - 1) / S);
   long long acc = 0;
-  for (int m = 0; m < n; ++m) {
+  for (int m = (int)(threadIdx.x & 63); m < n; m += 64) {
     long long b0 = cu[m], b1 = cu[m + 1];
     b0 = b0 < 0 ? 0 : (b0 > Tlen ? Tlen : b0);
     b1 = b1 < b0 ? b0 : (b1 > Tlen ? Tlen : b1);
     acc += (b1 - b0 + S - 1) / S;
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   return acc;
 }
 // bf16 GDN and KDA scans (direct-to-LDS staging, state / helper / mover waves);

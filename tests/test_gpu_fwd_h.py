@@ -76,6 +76,16 @@ def test_fwd_h_key_first_layout(gate, fp32_states):
 
 
 @pytest.mark.parametrize("gate", ["gdn", "gv", "kda"])
+def test_fwd_h_many_sequences(gate):
+    """150 packed sequences of 0..100 tokens: stored-state offsets summed over
+    many earlier sequences, in each of the three kernels."""
+    lens = workloads.draw_seqlens(150, 0, 100, seed=540)
+    inp = workloads.make_prefill(1, sum(lens), 1, 2, 128, 128, dtype=torch.bfloat16, seed=541, h0=True,
+                                 gate="kda" if gate == "kda" else "gdn", seqlens=lens, name="fwd_h_many150")
+    _case(inp, gate, 64, seed=542, fp32_states=True)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "gv", "kda"])
 def test_fwd_h_key_first_k64(gate):
     inp = workloads.make_prefill(2, 150, 1, 2, 64, 64, dtype=torch.bfloat16, seed=85, h0=True,
                                  gate="kda" if gate == "kda" else "gdn", name="fwd_h_kfirst_K64")

@@ -63,6 +63,25 @@ def test_gdn_bf16_snapshots_64_column_work_groups(S, fp32_states):
     _gdn(inp, S, fp32_states)
 
 
+@pytest.mark.parametrize("N,K,hi", [(150, 128, 100), (150, 64, 100), (1100, 64, 3)],
+                         ids=["150seqs_K128", "150seqs_K64", "1100seqs_tiny"])
+def test_gdn_many_sequences_with_snapshots(N, K, hi):
+    # snapshot offsets summed over many earlier sequences (more than one
+    # 64-lane stride), chunk tables and the longest-first order for N <= 1024
+    # and beyond it; lengths 0 .. hi, empty sequences included
+    lens = workloads.draw_seqlens(N, 0, hi, seed=520 + N + K)
+    inp = workloads.make_prefill(1, sum(lens), 1, 2, K, K, dtype=torch.bfloat16, seed=521 + N, h0=True,
+                                 seqlens=lens, name=f"many{N}_K{K}")
+    _gdn(inp, 64)
+
+
+def test_kda_many_sequences_with_snapshots():
+    lens = workloads.draw_seqlens(150, 0, 100, seed=530)
+    inp = workloads.make_prefill(1, sum(lens), 1, 1, 128, 128, dtype=torch.bfloat16, seed=531, gate="kda",
+                                 h0=True, seqlens=lens, name="kda_many150")
+    _kda(inp, 64)
+
+
 def test_gdn_bf16_fixed_snapshots_every_chunk():
     inp = workloads.make_prefill(2, 200, 1, 2, 64, 64, dtype=torch.bfloat16, seed=5, h0=True,
                                  name="bf16_K64")
