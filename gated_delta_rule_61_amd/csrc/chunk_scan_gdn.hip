@@ -60,6 +60,8 @@
 // read before the mid-chunk barrier and the movers refill only after the
 // mover that loads v has stored o from it.
 
+#include <atomic>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 #include "scan_tiles.h"
@@ -672,17 +674,18 @@ hipError_t launch_dk(const ChunkArgs& a, const void* qop, const void* kop, const
   return hipGetLastError();
 }
 
-// compute units of the current device (queried once per device)
+// compute units of the current device (queried once per device; calls from
+// several host threads may race to fill the cache with the same value)
 int cu_count() {
-  static int counts[64] = {0};
+  static std::atomic<int> counts[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (counts[dev] == 0) {
-    int n = 0;
+  int n = counts[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    counts[dev] = n;
+    counts[dev].store(n, std::memory_order_relaxed);
   }
-  return counts[dev];
+  return n;
 }
 
 }  // namespace
