@@ -597,7 +597,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the method shards over "
-              "(sequence, head) with no communication, see DESIGN.md", file=sys.stderr)
+              "(sequence, head) with no communication between GPUs", file=sys.stderr)
         sys.exit(2)
     from gated_delta_rule_61_amd import workloads
     cpu = None
