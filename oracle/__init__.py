@@ -30,7 +30,7 @@ cases, library routines, hand-computed fixtures).  No function is
 """
 
 from .recurrence import delta_rule_recurrent, gdn_recurrent, kda_recurrent
-from .intra import chunk_intra_matrices
+from .intra import chunk_intra_matrices, chunk_intra_wu
 from .decode import decode_gate, decode_normalize, gdn_decode
 from .bf16 import round_to_bf16
 from .handoff import state_to_pool
@@ -39,7 +39,7 @@ from .state_scan import state_scan
 
 __all__ = [
     "delta_rule_recurrent", "gdn_recurrent", "kda_recurrent",
-    "chunk_intra_matrices",
+    "chunk_intra_matrices", "chunk_intra_wu",
     "decode_gate", "decode_normalize", "gdn_decode",
     "round_to_bf16", "state_to_pool", "state_grad_scan", "state_scan",
 ]

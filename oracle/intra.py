@@ -77,3 +77,53 @@ def chunk_intra_matrices(q, k, beta, scale: float, g=None, gk=None, cu_seqlens=N
                 A = beta[b, rows, j][:, None] * np.where(strict, kk, 0.0)
                 Ainv[b, rows, j, :n] = np.linalg.inv(np.eye(n) + A)
     return Aqk, Ainv
+
+
+def chunk_intra_wu(k, v, beta, g=None, cu_seqlens=None, chunk_size: int = 64, g_cumulative: bool = False,
+                   heads: Optional[list] = None):
+    """Return (A, w, u) of the scalar-gate intra-chunk step, float64:
+
+      A = (I + Akk)^-1                 [B, T, HV, BT] (rows per token, as above)
+      w = A diag(beta e^G) K           [B, T, HV, K]
+      u = A diag(beta) V               [B, T, HV, V]
+
+    per chunk and v-head ("sglang srt/layers/attention/fla/chunk_fwd.py",
+    chunk_gated_delta_rule_fwd_intra: the fused K K^T + solve, then
+    recompute_w_u, which scales the k rows by beta and exp(G) and the v rows
+    by beta before the product with A).  ``g`` holds per-token log-gates
+    [B, T, HV] (their chunk-local cumulative sums G are taken here) or, with
+    ``g_cumulative``, the chunk-local cumulative sums themselves, as that
+    page's wrapper takes them; None means no gate.  With w and u, the state
+    after a chunk is h_end = e^{G_last} h + (K o e^{G_last - G})^T (u - w h)
+    (h = S^T, K x V).
+    """
+    k, v, beta, g = _f64(k), _f64(v), _f64(beta), _f64(g)
+    B, T, Hk, K = k.shape
+    HV, V = v.shape[2], v.shape[3]
+    BT = chunk_size
+    hs = range(HV) if heads is None else heads
+    A_out = np.zeros((B, T, HV, BT))
+    w_out = np.zeros((B, T, HV, K))
+    u_out = np.zeros((B, T, HV, V))
+    for (b, bos, eos) in sequences(B, T, cu_seqlens):
+        for c0 in range(bos, eos, BT):
+            n = min(BT, eos - c0)
+            rows = slice(c0, c0 + n)
+            strict = np.tril(np.ones((n, n), dtype=bool), -1)
+            for j in hs:
+                kc = k[b, rows, j // (HV // Hk)]               # [n, K]
+                vc = v[b, rows, j]                               # [n, V]
+                bc = beta[b, rows, j]                            # [n]
+                if g is None:
+                    G = np.zeros(n)
+                elif g_cumulative:
+                    G = g[b, rows, j]
+                else:
+                    G = np.cumsum(g[b, rows, j])
+                E = np.exp(np.where(strict, G[:, None] - G[None, :], 0.0))
+                A = bc[:, None] * np.where(strict, (kc @ kc.T) * E, 0.0)
+                Ainv = np.linalg.inv(np.eye(n) + A)
+                A_out[b, rows, j, :n] = Ainv
+                w_out[b, rows, j] = Ainv @ ((bc * np.exp(G))[:, None] * kc)
+                u_out[b, rows, j] = Ainv @ (bc[:, None] * vc)
+    return A_out, w_out, u_out
