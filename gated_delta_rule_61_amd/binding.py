@@ -62,6 +62,10 @@ _SIGNATURES = {
                                  _c_void_p, _c_void_p, _c_int, _c_ll, _c_int, _c_int, _c_void_p, _c_void_p, _c_int,
                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_void_p]),
+    "gdn_chunk_intra_workspace_bytes": (_c_size_t, [_c_int]),
+    "gdn_chunk_intra": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_int,
+                                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "gdn_state_to_pool": (_c_int, [_c_void_p, _c_void_p, _c_void_p,
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
 }
@@ -367,6 +371,41 @@ def gdn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tenso
                             float(scale), float(softplus_beta), float(softplus_threshold),
                             1 if use_qk_l2norm else 0, float(eps), _stream(dev)))
     return o
+
+
+def gdn_chunk_intra(k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor], beta: torch.Tensor,
+                    cu_seqlens: Optional[torch.Tensor] = None, g_cumulative: bool = False,
+                    output_wu: bool = True, chunk_size: int = 64,
+                    workspace: Optional[torch.Tensor] = None):
+    """The scalar-gate intra-chunk step: returns (w [B,T,HV,K], u [B,T,HV,V],
+    A [B,T,HV,64]) in the io dtype, w and u None without ``output_wu``.  ``g``
+    holds per-token log-gates, or with ``g_cumulative`` their chunk-local
+    cumulative sums."""
+    if k.dim() != 4 or v.dim() != 4:
+        raise ValueError("k must be [B, T, Hk, K] and v [B, T, HV, V]")
+    B, T, Hk, K = k.shape
+    HV, V = v.shape[2], v.shape[3]
+    dev, io = k.device, k.dtype
+    _io_code(io)
+    _need(k, "k", io, None, dev)
+    _need(v, "v", io, (B, T, HV, V), dev)
+    _need(g, "g", torch.float32, (B, T, HV), dev)
+    _need(beta, "beta", torch.float32, (B, T, HV), dev)
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int64, None, dev)
+        N = cu_seqlens.numel() - 1
+    A = torch.empty((B, T, HV, chunk_size), dtype=io, device=dev)
+    w = torch.empty((B, T, HV, K), dtype=io, device=dev) if output_wu else None
+    u = torch.empty((B, T, HV, V), dtype=io, device=dev) if output_wu else None
+    nbytes = int(lib().gdn_chunk_intra_workspace_bytes(N)) if cu_seqlens is not None else 0
+    if nbytes and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(lib().gdn_chunk_intra(_ptr(k), _ptr(v), _ptr(g), 1 if g_cumulative else 0, _ptr(beta),
+                                 _ptr(cu_seqlens), N, B, T, Hk, HV, K, V, chunk_size, _io_code(io),
+                                 _ptr(A), _ptr(w), _ptr(u), _ptr(workspace) if nbytes else None,
+                                 workspace.numel() if nbytes else 0, _stream(dev)))
+    return w, u, A
 
 
 def state_to_pool(ht: torch.Tensor, pool_state: torch.Tensor,

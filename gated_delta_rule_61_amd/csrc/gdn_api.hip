@@ -363,6 +363,74 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   return ok();
 }
 
+size_t gdn_chunk_intra_workspace_bytes(int num_seqs) {
+  if (num_seqs < 0) return 0;
+  return ((2 * (size_t)num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;   // chunk offsets, order
+}
+
+int gdn_chunk_intra(const void* k, const void* v, const float* g, int g_cumulative, const float* beta,
+                    const int64_t* cu_seqlens, int num_seqs, int B, int T, int Hk, int HV, int K, int V,
+                    int chunk_size, int dtype, void* A, void* w, void* u, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0 || Hk <= 0 || HV <= 0 || K <= 0 || V <= 0)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "sizes must be positive (B, T >= 0): B=%d T=%d Hk=%d HV=%d K=%d V=%d",
+                B, T, Hk, HV, K, V);
+  if (HV % Hk != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "HV (%d) must be a multiple of Hk (%d)", HV, Hk);
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "unknown dtype code %d", dtype);
+  if (g_cumulative != 0 && g_cumulative != 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "g_cumulative must be 0 or 1 (got %d)", g_cumulative);
+  if (chunk_size != 64) return fail(GDN_ERR_UNSUPPORTED, "chunk_size must be 64 (got %d)", chunk_size);
+  if ((K != 64 && K != 128) || (V != 64 && V != 128))
+    return fail(GDN_ERR_UNSUPPORTED, "supported head dims are K, V in {64, 128} (got K=%d V=%d)", K, V);
+  if ((long long)B * T >= (1LL << 31) / 64)
+    return fail(GDN_ERR_UNSUPPORTED, "B*T too large (got %lld tokens)", (long long)B * T);
+  int N = B;
+  if (cu_seqlens) {
+    if (B != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens requires B == 1 (got B=%d)", B);
+    if (num_seqs < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0 (got %d)", num_seqs);
+    N = num_seqs;
+  }
+  {
+    const long long slots = cu_seqlens ? (long long)(T + 63) / 64 + N : (long long)B * ((T + 63) / 64);
+    if ((slots + 8) * HV * 8 >= (1LL << 31))
+      return fail(GDN_ERR_UNSUPPORTED, "too many chunks x heads for one launch (HV=%d)", HV);
+  }
+  const bool work = (long long)B * T > 0 && N > 0;
+  if (work && (!k || !beta || !A)) return fail(GDN_ERR_INVALID_ARGUMENT, "k, beta and A are required");
+  if (work && u && !v) return fail(GDN_ERR_INVALID_ARGUMENT, "v is required for u");
+  const void* ptrs[] = {k, v, A, w, u};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(GDN_ERR_INVALID_ARGUMENT, "k, v, A, w and u must be 16-byte aligned");
+  if (cu_seqlens) {
+    const size_t need = gdn_chunk_intra_workspace_bytes(N);
+    if (!workspace || workspace_bytes < need)
+      return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace & 255u) != 0)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  }
+  if (!work) return ok();
+  IntraArgs a;
+  a.k = k; a.v = v; a.g = g; a.g_cumulative = g_cumulative != 0; a.beta = beta;
+  a.A = A; a.w = w; a.u = u; a.cu_seqlens = cu_seqlens;
+  a.chunk_off = cu_seqlens ? (int32_t*)workspace : nullptr;
+  a.N = N; a.B = B; a.T = T; a.Hk = Hk; a.HV = HV; a.K = K; a.V = V;
+  a.bf16 = dtype == GDN_DTYPE_BF16;
+  const hipStream_t s = (hipStream_t)stream;
+  prof_begin(GDN_STAGE_INTRA, s);
+  hipError_t e = hipSuccess;
+  if (cu_seqlens) {
+    hipLaunchKernelGGL(varlen_tables_kernel, dim3(1), dim3(1024), 0, s, cu_seqlens, N, T, a.chunk_off,
+                       a.chunk_off + N + 1);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = launch_intra_wu(a, s);
+  prof_end(GDN_STAGE_INTRA, s);
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"
 
 // ------------------------------------------------ no-allocation prefill entry

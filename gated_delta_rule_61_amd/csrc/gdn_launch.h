@@ -113,6 +113,20 @@ struct KdaBuffers {
 };
 hipError_t launch_kda_fwd(const ChunkArgs& a, const KdaBuffers& kb, hipStream_t s);
 
+// The scalar-gate intra-chunk step on its own: A = (I + L)^-1, w, u.
+struct IntraArgs {
+  const void *k, *v;               // [B*T, Hk, K], [B*T, HV, V] io dtype
+  const float* g;                  // [B*T, HV] log-gates or their chunk-local sums, or nullptr
+  bool g_cumulative;               // g holds chunk-local cumulative sums
+  const float* beta;               // [B*T, HV]
+  void *A, *w, *u;                 // [B*T, HV, 64], [B*T, HV, K], [B*T, HV, V] io dtype; w, u optional
+  const int64_t* cu_seqlens;
+  int32_t* chunk_off;              // [N + 1] varlen chunk offsets (workspace) or nullptr
+  int N, B, T, Hk, HV, K, V;
+  int bf16;
+};
+hipError_t launch_intra_wu(const IntraArgs& a, hipStream_t s);
+
 // Workspace layout shared by the size query and the launcher.
 struct ChunkWorkspace {
   size_t ainv_off, aqk_off, gf_off, coff_off, order_off;

@@ -91,8 +91,9 @@ const char* gdn_version(void);
  * Workspace needed by gdn_chunk_fwd / kda_chunk_fwd, in bytes, for the
  * given problem (num_seqs = N of cu_seqlens, or B without it).  Returns 0
  * when the arguments are invalid.  The workspace holds the per-chunk
- * (I + A)^-1 and masked, gated Q K^T blocks ([B*T, HV, 64] each, io dtype)
- * and the varlen chunk tables.
+ * (I + A)^-1 and masked, gated Q K^T blocks ([B*T, HV, 64] each; fp16 for
+ * bf16 io, fp32 for fp32 io), the per-token gate factors and the varlen
+ * chunk tables (KDA: also its gated operands and decay rows).
  */
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hk, int HV, int K, int V,
                                      int num_seqs, int dtype);
@@ -215,6 +216,44 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
                   void* o, void* Aqk, void* Akk_inv,
                   void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * The scalar-gate intra-chunk step on its own ("sglang srt/layers/attention/
+ * fla/chunk_fwd.py", chunk_gated_delta_rule_fwd_intra: the fused beta K K^T
+ * + solve, then recompute_w_u).  Per chunk of 64 tokens (restarting at every
+ * sequence start) and v-head, with G the chunk-local cumulative log-gate:
+ *   A = (I + L)^-1,  L_ts = beta_t (k_t . k_s) e^{G_t - G_s} for s < t
+ *   w = A diag(beta e^G) K,   u = A diag(beta) V
+ * (gdn_chunk_fwd never forms w and u: its scan computes u - w S^T in one
+ * step.)  With h = S^T the state after a chunk is
+ * e^{G_last} h + (K o e^{G_last - G})^T (u - w h).
+ *
+ *   k            [B, T, Hk, K]  io dtype (key head of v-head j: j / (HV / Hk))
+ *   v            [B, T, HV, V]  io dtype, read when u is requested
+ *   g            [B, T, HV]     fp32: per-token log-gates (g_cumulative = 0)
+ *                or their chunk-local cumulative sums, as the page's
+ *                wrapper takes them (g_cumulative = 1); NULL = no gate
+ *   beta         [B, T, HV]     fp32
+ *   A            [B, T, HV, 64] io dtype out: row t holds row (t - chunk
+ *                start) of the chunk's A (entries past the chunk end 0)
+ *   w            [B, T, HV, K]  io dtype out, or NULL (not formed)
+ *   u            [B, T, HV, V]  io dtype out, or NULL (not formed)
+ *   cu_seqlens, num_seqs, B, T, Hk, HV, chunk_size, dtype  as in gdn_chunk_fwd
+ *   workspace    device buffer of at least gdn_chunk_intra_workspace_bytes(N)
+ *                bytes, 256-byte aligned, with cu_seqlens (the chunk
+ *                tables); unused (NULL allowed) without
+ * Supported: K, V in {64, 128}, chunk_size = 64, bf16 or fp32 io.  A is
+ * formed in fp32 (forward substitution and block merge) and stored once in
+ * the io dtype; w and u are fp32 products of that inverse with the scaled
+ * rows.  Errors and pointer rules as in gdn_chunk_fwd.  Asynchronous on
+ * `stream`.
+ */
+size_t gdn_chunk_intra_workspace_bytes(int num_seqs);
+int gdn_chunk_intra(const void* k, const void* v, const float* g, int g_cumulative,
+                    const float* beta, const int64_t* cu_seqlens, int num_seqs,
+                    int B, int T, int Hk, int HV, int K, int V,
+                    int chunk_size, int dtype, void* A, void* w, void* u,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * GDN decode step over a bf16 state pool, T = 1..4 tokens per call.

@@ -125,6 +125,39 @@ def test_launch_index_range_is_checked(L):
     assert b"for one launch" in L.gdn_last_error()
 
 
+def _intra(L, **kw):
+    a = dict(k=FAKE, v=FAKE, g=None, gc=0, beta=FAKE, cu=None, ns=0, B=1, T=64, Hk=1, HV=2, K=64, V=64, cs=64,
+             dt=1, A=FAKE, w=None, u=None, ws=None, wsb=0)
+    a.update(kw)
+    return L.gdn_chunk_intra(a["k"], a["v"], a["g"], a["gc"], a["beta"], a["cu"], a["ns"], a["B"], a["T"], a["Hk"],
+                             a["HV"], a["K"], a["V"], a["cs"], a["dt"], a["A"], a["w"], a["u"], a["ws"], a["wsb"],
+                             None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(cs=32), 2, b"chunk_size"),
+    (dict(K=96), 2, b"head dims"),
+    (dict(Hk=3, HV=4), 1, b"multiple"),
+    (dict(dt=5), 1, b"dtype"),
+    (dict(gc=2), 1, b"g_cumulative"),
+    (dict(A=None), 1, b"required"),
+    (dict(u=FAKE, v=None), 1, b"v is required"),
+    (dict(w=FAKE + 8), 1, b"aligned"),
+    (dict(cu=FAKE, ns=3), 4, b"workspace"),
+    (dict(cu=FAKE, ns=3, ws=FAKE + 16, wsb=1 << 20), 1, b"256-byte"),
+    (dict(B=2, cu=FAKE, ns=3), 1, b"B == 1"),
+])
+def test_chunk_intra_rejects(L, kw, status, msg):
+    assert _intra(L, **kw) == status
+    assert msg in L.gdn_last_error()
+
+
+def test_chunk_intra_workspace_query(L):
+    assert L.gdn_chunk_intra_workspace_bytes(0) == 256
+    assert L.gdn_chunk_intra_workspace_bytes(100) == 1024
+    assert L.gdn_chunk_intra_workspace_bytes(-1) == 0
+
+
 def test_kda_rejects_undersized_snapshots(L):
     r = L.kda_chunk_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, None, None, FAKE, 128, 1, 0, None, 0, 2, 64, 1, 1, 64, 64,
                         64, 1, FAKE, None, None, FAKE, 1 << 40, None)
