@@ -77,7 +77,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-extra", action="store_true", help="prefill workload only")
-    p.add_argument("--only", choices=["prefill", "decode", "kda", "varlen", "handoff", "bwd_dh", "fwd_h", "copy",
+    p.add_argument("--only", choices=["prefill", "decode", "kda", "varlen", "handoff", "bwd_dh", "fwd_h", "intra_wu",
+                                      "copy",
                                       "cpu", "snapshots"],
                    default=None,
                    help="run one workload (for profiling) and print its figures")
@@ -484,6 +485,25 @@ def bench_handoff(args, binding, workloads, torch):
             "algorithmic_bytes": nbytes, "measured_bytes": measured_traffic("handoff")}
 
 
+def bench_intra_wu(args, binding, workloads, torch):
+    """The intra-chunk step on its own (gdn_chunk_intra: A, w and u) on the
+    headline shape.  Bytes per token and v-head: k (shared by the HV / Hk
+    v-heads of a q / k head), v, g and beta in; A, w and u out."""
+    inp = workloads.gdn_bf16_b4_t4096()
+    dev = "cuda:0"
+    k, v, g, beta = inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev)
+    B, T, Hk, HV, K, V = inp.dims
+
+    def step():
+        binding.gdn_chunk_intra(k, v, g, beta)
+
+    ms = timed(step, args.steps, args.warmup)
+    nbytes = B * T * (Hk * K * 2 + HV * (V * 2 + 4 + 4 + 64 * 2 + K * 2 + V * 2))
+    return {"workload": f"gdn_chunk_intra B={B} T={T} H={HV} K=V={K} bf16, A, w and u out",
+            "ms_per_call": round(ms, 5), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}
+
+
 # --------------------------------------------------------------- CPU oracle
 _CPU = {}   # workload inputs, set before the worker processes fork
 
@@ -626,7 +646,7 @@ def main():
         print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "calls": args.steps}), flush=True)
         return
     single = {"kda": bench_kda, "bwd_dh": bench_bwd_dh, "fwd_h": bench_fwd_h, "handoff": bench_handoff,
-              "varlen": bench_varlen}
+              "varlen": bench_varlen, "intra_wu": bench_intra_wu}
     if args.only in single:
         print(json.dumps({args.only: single[args.only](args, binding, workloads, torch)}), flush=True)
         return
@@ -678,6 +698,7 @@ def main():
         out["snapshots"] = bench_snapshots(args, binding, workloads, torch, ms)
         out["bwd_dh"] = bench_bwd_dh(args, binding, workloads, torch)
         out["fwd_h"] = bench_fwd_h(args, binding, workloads, torch)
+        out["intra_wu"] = bench_intra_wu(args, binding, workloads, torch)
     if cpu is not None:
         c = cpu["prefill"]
         out["cpu_baseline"] = {"value": c["tokens_per_s"], "unit": "tokens/s", "cores": cpu["cores"],
