@@ -60,6 +60,8 @@ SPECS = [
      {"state_scan_ring_kernel<128,true,true>": "fwd_h:fp32"}),
     ("handoff", "gdn_state_to_pool_N256_HV32_K128", "--only handoff",
      {"state_to_pool_kernel": "handoff"}),
+    ("intra_wu", "gdn_chunk_intra_B4_T4096_H16_K128_bf16", "--only intra_wu",
+     {"gdn_intra_wu_bf16_kernel<128,128>": "intra_wu"}),
 ]
 MFMA_WORKLOADS = ("prefill", "varlen", "kda")
 
@@ -85,7 +87,7 @@ def kernel_name(raw: str):
         base, rest = n[m.end():m.end() + ln], n[m.end() + ln:]
         targs = {"ILi128ELb0ELi2E": "<128,false,2>", "ILi128ELb0ELi4E": "<128,false,4>",
                  "ILi128ELb1ELi2E": "<128,true,2>", "ILi128ELb0E": "<128,false>", "ILi128ELb1E": "<128,true>",
-                 "ItLi128E": "<ushort,128,half>"}
+                 "ItLi128E": "<ushort,128,half>", "ILi128ELi128EE": "<128,128>"}
         return base + next((v for k, v in targs.items() if rest.startswith(k)), "")
     m = re.search(r"gdn::\(anonymous namespace\)::(\w+)(<[^>]*>)?", n)
     if not m:
