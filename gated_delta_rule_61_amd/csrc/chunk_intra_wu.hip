@@ -17,13 +17,14 @@
 //     memory (bf16 16x16x32, fp32 io 16x16x4), gate / beta / mask on the
 //     accumulators, forward substitution and block merge in LDS (fp32);
 //   * A leaves as 16-byte rows in the io dtype;
-//   * bf16 io: w and u as bf16 MFMA (16x16x32) of the bf16-rounded inverse
-//     and the bf16-rounded scaled rows, the page's own operand precision.
+//   * bf16 io: w and u as fp16 MFMA (16x16x32) of the fp16-rounded inverse
+//     and the fp16-rounded scaled rows (the page rounds both to bf16; fp16's
+//     2^-11 keeps the products within the bf16 storage error at any length).
 //     The k fragments of K K^T stay in registers and are reused; the v
-//     fragments are loaded at the start, so both streams are in flight
-//     during the solve.  The inverse's six nonzero 16 x 32 operand blocks
-//     sit in registers, which frees the fp32 tile: the transposed staging
-//     tile of 64 scaled columns ([column][token], bf16) takes its place in
+//     fragments are loaded after the solve and arrive while w is formed.
+//     The inverse's six nonzero 16 x 32 operand blocks sit in registers,
+//     which frees the fp32 tile: the transposed staging tile of 64 scaled
+//     columns ([column][token], fp16) takes its place in
 //     LDS, 17 KB per wave in all.  The products run transposed (X^T A^T),
 //     so each lane ends with four consecutive columns of one token row:
 //     8-byte stores, no staging of the result.
@@ -46,7 +47,7 @@ namespace {
 using namespace intra;
 
 constexpr int XT = 68;   // padded token column of the fp32 32 x 64 staging tile
-constexpr int XP = 72;   // padded token row of the bf16 64 x 64 staging tile (144 B)
+constexpr int XP = 72;   // padded token row of the fp16 64 x 64 staging tile (144 B)
 
 // Gate scan (G and beta, lane = token, zero past the chunk end), the ten
 // lower blocks of K K^T, L = beta_r (k_r . k_s) e^{G_r - G_s} (s < r), its
@@ -185,12 +186,12 @@ __host__ __device__ constexpr int apair(int rb, int kk) { return rb < 2 ? rb : 2
 
 // Columns 64 H .. 64 H + 63 of w or u for bf16 io: the wave's scaled
 // fragments (lane holds X[16 rb + row][32 s + 8 grp .. + 8] of slab s, scale
-// f[rb] for its token) go to the staging tile as bf16, column-major; then, per 16-column
-// block cb and token block rb, out^T = X^T A^T over the two 32-token halves
+// f[rb] for its token) go to the staging tile as fp16, column-major; then,
+// per 16-column block cb and token block rb, out^T = X^T A^T over the two 32-token halves
 // kk (only kk <= rb / 2 meet nonzero entries of A).
 template <int H, int NS>
 __device__ __forceinline__ void wu_half(const Frag<bf16_t> (&src)[NS][4], const float (&f)[4],
-                                        const Frag<bf16_t> (&af)[6], uint16_t (*sX)[XP], bf16_t* __restrict__ dst,
+                                        const Frag<f16_t> (&af)[6], uint16_t (*sX)[XP], bf16_t* __restrict__ dst,
                                         size_t dst_row, int c0, int nrow, int lane) {
   const int row = lane & 15, grp = lane >> 4;
   __syncthreads();                           // the last readers of the tile are done
@@ -199,13 +200,13 @@ __device__ __forceinline__ void wu_half(const Frag<bf16_t> (&src)[NS][4], const 
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sX[32 * sl + 8 * grp + e][16 * rb + row] = f2bf(src[2 * H + sl][rb].get(e) * f[rb]);
+      for (int e = 0; e < 8; ++e) sX[32 * sl + 8 * grp + e][16 * rb + row] = __builtin_bit_cast(uint16_t, from_f<f16_t>(src[2 * H + sl][rb].get(e) * f[rb]));
   __syncthreads();
-  Frag<bf16_t> xf[4][2];                     // lane holds X[32 kk + 8 grp .. + 8][16 cb + row]
+  Frag<f16_t> xf[4][2];                      // lane holds X[32 kk + 8 grp .. + 8][16 cb + row]
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) xf[cb][kk].v = *reinterpret_cast<const bf16x8*>(&sX[16 * cb + row][32 * kk + 8 * grp]);
+    for (int kk = 0; kk < 2; ++kk) xf[cb][kk].v = *reinterpret_cast<const f16x8*>(&sX[16 * cb + row][32 * kk + 8 * grp]);
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int t = 16 * rb + row;             // this lane's token of the result
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(64) void gdn_intra_wu_bf16_kernel(
     const int64_t* __restrict__ cu, const int32_t* __restrict__ coff, int Tlen, int N, int NT, int nslots,
     int Hk, int HV) {
   // the fp32 inverse, then (once its operand blocks are in registers) the
-  // bf16 staging tile in the same bytes
+  // fp16 staging tile in the same bytes
   __shared__ __attribute__((aligned(16))) union {
     float a[BT][AP];
     uint16_t x[64][XP];
@@ -258,14 +259,15 @@ __global__ __launch_bounds__(64) void gdn_intra_wu_bf16_kernel(
   }
 
   // B operands of the products: lane holds A[16 rb + row][32 kk + 8 grp .. + 8]
-  Frag<bf16_t> af[6];
+  Frag<f16_t> af[6];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int kk = 0; kk <= rb / 2; ++kk) {
       const float* a = &sm.a[16 * rb + row][32 * kk + 8 * grp];
-      const uint4 pk{pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]), pack_bf2(a[6], a[7])};
-      af[apair(rb, kk)].v = __builtin_bit_cast(bf16x8, pk);
+      const uint4 pk{pack2<f16_t>(a[0], a[1]), pack2<f16_t>(a[2], a[3]), pack2<f16_t>(a[4], a[5]),
+                     pack2<f16_t>(a[6], a[7])};
+      af[apair(rb, kk)].v = __builtin_bit_cast(f16x8, pk);
     }
 
   // per-token scales of the rows: beta e^G for k, beta for v (0 past the end)

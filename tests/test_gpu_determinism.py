@@ -114,3 +114,21 @@ def test_state_scans_bitwise_repeatable(gate):
         torch.cuda.synchronize()
         runs.append([h, ht, dh, dh0])
     _same(runs[0], runs[1], f"state scans gate={gate}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_chunk_intra_bitwise_repeatable_and_workspace_independent(dtype):
+    print(f"determinism chunk_intra {dtype}", flush=True)
+    inp = workloads.make_prefill(1, 900, 2, 4, 128, 128, dtype=dtype, seed=430, seqlens=[300, 0, 1, 535, 64])
+    nbytes = binding.lib().gdn_chunk_intra_workspace_bytes(inp.num_seqs)
+
+    def run(ws):
+        r = binding.gdn_chunk_intra(d(inp.k), d(inp.v), d(inp.g), d(inp.beta), cu_seqlens=d(inp.cu_seqlens),
+                                    workspace=ws)
+        torch.cuda.synchronize()
+        return [x.clone() for x in r]
+
+    ff, zero = _workspaces(nbytes)
+    first = run(ff)
+    _same(first, run(zero), "chunk_intra: 0xFF against zeroed workspace")
+    _same(first, run(ff), "chunk_intra: second call")

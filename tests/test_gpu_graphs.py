@@ -145,3 +145,25 @@ def test_state_scan_graph_replays():
         torch.cuda.synchronize()
         _same(outs, ref, f"state scans replay {rep}")
         _other_work()
+
+
+def test_chunk_intra_graph_replays():
+    print("graph replay chunk_intra", flush=True)
+    inp = workloads.make_prefill(1, 700, 2, 4, 128, 128, dtype=torch.bfloat16, seed=470, seqlens=[450, 1, 249])
+    k, v, gg, beta, cu = d(inp.k), d(inp.v), d(inp.g), d(inp.beta), d(inp.cu_seqlens)
+    ws = torch.empty(binding.lib().gdn_chunk_intra_workspace_bytes(inp.num_seqs), dtype=torch.uint8, device=DEV)
+
+    def call():
+        return binding.gdn_chunk_intra(k, v, gg, beta, cu_seqlens=cu, workspace=ws)
+
+    ref = [x.clone() for x in call()]
+    torch.cuda.synchronize()
+    g, outs = _capture(call)
+    for rep in range(3):
+        for x in outs:
+            x.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(outs, ref, f"chunk_intra replay {rep}")
+        _other_work()

@@ -1,6 +1,7 @@
 """GPU parity at sizes whose tensors pass 4 GiB, so that element and byte
 offsets into them need more than 32 bits: the bf16 GDN prefill with q, k, v
-and o of 4.56 GB each, the forward state scan with fp32 states stored every
+and o of 4.56 GB each, the intra-chunk step with k, v, w and u of 4.56 GB
+each, the forward state scan with fp32 states stored every
 chunk (4.56 GB), and decode and the handoff on a bf16 state pool of 8.6 GB.
 
 Only a few heads or pool slots carry seeded random data (among them the
@@ -68,6 +69,39 @@ def test_gdn_prefill_offsets_past_4gib():
     assert not bool(torch.any(o != 0)), "output written outside the sampled heads"
     assert not bool(torch.any(ht != 0)), "final state written outside the sampled heads"
     del o, ht, h0
+    _release()
+
+
+def test_chunk_intra_offsets_past_4gib():
+    H, K, T = 128, 128, T_BIG
+    small = _heads(T, (0, H - 1), "big_intra", 311)
+    print(f"intra w/u offsets past 4 GiB: B=1 T={T} Hk=HV={H} K=V={K} bf16, sampled heads {list(small)}",
+          flush=True)
+    k, v = _zeros(1, T, H, K), _zeros(1, T, H, K)
+    g, beta = _zeros(1, T, H, dtype=torch.float32), _zeros(1, T, H, dtype=torch.float32)
+    for j, s in small.items():
+        k[:, :, j] = s.k[:, :, 0].to(DEV)
+        v[:, :, j] = s.v[:, :, 0].to(DEV)
+        g[:, :, j] = s.g[:, :, 0].to(DEV)
+        beta[:, :, j] = s.beta[:, :, 0].to(DEV)
+    w, u, A = binding.gdn_chunk_intra(k, v, g, beta)
+    torch.cuda.synchronize()
+    assert w.numel() * w.element_size() > 1 << 32
+    del k, v, g, beta
+    # zero heads: beta 0 gives A = I, w = u = 0
+    eye = (torch.arange(64, device=DEV)[None, :] == (torch.arange(T, device=DEV) % 64)[:, None]).to(A.dtype)
+    for j, s in small.items():
+        A_ref, w_ref, u_ref = oracle.chunk_intra_wu(s.k, s.v, s.beta, g=s.g)
+        print(f"  head {j}:", check("A", A[:, :, j:j + 1].cpu(), A_ref, torch.bfloat16),
+              check("w", w[:, :, j:j + 1].cpu(), w_ref, torch.bfloat16),
+              check("u", u[:, :, j:j + 1].cpu(), u_ref, torch.bfloat16), flush=True)
+        w[:, :, j] = 0
+        u[:, :, j] = 0
+        A[0, :, j] = eye
+    assert not bool(torch.any(w != 0)), "w written outside the sampled heads"
+    assert not bool(torch.any(u != 0)), "u written outside the sampled heads"
+    assert bool(torch.all(A == eye[None, :, None, :])), "A written outside the sampled heads"
+    del w, u, A, eye
     _release()
 
 
