@@ -187,8 +187,8 @@ __host__ __device__ constexpr int apair(int rb, int kk) { return rb < 2 ? rb : 2
 // Columns 64 H .. 64 H + 63 of w or u for bf16 io: the wave's scaled
 // fragments (lane holds X[16 rb + row][32 s + 8 grp .. + 8] of slab s, scale
 // f[rb] for its token) go to the staging tile as fp16, column-major; then,
-// per 16-column block cb and token block rb, out^T = X^T A^T over the two 32-token halves
-// kk (only kk <= rb / 2 meet nonzero entries of A).
+// per 16-column block cb and token block rb, out^T = X^T A^T over the two
+// 32-token halves kk (only kk <= rb / 2 meet nonzero entries of A).
 template <int H, int NS>
 __device__ __forceinline__ void wu_half(const Frag<bf16_t> (&src)[NS][4], const float (&f)[4],
                                         const Frag<f16_t> (&af)[6], uint16_t (*sX)[XP], bf16_t* __restrict__ dst,
@@ -200,13 +200,16 @@ __device__ __forceinline__ void wu_half(const Frag<bf16_t> (&src)[NS][4], const 
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sX[32 * sl + 8 * grp + e][16 * rb + row] = __builtin_bit_cast(uint16_t, from_f<f16_t>(src[2 * H + sl][rb].get(e) * f[rb]));
+      for (int e = 0; e < 8; ++e)
+        sX[32 * sl + 8 * grp + e][16 * rb + row] =
+            __builtin_bit_cast(uint16_t, from_f<f16_t>(src[2 * H + sl][rb].get(e) * f[rb]));
   __syncthreads();
   Frag<f16_t> xf[4][2];                      // lane holds X[32 kk + 8 grp .. + 8][16 cb + row]
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) xf[cb][kk].v = *reinterpret_cast<const f16x8*>(&sX[16 * cb + row][32 * kk + 8 * grp]);
+    for (int kk = 0; kk < 2; ++kk)
+      xf[cb][kk].v = *reinterpret_cast<const f16x8*>(&sX[16 * cb + row][32 * kk + 8 * grp]);
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int t = 16 * rb + row;             // this lane's token of the result
@@ -313,7 +316,8 @@ hipError_t launch_intra_wu(const IntraArgs& a, hipStream_t s) {
   const int nslots = a.cu_seqlens ? NT + a.N : a.B * NT;
   if (nslots <= 0 || (long long)a.B * a.T <= 0) return hipSuccess;
   if (a.bf16) {
-    if (a.K == 128) return a.V == 128 ? launch_bf16<128, 128>(a, s, NT, nslots) : launch_bf16<128, 64>(a, s, NT, nslots);
+    if (a.K == 128)
+      return a.V == 128 ? launch_bf16<128, 128>(a, s, NT, nslots) : launch_bf16<128, 64>(a, s, NT, nslots);
     return a.V == 128 ? launch_bf16<64, 128>(a, s, NT, nslots) : launch_bf16<64, 64>(a, s, NT, nslots);
   }
   return a.K == 128 ? launch_f32<128>(a, s, NT, nslots) : launch_f32<64>(a, s, NT, nslots);
