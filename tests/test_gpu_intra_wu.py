@@ -1,8 +1,8 @@
 """GPU parity of the scalar-gate intra-chunk step (gdn_chunk_intra, C ABI)
 against the fp64 oracle (oracle.chunk_intra_wu): A = (I + L)^-1, w and u,
-element by element, for bf16 and fp32 io, K and V in {64, 128}, GQA heads,
-ragged chunks, packed sequences with empty and one-token entries, per-token
-or chunk-local cumulative gates, no gate, and A alone."""
+element by element, for bf16 and fp32 io, K and V in {64, 128} (equal or
+not), GQA heads, ragged chunks, packed sequences with empty and one-token
+entries, per-token or chunk-local cumulative gates, no gate, and A alone."""
 
 import numpy as np
 import pytest
@@ -49,6 +49,13 @@ def _case(inp, gate="gdn", cumulative=False, wu=True):
 @pytest.mark.parametrize("K", [64, 128])
 def test_intra_wu_bf16_dense_gqa(K):
     inp = workloads.make_prefill(2, 200, 2, 4, K, K, dtype=torch.bfloat16, seed=600 + K, name=f"bf16_K{K}")
+    _case(inp)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("K,V", [(64, 128), (128, 64)])
+def test_intra_wu_unequal_head_dims(K, V, dtype):
+    inp = workloads.make_prefill(1, 170, 1, 2, K, V, dtype=dtype, seed=670 + K, name=f"K{K}_V{V}")
     _case(inp)
 
 
