@@ -107,3 +107,23 @@ def test_intra_wu_chunk_update_matches_prefill_state():
         h = np.exp(G[-1]) * h + (k[r] * np.exp(G[-1] - G)[:, None]).T @ (u[r] - w[r] @ h)
     got = ht[0, 0].cpu().double().numpy()
     assert np.abs(h.T - got).max() < 1e-4 * max(1.0, np.abs(got).max())
+
+
+def test_intra_wu_bf16_no_gate():
+    inp = workloads.make_prefill(2, 140, 2, 2, 128, 64, dtype=torch.bfloat16, seed=680, gate="none",
+                                 name="bf16_nogate")
+    _case(inp, gate=None)
+
+
+def test_intra_wu_empty_inputs():
+    """T = 0, and packed sequences that are all empty: nothing to do, no error."""
+    print("intra w/u empty inputs", flush=True)
+    for B, T, lens in ((2, 0, None), (1, 0, [0, 0, 0])):
+        k = torch.zeros((B, T, 1, 64), dtype=torch.bfloat16, device=DEV)
+        v = torch.zeros((B, T, 2, 64), dtype=torch.bfloat16, device=DEV)
+        g = torch.zeros((B, T, 2), dtype=torch.float32, device=DEV)
+        beta = torch.zeros((B, T, 2), dtype=torch.float32, device=DEV)
+        cu = None if lens is None else torch.tensor([0, *np.cumsum(lens)], dtype=torch.int64, device=DEV)
+        w, u, A = binding.gdn_chunk_intra(k, v, g, beta, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        assert w.shape == (B, 0, 2, 64) and u.shape == (B, 0, 2, 64) and A.shape == (B, 0, 2, 64)
