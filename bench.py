@@ -501,7 +501,8 @@ def bench_intra_wu(args, binding, workloads, torch):
     nbytes = B * T * (Hk * K * 2 + HV * (V * 2 + 4 + 4 + 64 * 2 + K * 2 + V * 2))
     return {"workload": f"gdn_chunk_intra B={B} T={T} H={HV} K=V={K} bf16, A, w and u out",
             "ms_per_call": round(ms, 5), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+            "measured_bytes": measured_traffic("intra_wu")}
 
 
 # --------------------------------------------------------------- CPU oracle
