@@ -244,9 +244,11 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v,
  *                tables); unused (NULL allowed) without
  * Supported: K, V in {64, 128}, chunk_size = 64, bf16 or fp32 io.  A is
  * formed in fp32 (forward substitution and block merge) and stored once in
- * the io dtype; w and u are fp32 products of that inverse with the scaled
- * rows.  Errors and pointer rules as in gdn_chunk_fwd.  Asynchronous on
- * `stream`.
+ * the io dtype.  w and u are products of that inverse with the scaled rows,
+ * accumulated in fp32: with fp32 io from fp32 operands, with bf16 io from
+ * the inverse and the scaled rows rounded to fp16 (saturating at +-65504;
+ * the page rounds both to bf16).  Errors and pointer rules as in
+ * gdn_chunk_fwd.  Asynchronous on `stream`.
  */
 size_t gdn_chunk_intra_workspace_bytes(int num_seqs);
 int gdn_chunk_intra(const void* k, const void* v, const float* g, int g_cumulative,
