@@ -164,14 +164,16 @@ def stage_times(binding, torch, step, steps):
 
 # --------------------------------------------------------------- counters
 def source_hash() -> str:
-    """Hash of the kernel sources (the same hash the profile summaries record),
-    taken over the code only: comments, indentation and blank lines are
-    dropped, so that an edit of the text around a kernel does not void its
-    measured counters."""
+    """Hash of the kernel sources and their compiler flags (the same hash the
+    profile summaries record), taken over the code only: comments,
+    indentation and blank lines are dropped, so that an edit of the text
+    around a kernel does not void its measured counters."""
     import glob
     import hashlib
     import re
+    from gated_delta_rule_61_amd import build
     h = hashlib.sha256()
+    h.update(repr((build.HIPCC_FLAGS, sorted(build.FILE_FLAGS.items()))).encode())
     for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_61_amd", "csrc", "*"))):
         with open(f, encoding="utf-8") as fh:
             text = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
