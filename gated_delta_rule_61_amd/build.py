@@ -31,12 +31,14 @@ HIPCC_FLAGS = [
 # The bf16 scan and the decode kernels keep MFMA accumulators in ordinary
 # VGPRs, which their VALU work reads and writes right away; with the
 # accumulation registers the compiler copies them back and forth.  The state
-# scans run about 3 % faster under the compiler's ILP-first scheduler (same
-# occupancy, no spills).
+# scans and the KDA intra kernel run about 3 % faster under the compiler's
+# ILP-first scheduler (same occupancy; the intra kernel spills 8 bytes per
+# lane instead of 12).
 FILE_FLAGS = {
     "chunk_scan_gdn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "state_scans.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "kda_intra.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 NOISE = "is not a recognized feature for this target"
